@@ -1,0 +1,200 @@
+"""Benchmark of the sparse MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one moe_forward (router + top-k, dispatch, grouped expert FFN up
+and down, combine) over one batch of synthetic tokens already resident in
+HBM.  W untimed steps, then K timed steps between device synchronisations;
+the expert weights rotate over several identical copies so that each step
+reads them from HBM rather than from the 256 MB last-level cache.
+
+Printed (one JSON line on stdout): tokens/s of the layer, plus
+  roofline     -- the dominant kernel (the grouped up-projection with the
+                  SwiGLU epilogue, 2/3 of the FLOPs) timed with HIP events
+                  on its stream over K launches, against the bf16 dense MFMA
+                  peak (decode workloads: against HBM bandwidth),
+  cpu_baseline -- the float64 CPU oracle on a bounded token sample of the
+                  same workload, on this host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % HBM peak (decode) / % MFMA peak (prefill)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(L, counts):
+    """FLOPs of the routed layer and HBM bytes of what it must read/write."""
+    n, d, E, k, f = L["n"], L["d"], L["E"], L["k"], L["d_ff"]
+    R = n * k
+    flops_up = 4.0 * R * d * f
+    flops = 2.0 * n * d * E + flops_up + 2.0 * R * f * d
+    act_b = 2 if L["x_dtype"] == "bf16" else 4
+    if L["w_dtype"] == "mxfp4":
+        per_expert = 3 * d * f // 2 + 3 * d * f // 32
+    else:
+        per_expert = 3 * d * f * (2 if L["w_dtype"] == "bf16" else 4)
+    active = int((counts > 0).sum())
+    bytes_ = E * d * act_b + 2 * n * d * act_b + active * per_expert
+    up_bytes = active * (2 * d * f * (per_expert / (3 * d * f))) + n * d * act_b + R * f * 2
+    return {"flops": flops, "flops_up": flops_up, "bytes": bytes_, "up_bytes": up_bytes,
+            "active_experts": active}
+
+
+def cpu_baseline(L, budget_s=15.0, threads=16):
+    """Time the float64 oracle on a token sample (about budget_s seconds)."""
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    with threadpool_limits(limits=threads):
+        m = min(L["n"], 64)
+        t0 = time.perf_counter()
+        oracle.forward(L, L["k"], L["renorm"], rows=np.arange(m))
+        dt = time.perf_counter() - t0
+        if dt < budget_s / 3 and m < L["n"]:
+            m = int(min(L["n"], max(m, m * budget_s / max(dt, 1e-3))))
+            t0 = time.perf_counter()
+            oracle.forward(L, L["k"], L["renorm"], rows=np.arange(m))
+            dt = time.perf_counter() - t0
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": m / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+            "sample": f"float64 dense-then-masked oracle on the first {m} of {L['n']} tokens "
+                      f"(all {L['E']} experts per token), one run, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is built and measured on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_layer_wave_amd import binding as B
+    from mixture_experts_layer_wave_amd import workloads as W
+    from mixture_experts_layer_wave_amd.device import DeviceLayer, to_device
+
+    name = args.workload or W.SWITCH
+    wl = W.WORKLOADS[name]
+    log(f"[bench] workload {name}: generating inputs")
+    L = W.make_layer(name, cache=False)
+    torch.cuda.set_device(0)
+    D = DeviceLayer(L)
+    stream = torch.cuda.current_stream()
+
+    # Identical weight copies in distinct HBM buffers, rotated per step.
+    copies = [D.weights]
+    keep = []
+    for _ in range(max(0, args.copies - 1)):
+        ws = {key: (None if D.w[key] is None else D.w[key].clone()) for key in D.w}
+        keep.append(ws)
+        copies.append(B.ExpertWeights(D.weights.dtype, *(B._ptr(ws[key]) for key in ("w1", "w3", "w2", "s1", "s3", "s2"))))
+
+    def step(i):
+        B.moe_forward(D.shape, D.x, D.act, D.wg, D.bias, copies[i % len(copies)], D.y, D.act,
+                      D.idx, D.topw, D.ws, D.ws_bytes, stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    # Routing of this batch (for the work model and the dominant-kernel loop).
+    n, E, k = D.n, D.E, D.k
+    R = n * k
+    logits = torch.empty((n, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((n, k), dtype=torch.int32, device="cuda")
+    tw = torch.empty((n, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(R, dtype=torch.int32, device="cuda")
+    inv = torch.empty((n, k), dtype=torch.int32, device="cuda")
+    B.moe_router_topk(D.shape, D.x, D.act, D.wg, D.bias, logits, idx, tw, stream)
+    B.moe_dispatch(D.shape, idx, counts, offsets, perm, inv, None, D.act, None, None, 0, stream)
+    h = torch.empty((R, D.d_ff), dtype=torch.int16 if D.wdt != "f32" else torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    work = algorithmic_work(L, counts.cpu().numpy())
+
+    # Dominant kernel: the grouped up-projection, one launch per call.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.warmup):
+        B.moe_expert_up(D.shape, D.x, D.act, perm, offsets, copies[i % len(copies)], h, stream)
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        B.moe_expert_up(D.shape, D.x, D.act, perm, offsets, copies[i % len(copies)], h, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    up_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    decode = wl.wdt == "mxfp4" and wl.n <= 64
+    if decode:
+        achieved = work["up_bytes"] / (up_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        achieved = work["flops_up"] / (up_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "grouped_gemm_kernel<up, gather> (moe_expert_up)"
+    roof["kernel_us"] = up_ms * 1e3
+    log(f"[bench] up kernel {up_ms * 1e3:.1f} us -> {roof['achieved']:.1f} {roof['unit']} ({100 * roof['frac']:.1f}% of peak)")
+    layer_tflops = work["flops"] / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] whole layer {layer_tflops:.1f} TFLOP/s, {work['bytes'] / (ms_per_step * 1e-3) / 1e9:.1f} GB/s algorithmic; active experts {work['active_experts']}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host")
+        cpu = cpu_baseline(L)
+        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    value = n / (ms_per_step * 1e-3)
+    line = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": D.act if D.wdt != "mxfp4" else "bf16 (mxfp4 weights)",
+        "data": "synthetic",
+        "config": {"workload": name, "n": wl.n, "d": wl.d, "E": wl.E, "k": wl.k, "d_ff": wl.d_ff,
+                   "weights": wl.wdt, "activations": wl.act, "weight_copies": len(copies),
+                   "layer_tflops": layer_tflops},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so, the sparse Mixture-of-Experts layer
+ * forward for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed follows "How Mixture of Experts Scales Model Parameters"
+ * (zhangchitc.github.io/posts/mixture-of-experts/):
+ *   - section "Routing: a router scores the experts, and the top one runs":
+ *     a d x E linear router W_g and a softmax over each row;
+ *   - section "Top-K: several experts, added up by weight": the K best
+ *     experts, weights renormalised over the K when K > 1;
+ *   - section "The forward pass: dispatch, then combine": per-expert piles,
+ *     each expert's FFN on its pile, weighted outputs put back in order;
+ *   - section "Dense models: ...": the FFN is up-projection, activation,
+ *     down-projection; here the SiLU-gated form silu(x W1) * (x W3) then W2.
+ * MXFP4 weights (minseoc03.com feed, note "What is MXFP4?": 4-bit values in
+ * blocks of 32 sharing one scale) use the OCP MX v1.0 encoding: E2M1
+ * elements, one E8M0 scale per 32 consecutive elements along K.
+ *
+ * Conventions shared by every entry point
+ *   - Data pointers are DEVICE pointers unless stated otherwise.  Structs
+ *     (moe_shape, moe_expert_weights) live in HOST memory and are read
+ *     during the call only.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every entry point only enqueues work on it and never synchronises
+ *     with the host, so the sequence is capturable in a HIP graph.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     allocates no device memory and keeps no state between calls; calls on
+ *     different streams with different buffers may run concurrently.
+ *   - Inputs are never written.  Outputs are fully overwritten.
+ *   - All argument checks run on the host before anything is enqueued: on
+ *     an error return nothing has been launched.  A launch failure returns
+ *     MOE_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation, as for any HIP work.
+ *   - Row-major layouts.  bf16 is stored as its 16-bit pattern.  MXFP4
+ *     matrices are [rows][K/2] bytes with the even-K element in the low
+ *     nibble, plus [rows][K/32] E8M0 scale bytes.
+ *   - Rounding: products are accumulated in float32; the expert hidden
+ *     activation is rounded to bf16 (round to nearest even) before the
+ *     down-projection when the weights are bf16 or MXFP4; pile outputs are
+ *     kept in float32 and rounded once in the combine.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  MOE_ERR_SHAPE = -2,       /* n, d, E, k, d_ff out of range or inconsistent */
+  MOE_ERR_DTYPE = -3,       /* unsupported dtype or dtype combination        */
+  MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned              */
+  MOE_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required       */
+  MOE_ERR_HIP = -6          /* a HIP launch failed                           */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+
+/* Layer shape.  n tokens of width d, E experts of hidden width d_ff, k
+ * experts per token.  renorm: 1 = divide the k probabilities by their sum,
+ * 0 = use the raw probabilities, -1 = renormalise iff k > 1.
+ * Limits: n >= 1, d >= 1, d_ff >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32),
+ * n * k < 2^31.  MXFP4 weights need d % 32 == 0 and d_ff % 32 == 0; bf16
+ * activations need d % 8 == 0 and d_ff % 8 == 0. */
+typedef struct {
+  int32_t n, d, E, k, d_ff;
+  int32_t renorm;
+} moe_shape;
+
+/* Expert weights (read only, caller owned).
+ *   w1, w3: [E][d_ff][d]  (gate and value up-projections, K = d contiguous)
+ *   w2:     [E][d][d_ff]  (down-projection, K = d_ff contiguous)
+ * For MXFP4, w1/w3 are [E][d_ff][d/2] bytes and w2 is [E][d][d_ff/2] bytes,
+ * with scales s1/s3 [E][d_ff][d/32] and s2 [E][d][d_ff/32]; s* are NULL for
+ * the other dtypes.  F32 weights require F32 activations; BF16 and MXFP4
+ * weights require BF16 activations. */
+typedef struct {
+  int32_t dtype; /* moe_dtype */
+  const void *w1, *w3, *w2;
+  const uint8_t *s1, *s3, *s2;
+} moe_expert_weights;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static, host-side description of a status code. */
+const char *moe_status_string(int status);
+
+/* Workspace bytes that moe_forward needs for this shape and weight dtype
+ * (also enough for moe_grouped_ffn).  Returns 0 for an invalid shape. */
+size_t moe_workspace_bytes(const moe_shape *s, int w_dtype);
+
+/* Router and top-k (routing and Top-K sections of the MoE page).
+ *   x      [n][d]   activations (act = MOE_F32 or MOE_BF16)
+ *   wg     [E][d]   router matrix W_g stored transposed, same dtype as x
+ *   bias   [E] f32  added to every logit, or NULL
+ *   logits [n][E] f32 output of x W_g (+ bias); required (the top-k pass
+ *          reads it back)
+ *   topk_idx [n][k] int32 output: chosen experts, best first (descending
+ *            logit, equal logits to the lower index)
+ *   topk_w   [n][k] f32 output: softmax probability of each chosen expert
+ *            over all E logits, divided by the sum over the k chosen when
+ *            renormalising.
+ * The softmax subtracts the row maximum before exponentiating ("Why
+ * FlashAttention is So Fast", section "A fused kernel, and an overflow
+ * problem"). */
+int moe_router_topk(const moe_shape *s, const void *x, int act, const void *wg,
+                    const float *bias, float *logits, int32_t *topk_idx,
+                    float *topk_w, void *stream);
+
+/* Dispatch (forward-pass section of the MoE page): regroup the n*k
+ * (token, slot) pairs into per-expert piles, expert by expert, each pile in
+ * ascending token then slot order; empty piles are allowed.
+ *   topk_idx [n][k] int32 input (every value in [0, E))
+ *   counts   [E]    int32 output: pile sizes
+ *   offsets  [E+1]  int32 output: pile e is rows offsets[e] .. offsets[e+1]
+ *   perm     [n*k]  int32 output: token of each pile row
+ *   inv      [n][k] int32 output: pile row of each (token, slot)
+ *   x / x_perm: if x_perm is not NULL, x_perm[r] = x[perm[r]] ([n*k][d],
+ *           dtype act) is gathered too (the row size d * sizeof(act) must be
+ *           a multiple of 4 bytes); x may be NULL when x_perm is NULL.
+ *   ws / ws_bytes: unused, may be NULL / 0.
+ * Results are deterministic (no order-dependent atomics). */
+int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
+                 int32_t *offsets, int32_t *perm, int32_t *inv, const void *x,
+                 int act, void *x_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped expert FFN (forward-pass section): for every expert e, the rows
+ * offsets[e] .. offsets[e+1] of x_perm go through expert e:
+ *   y_perm[r] = (silu(x_perm[r] W1_e^T) * (x_perm[r] W3_e^T)) W2_e^T
+ *   x_perm  [n*k][d] activations (act)
+ *   offsets [E+1]    int32, device, as produced by moe_dispatch
+ *   y_perm  [n*k][d] float32 output (out must be MOE_F32)
+ *   ws      device workspace of at least moe_workspace_bytes(s, w->dtype).
+ * offsets is read on the device only; empty experts cost nothing. */
+int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act,
+                    const int32_t *offsets, const moe_expert_weights *w,
+                    void *y_perm, int out, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* The two halves of moe_grouped_ffn, for callers that want them apart.
+ *
+ * moe_expert_up: h[r] = silu(a[src(r)] W1_e^T) * (a[src(r)] W3_e^T) for the
+ *   rows r of every pile e ("Dense models" section: up-projection and
+ *   activation).  src(r) = perm[r] when perm is not NULL (the rows are
+ *   gathered from the token matrix x [n][d]), else r (a = x_perm [n*k][d]).
+ *   h [n*k][d_ff] output: bf16 for BF16/MXFP4 weights (rounded to nearest
+ *   even), f32 for F32 weights.
+ * moe_expert_down: y_perm[r] = h[r] W2_e^T ("Dense models" section:
+ *   down-projection), y_perm [n*k][d] f32.
+ * offsets [E+1] as produced by moe_dispatch; read on the device only. */
+int moe_expert_up(const moe_shape *s, const void *a, int act, const int32_t *perm,
+                  const int32_t *offsets, const moe_expert_weights *w, void *h,
+                  void *stream);
+int moe_expert_down(const moe_shape *s, const void *h, const int32_t *offsets,
+                    const moe_expert_weights *w, float *y_perm, void *stream);
+
+/* Combine (forward-pass and Top-K sections): put the weighted pile rows
+ * back in token order and add the k contributions:
+ *   y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv[t][j]]
+ * summed in slot order in float32, then rounded to `out` (F32 or BF16).
+ *   y_perm [n*k][d] f32 (in must be MOE_F32); inv, topk_w [n][k]; y [n][d]. */
+int moe_combine(const moe_shape *s, const void *y_perm, int in,
+                const int32_t *inv, const float *topk_w, void *y, int out,
+                void *stream);
+
+/* The whole layer: router + top-k, dispatch, grouped FFN, combine.
+ *   x [n][d] (act), wg [E][d] (act), bias [E] f32 or NULL, w: experts,
+ *   y [n][d] output (out = act, or F32),
+ *   topk_idx / topk_w: optional [n][k] outputs (NULL = keep internal),
+ *   ws: workspace of at least moe_workspace_bytes(s, w->dtype) bytes,
+ *       16-byte aligned; its contents on entry do not matter. */
+int moe_forward(const moe_shape *s, const void *x, int act, const void *wg,
+                const float *bias, const moe_expert_weights *w, void *y,
+                int out, int32_t *topk_idx, float *topk_w, void *ws,
+                size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

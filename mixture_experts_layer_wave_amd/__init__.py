@@ -15,6 +15,8 @@ _BINDING_NAMES = (
     "moe_router_topk",
     "moe_dispatch",
     "moe_grouped_ffn",
+    "moe_expert_up",
+    "moe_expert_down",
     "moe_combine",
     "moe_forward",
     "MoeError",

@@ -1,0 +1,47 @@
+// Internal launch helpers of libmoe_mi355x (host side).  Each returns the
+// hipError_t of its launches; argument validation happens in moe_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- router ---------------------------------------------------------------
+// logits[n][E] = x[n][d] . wg[E][d] (+ bias[E]); x, wg are bf16 (is_bf16) or f32.
+hipError_t launch_router_logits(const void *x, const void *wg, const float *bias,
+                                float *logits, int n, int d, int E, bool is_bf16,
+                                hipStream_t st);
+// idx/w[n][k] from logits[n][E]: softmax over E, top-k, optional renorm.
+hipError_t launch_router_topk(const float *logits, int n, int E, int k, bool renorm,
+                              int32_t *idx, float *w, hipStream_t st);
+
+// ---- dispatch -------------------------------------------------------------
+hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *counts,
+                           int32_t *offsets, int32_t *perm, int32_t *inv,
+                           hipStream_t st);
+// x_perm[r] = x[perm[r]] for r < R, rows of row_bytes bytes (multiple of 4).
+hipError_t launch_gather_rows(const void *x, const int32_t *perm, void *x_perm, int R,
+                              int row_bytes, hipStream_t st);
+
+// ---- grouped FFN ----------------------------------------------------------
+struct FfnArgs {
+  const void *a;          // activations: x (gathered through perm) or x_perm
+  const int32_t *perm;    // row -> token, or NULL for contiguous rows
+  const int32_t *offsets; // [E+1]
+  int E, R, d, d_ff;
+  int w_dtype;            // 0 f32, 1 bf16, 2 mxfp4
+  const void *w1, *w3, *w2;
+  const uint8_t *s1, *s3, *s2;
+  void *h;                // [R][d_ff] hidden (bf16, or f32 for f32 weights)
+  float *y_perm;          // [R][d] f32
+};
+hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st);    // A -> h
+hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st);  // h -> y_perm
+hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st);  // both
+
+// ---- combine --------------------------------------------------------------
+hipError_t launch_combine(const float *y_perm, const int32_t *inv, const float *w,
+                          int n, int k, int d, void *y, bool out_bf16, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,264 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout and the launch sequence on the caller's stream.  Nothing
+// here allocates device memory or synchronises with the host.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct WsLayout {
+  size_t logits, idx, w, counts, offsets, perm, inv, h, yp, total;
+};
+
+int check_shape(const moe_shape *s) {
+  if (!s) return MOE_ERR_NULL;
+  if (s->n < 1 || s->d < 1 || s->d_ff < 1 || s->E < 1 || s->E > 1024 || s->k < 1 ||
+      s->k > s->E || s->k > 32 || s->renorm < -1 || s->renorm > 1)
+    return MOE_ERR_SHAPE;
+  if ((long long)s->n * s->k >= (1ll << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+bool renorm_of(const moe_shape *s) { return s->renorm < 0 ? s->k > 1 : s->renorm == 1; }
+
+// Activation / weight dtype pairing and the shape rules each needs.
+int check_dtypes(const moe_shape *s, int act, int wdt) {
+  if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_DTYPE;
+  if (wdt == MOE_F32) {
+    if (act != MOE_F32) return MOE_ERR_DTYPE;
+  } else if (wdt == MOE_BF16 || wdt == MOE_MXFP4) {
+    if (act != MOE_BF16) return MOE_ERR_DTYPE;
+    if (s->d % 8 || s->d_ff % 8) return MOE_ERR_SHAPE;
+    if (wdt == MOE_MXFP4 && (s->d % 32 || s->d_ff % 32)) return MOE_ERR_SHAPE;
+  } else {
+    return MOE_ERR_DTYPE;
+  }
+  return MOE_OK;
+}
+
+WsLayout layout(const moe_shape *s, int wdt) {
+  WsLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t n = (size_t)s->n, E = (size_t)s->E, R = n * (size_t)s->k;
+  L.logits = take(n * E * 4);
+  L.idx = take(R * 4);
+  L.w = take(R * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(R * 4);
+  L.inv = take(R * 4);
+  L.h = take(R * (size_t)s->d_ff * (wdt == MOE_F32 ? 4 : 2));
+  L.yp = take(R * (size_t)s->d * 4);
+  L.total = o;
+  return L;
+}
+
+int check_weights(const moe_shape *s, int act, const moe_expert_weights *w) {
+  if (!w) return MOE_ERR_NULL;
+  const int st = check_dtypes(s, act, w->dtype);
+  if (st != MOE_OK) return st;
+  if (!w->w1 || !w->w3 || !w->w2) return MOE_ERR_NULL;
+  if (w->dtype == MOE_MXFP4 && (!w->s1 || !w->s3 || !w->s2)) return MOE_ERR_NULL;
+  if (w->dtype != MOE_F32 && (!aligned16(w->w1) || !aligned16(w->w3) || !aligned16(w->w2)))
+    return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe::FfnArgs ffn_args(const moe_shape *s, const void *a, const int32_t *perm,
+                      const int32_t *offsets, const moe_expert_weights *w, void *h, float *yp) {
+  moe::FfnArgs f{};
+  f.a = a;
+  f.perm = perm;
+  f.offsets = offsets;
+  f.E = s->E;
+  f.R = s->n * s->k;
+  f.d = s->d;
+  f.d_ff = s->d_ff;
+  f.w_dtype = w->dtype;
+  f.w1 = w->w1;
+  f.w3 = w->w3;
+  f.w2 = w->w2;
+  f.s1 = w->s1;
+  f.s3 = w->s3;
+  f.s2 = w->s2;
+  f.h = h;
+  f.y_perm = yp;
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "shape out of range or inconsistent";
+    case MOE_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_bytes(const moe_shape *s, int w_dtype) {
+  if (check_shape(s) != MOE_OK) return 0;
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_MXFP4) return 0;
+  return layout(s, w_dtype).total;
+}
+
+int moe_router_topk(const moe_shape *s, const void *x, int act, const void *wg,
+                    const float *bias, float *logits, int32_t *topk_idx, float *topk_w,
+                    void *stream) {
+  int st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!x || !wg || !logits || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  if (act == MOE_BF16 && s->d % 8 == 0 && (!aligned16(x) || !aligned16(wg)))
+    return MOE_ERR_ALIGN;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = moe::launch_router_logits(x, wg, bias, logits, s->n, s->d, s->E,
+                                           act == MOE_BF16, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_router_topk(logits, s->n, s->E, s->k, renorm_of(s), topk_idx,
+                                            topk_w, hs));
+}
+
+int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
+                 int32_t *offsets, int32_t *perm, int32_t *inv, const void *x, int act,
+                 void *x_perm, void *ws, size_t ws_bytes, void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !counts || !offsets || !perm || !inv) return MOE_ERR_NULL;
+  const int row_bytes = s->d * (act == MOE_F32 ? 4 : 2);
+  if (x_perm) {
+    if (!x) return MOE_ERR_NULL;
+    if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_DTYPE;
+    if (row_bytes % 4) return MOE_ERR_SHAPE;  // rows are copied in 4-byte words
+    if (row_bytes % 16 == 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGN;
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = moe::launch_dispatch(topk_idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (x_perm) {
+    e = moe::launch_gather_rows(x, perm, x_perm, s->n * s->k, row_bytes, hs);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act, const int32_t *offsets,
+                    const moe_expert_weights *w, void *y_perm, int out, void *ws,
+                    size_t ws_bytes, void *stream) {
+  int st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_weights(s, act, w);
+  if (st != MOE_OK) return st;
+  if (!x_perm || !offsets || !y_perm) return MOE_ERR_NULL;
+  if (out != MOE_F32) return MOE_ERR_DTYPE;
+  if (act == MOE_BF16 && !aligned16(x_perm)) return MOE_ERR_ALIGN;
+  const WsLayout L = layout(s, w->dtype);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  char *base = (char *)ws;
+  const moe::FfnArgs f = ffn_args(s, x_perm, nullptr, offsets, w, base + L.h, (float *)y_perm);
+  return hip_status(moe::launch_grouped_ffn(f, (hipStream_t)stream));
+}
+
+int moe_expert_up(const moe_shape *s, const void *a, int act, const int32_t *perm,
+                  const int32_t *offsets, const moe_expert_weights *w, void *h, void *stream) {
+  int st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_weights(s, act, w);
+  if (st != MOE_OK) return st;
+  if (!a || !offsets || !h) return MOE_ERR_NULL;
+  if (act == MOE_BF16 && !aligned16(a)) return MOE_ERR_ALIGN;
+  const moe::FfnArgs f = ffn_args(s, a, perm, offsets, w, h, nullptr);
+  return hip_status(moe::launch_expert_up(f, (hipStream_t)stream));
+}
+
+int moe_expert_down(const moe_shape *s, const void *h, const int32_t *offsets,
+                    const moe_expert_weights *w, float *y_perm, void *stream) {
+  int st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!w) return MOE_ERR_NULL;
+  st = check_weights(s, w->dtype == MOE_F32 ? MOE_F32 : MOE_BF16, w);
+  if (st != MOE_OK) return st;
+  if (!h || !offsets || !y_perm) return MOE_ERR_NULL;
+  if (w->dtype != MOE_F32 && !aligned16(h)) return MOE_ERR_ALIGN;
+  const moe::FfnArgs f = ffn_args(s, nullptr, nullptr, offsets, w, (void *)h, y_perm);
+  return hip_status(moe::launch_expert_down(f, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_shape *s, const void *y_perm, int in, const int32_t *inv,
+                const float *topk_w, void *y, int out, void *stream) {
+  int st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !inv || !topk_w || !y) return MOE_ERR_NULL;
+  if (in != MOE_F32 || (out != MOE_F32 && out != MOE_BF16)) return MOE_ERR_DTYPE;
+  if (s->d % 4 == 0 && (!aligned16(y_perm) || !aligned16(y))) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_combine((const float *)y_perm, inv, topk_w, s->n, s->k, s->d, y,
+                                        out == MOE_BF16, (hipStream_t)stream));
+}
+
+int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, const float *bias,
+                const moe_expert_weights *w, void *y, int out, int32_t *topk_idx,
+                float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_shape(s);
+  if (st != MOE_OK) return st;
+  st = check_weights(s, act, w);
+  if (st != MOE_OK) return st;
+  if (!x || !wg || !y) return MOE_ERR_NULL;
+  if (out != MOE_F32 && out != MOE_BF16) return MOE_ERR_DTYPE;
+  if (act == MOE_BF16 && (!aligned16(x) || !aligned16(wg))) return MOE_ERR_ALIGN;
+  if (s->d % 4 == 0 && !aligned16(y)) return MOE_ERR_ALIGN;
+  const WsLayout L = layout(s, w->dtype);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  char *base = (char *)ws;
+  float *logits = (float *)(base + L.logits);
+  int32_t *idx = topk_idx ? topk_idx : (int32_t *)(base + L.idx);
+  float *wt = topk_w ? topk_w : (float *)(base + L.w);
+  int32_t *counts = (int32_t *)(base + L.counts);
+  int32_t *offsets = (int32_t *)(base + L.offsets);
+  int32_t *perm = (int32_t *)(base + L.perm);
+  int32_t *inv = (int32_t *)(base + L.inv);
+  float *yp = (float *)(base + L.yp);
+  hipStream_t hs = (hipStream_t)stream;
+
+  hipError_t e = moe::launch_router_logits(x, wg, bias, logits, s->n, s->d, s->E,
+                                           act == MOE_BF16, hs);
+  if (e == hipSuccess)
+    e = moe::launch_router_topk(logits, s->n, s->E, s->k, renorm_of(s), idx, wt, hs);
+  if (e == hipSuccess)
+    e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
+  if (e == hipSuccess)
+    e = moe::launch_grouped_ffn(ffn_args(s, x, perm, offsets, w, base + L.h, yp), hs);
+  if (e == hipSuccess)
+    e = moe::launch_combine(yp, inv, wt, s->n, s->k, s->d, y, out == MOE_BF16, hs);
+  return hip_status(e);
+}
+
+}  // extern "C"

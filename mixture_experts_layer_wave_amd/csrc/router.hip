@@ -1,0 +1,177 @@
+// Router: logits = x W_g (+ bias), row softmax, top-k and combine weights.
+//
+// "How Mixture of Experts Scales Model Parameters", section "Routing: a
+// router scores the experts, and the top one runs" (a single d x E linear
+// layer followed by a softmax per token) and section "Top-K: several
+// experts, added up by weight" (keep the K best, renormalise over them).
+// The softmax subtracts the row maximum first ("Why FlashAttention is So
+// Fast", section "A fused kernel, and an overflow problem").
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+// bf16 logits on MFMA.  One wave owns a 16-token x 16-expert tile and walks
+// K = d in steps of 32 with v_mfma_f32_16x16x32_bf16 (bf16 products are exact
+// in the fp32 accumulator).  Lane l holds tokens/experts (l % 16) and the 8
+// consecutive K values (l / 16) * 8 of each 32-wide step for both operands;
+// any fixed K order is valid as long as A and B agree.
+// Grid: x = token tiles (16), y = groups of 4 expert tiles.
+__global__ __launch_bounds__(256) void router_logits_bf16_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg,
+    const float *__restrict__ bias, float *__restrict__ logits, int n, int d, int E) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * 16;
+  const int e0 = (blockIdx.y * 4 + wave) * 16;
+  if (e0 >= E) return;  // no barriers in this kernel
+  const int row = lane & 15, kg = lane >> 4;
+  const int t = t0 + row, e = e0 + row;
+  const bool tv = t < n, ev = e < E;
+  const uint16_t *xr = x + (size_t)(tv ? t : 0) * d + kg * 8;
+  const uint16_t *wr = wg + (size_t)(ev ? e : 0) * d + kg * 8;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  int k0 = 0;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (; k0 + 64 <= d; k0 += 64) {
+    u32x4 a0 = tv ? *(const u32x4 *)(xr + k0) : zero;
+    u32x4 b0 = ev ? *(const u32x4 *)(wr + k0) : zero;
+    u32x4 a1 = tv ? *(const u32x4 *)(xr + k0 + 32) : zero;
+    u32x4 b1 = ev ? *(const u32x4 *)(wr + k0 + 32) : zero;
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                   __builtin_bit_cast(bf16x8, b0), acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                   __builtin_bit_cast(bf16x8, b1), acc1, 0, 0, 0);
+  }
+  for (; k0 < d; k0 += 32) {
+    const bool kv = k0 + kg * 8 < d;  // d % 8 == 0: a chunk is all in or all out
+    u32x4 a0 = (tv && kv) ? *(const u32x4 *)(xr + k0) : zero;
+    u32x4 b0 = (ev && kv) ? *(const u32x4 *)(wr + k0) : zero;
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                   __builtin_bit_cast(bf16x8, b0), acc0, 0, 0, 0);
+  }
+  // Output layout of the 16x16 tile: lane l holds rows (l / 16) * 4 + i, column l % 16.
+  if (ev) {
+    const float bb = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tt = t0 + kg * 4 + i;
+      if (tt < n) logits[(size_t)tt * E + e] = acc0[i] + acc1[i] + bb;
+    }
+  }
+}
+
+// float32 logits (any dtype pair is handled here when MFMA does not apply):
+// one thread per (token, expert), plain fused multiply-adds in K order.
+template <typename T>
+__global__ __launch_bounds__(256) void router_logits_valu_kernel(
+    const T *__restrict__ x, const T *__restrict__ wg, const float *__restrict__ bias,
+    float *__restrict__ logits, int n, int d, int E) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)n * E) return;
+  const int t = (int)(i / E), e = (int)(i % E);
+  const T *xr = x + (size_t)t * d;
+  const T *wr = wg + (size_t)e * d;
+  float acc = 0.f;
+  for (int k = 0; k < d; ++k) {
+    float a, b;
+    if constexpr (sizeof(T) == 2) {
+      a = bf16_bits_to_f32(xr[k]);
+      b = bf16_bits_to_f32(wr[k]);
+    } else {
+      a = xr[k];
+      b = wr[k];
+    }
+    acc = fmaf(a, b, acc);
+  }
+  logits[i] = acc + (bias ? bias[e] : 0.f);
+}
+
+// Softmax + top-k: one wave per token.  Lane l owns experts l, l + 64, ...
+// Each of the k rounds takes the wave-wide best (value, lowest index) of the
+// experts not taken yet.  Selection is on the float32 logits; the weights
+// are exp(z - max) over the full-row sum, or over the sum of the chosen k.
+constexpr int kPer = MOE_MAX_E / MOE_WAVE;  // experts per lane at most
+
+__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int n,
+                                                          int E, int k, int renorm,
+                                                          int32_t *__restrict__ idx,
+                                                          float *__restrict__ w) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= n) return;
+  const float *z = logits + (size_t)t * E;
+  const float NEG = -__builtin_inff();
+  float v[kPer];
+  float m = NEG;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + MOE_WAVE * j;
+    v[j] = e < E ? z[e] : NEG;
+    m = fmaxf(m, v[j]);
+  }
+  m = wave_max(m);
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (lane + MOE_WAVE * j < E) s += expf(v[j] - m);
+  s = wave_sum(s);
+
+  uint32_t taken = 0;
+  float my_v = NEG;
+  int my_i = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = NEG;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane + MOE_WAVE * j;
+      const bool ok = e < E && !((taken >> j) & 1u);
+      if (ok && (v[j] > bv || (v[j] == bv && e < bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+    wave_argmax(bv, bi);
+    if (bi < E && (bi & (MOE_WAVE - 1)) == lane) taken |= 1u << (bi / MOE_WAVE);
+    if (lane == r) {
+      my_v = bv;
+      my_i = bi;
+    }
+  }
+  const float num = lane < k ? expf(my_v - m) : 0.f;
+  float den = s;
+  if (renorm) den = wave_sum(num);
+  if (lane < k) {
+    idx[(size_t)t * k + lane] = my_i;
+    w[(size_t)t * k + lane] = num / den;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const void *x, const void *wg, const float *bias, float *logits,
+                                int n, int d, int E, bool is_bf16, hipStream_t st) {
+  if (is_bf16 && d % 8 == 0) {
+    dim3 grid((n + 15) / 16, (E + 63) / 64);
+    router_logits_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)x, (const uint16_t *)wg,
+                                                    bias, logits, n, d, E);
+  } else if (is_bf16) {
+    const long long tot = (long long)n * E;
+    router_logits_valu_kernel<uint16_t><<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
+        (const uint16_t *)x, (const uint16_t *)wg, bias, logits, n, d, E);
+  } else {
+    const long long tot = (long long)n * E;
+    router_logits_valu_kernel<float><<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
+        (const float *)x, (const float *)wg, bias, logits, n, d, E);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const float *logits, int n, int E, int k, bool renorm, int32_t *idx,
+                              float *w, hipStream_t st) {
+  router_topk_kernel<<<(n + 3) / 4, 256, 0, st>>>(logits, n, E, k, renorm ? 1 : 0, idx, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -285,7 +285,6 @@ def make_layer(wl: Workload | str, redraws: dict | None = None, bias: np.ndarray
     else:
         wts = {"wg": draw_router(wl), **draw_experts(wl)}
         if cache:
-            _layer_cache.clear()
             _layer_cache[key] = wts
     return {
         "name": wl.name, "n": wl.n, "d": wl.d, "E": wl.E, "k": wl.k, "d_ff": wl.d_ff,

@@ -119,9 +119,9 @@ def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     K = codes.shape[-1]
     if scales.shape[-1] * 32 != K:
         raise ValueError("scale count does not match K/32")
-    vals = decode_e2m1(codes)
-    sc = np.repeat(decode_e8m0(scales), 32, axis=-1)
-    return vals * sc
+    vals = decode_e2m1(np.arange(16))[codes]  # the 16 codes decoded once, then looked up
+    blocks = vals.reshape(*vals.shape[:-1], K // 32, 32) * decode_e8m0(scales)[..., None]
+    return blocks.reshape(vals.shape)
 
 
 def decode_matrix(raw: np.ndarray, dtype: str, scales: np.ndarray | None = None) -> np.ndarray:

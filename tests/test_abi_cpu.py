@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry
+point the header declares, and rejects bad arguments before launching."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    from mixture_experts_layer_wave_amd import binding as B
+
+    decl = _declared()
+    assert len(decl) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)", out))
+    for name in decl:
+        assert name in exported, name
+        assert name in B.EXPORTS, name
+        getattr(B.lib, name)
+
+
+def test_abi_version_and_status_strings():
+    from mixture_experts_layer_wave_amd import binding as B
+
+    ver = int(re.search(r"#define MOE_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert B.moe_abi_version() == ver
+    for st in range(0, -7, -1):
+        assert B.moe_status_string(st) != "unknown status"
+    assert B.moe_status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    from mixture_experts_layer_wave_amd import binding as B
+
+    n, d, E, k, f = 4096, 1024, 8, 1, 4096
+    ws = B.moe_workspace_bytes((n, d, E, k, f), "bf16")
+    R = n * k
+    # hidden [R][d_ff] bf16 and pile outputs [R][d] f32 dominate
+    assert ws >= R * f * 2 + R * d * 4 + n * E * 4
+    assert ws % 256 == 0
+    assert B.moe_workspace_bytes((n, d, E, 9, f), "bf16") == 0  # k > E
+    assert B.moe_workspace_bytes((n, d, E, k, f), 7) == 0
+
+
+@pytest.mark.parametrize("shape,status", [
+    (None, -1),
+    ((0, 8, 4, 1, 8), -2),
+    ((4, 8, 4, 5, 8), -2),
+    ((4, 8, 1025, 1, 8), -2),
+    ((4, 8, 64, 33, 8), -2),
+    ((4, 8, 4, 1, 8, 2), -2),
+])
+def test_forward_rejects_bad_shapes_before_launch(shape, status):
+    import ctypes
+
+    from mixture_experts_layer_wave_amd import binding as B
+
+    sp = None if shape is None else ctypes.byref(B._shape(shape))
+    w = B.ExpertWeights(1, None, None, None, None, None, None)
+    assert B.lib.moe_forward(sp, None, 1, None, None, ctypes.byref(w), None, 1, None, None, None, 0, None) == status
+
+
+def test_dtype_and_null_errors_before_launch():
+    import ctypes
+
+    from mixture_experts_layer_wave_amd import binding as B
+
+    sp = ctypes.byref(B._shape((4, 64, 4, 2, 64)))
+    w = B.ExpertWeights(1, None, None, None, None, None, None)
+    # bf16 weights with f32 activations: dtype error, checked first
+    assert B.lib.moe_forward(sp, None, 0, None, None, ctypes.byref(w), None, 1, None, None, None, 0, None) == -3
+    # MXFP4 needs d % 32 == 0
+    sp2 = ctypes.byref(B._shape((4, 40, 4, 2, 64)))
+    w4 = B.ExpertWeights(2, None, None, None, None, None, None)
+    assert B.lib.moe_forward(sp2, None, 1, None, None, ctypes.byref(w4), None, 1, None, None, None, 0, None) == -2
+    # missing weight pointers
+    assert B.lib.moe_forward(sp, None, 1, None, None, ctypes.byref(w), None, 1, None, None, None, 0, None) == -1
+    assert B.lib.moe_router_topk(sp, None, 1, None, None, None, None, None, None) == -1
+    assert B.lib.moe_combine(sp, None, 1, None, None, None, 1, None) == -1
+    assert B.lib.moe_dispatch(sp, None, None, None, None, None, None, 1, None, None, 0, None) == -1
+
+
+def test_product_path_fails_loudly_without_library(tmp_path):
+    """Importing the binding from a copy of the package without the built
+    library raises instead of falling back to anything."""
+    import shutil
+    import sys
+
+    pkg = os.path.join(ROOT, "mixture_experts_layer_wave_amd")
+    dst = tmp_path / "mixture_experts_layer_wave_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    code = "import mixture_experts_layer_wave_amd.binding"
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0 and "not built" in r.stderr

@@ -1,0 +1,75 @@
+"""GPU parity of moe_grouped_ffn and moe_combine against the oracle."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_support import SMALL, TOL, layer_of, oracle_routing, row_rel_err, sample_rows, say
+from mixture_experts_layer_wave_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _expert_ref(L, rows_x, e):
+    m = oracle.moe_oracle._expert_mats(L, e)
+    return oracle.swiglu_expert(rows_x, *m)
+
+
+@pytest.mark.parametrize("name", list(SMALL) + [W.SWITCH, W.DECODE[2], W.PREFILL_ZIPF])
+def test_grouped_ffn_matches_oracle(name):
+    import torch
+    from mixture_experts_layer_wave_amd import binding as B
+    from mixture_experts_layer_wave_amd.device import DeviceLayer, to_device
+
+    say(f"[ffn] {name}")
+    L = layer_of(name)
+    ref = oracle_routing(L)
+    D = DeviceLayer(L)
+    R = D.n * D.k
+    xp = to_device(L["x"][ref["perm"]])
+    off = to_device(ref["offsets"])
+    yp = torch.full((R, D.d), float("nan"), dtype=torch.float32, device="cuda")
+    B.moe_grouped_ffn(D.shape, xp, D.act, off, D.weights, yp, "f32", D.ws, D.ws_bytes)
+    torch.cuda.synchronize()
+    got = yp.double().cpu().numpy()
+    x = oracle.decode_matrix(L["x"], L["x_dtype"])
+    worst = 0.0
+    for e in range(L["E"]):
+        lo, hi = int(ref["offsets"][e]), int(ref["offsets"][e + 1])
+        if lo == hi:
+            continue
+        rows = np.arange(lo, hi)
+        if len(rows) > 24:  # sampled rows of large piles, always incl. the pile edges
+            rows = np.unique(np.concatenate([rows[:4], rows[-4:], np.random.default_rng(e).choice(rows, 16)]))
+        want = _expert_ref(L, x[ref["perm"][rows]], e)
+        worst = max(worst, row_rel_err(got[rows], want))
+        if e > 24 and name == W.PREFILL_ZIPF:
+            break
+    say(f"    max row rel err {worst:.3e}")
+    assert worst <= TOL[L["w_dtype"]]
+
+
+@pytest.mark.parametrize("k,d,out", [(1, 1024, "bf16"), (2, 4096, "bf16"), (4, 2880, "f32"), (3, 7, "f32"), (2, 10, "bf16")])
+def test_combine_matches_fp64(k, d, out):
+    import torch
+    from mixture_experts_layer_wave_amd import binding as B
+    from mixture_experts_layer_wave_amd.device import to_device
+
+    say(f"[combine] k={k} d={d} out={out}")
+    rng = np.random.default_rng(k * 1000 + d)
+    n = 257
+    E = 8
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(n)]).astype(np.int32)
+    dp = oracle.dispatch(idx, E)
+    yp = rng.standard_normal((n * k, d)).astype(np.float32)
+    w = rng.random((n, k)).astype(np.float32)
+    y = torch.empty((n, d), dtype=torch.int16 if out == "bf16" else torch.float32, device="cuda")
+    B.moe_combine((n, d, E, k, 8, -1), to_device(yp), "f32", to_device(dp["inv"]), to_device(w), y, out)
+    torch.cuda.synchronize()
+    want = sum(w[:, j:j + 1].astype(np.float64) * yp[dp["inv"][:, j]].astype(np.float64) for j in range(k))
+    if out == "bf16":
+        got = y.view(torch.bfloat16).double().cpu().numpy()
+        np.testing.assert_allclose(got, want, rtol=2 ** -8, atol=1e-6)
+    else:
+        got = y.double().cpu().numpy()
+        np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6)
