@@ -29,7 +29,8 @@ def _run_dispatch(idx_np, E, x_np=None):
         x = to_device(x_np)
         act = "f32" if x_np.dtype == np.float32 else "bf16"
         xp = torch.empty((n * k, x_np.shape[1]), dtype=x.dtype, device="cuda")
-    B.moe_dispatch((n, 1, E, k, 1, -1), idx, counts, offsets, perm, inv, x, act, xp)
+    d = 1 if x_np is None else x_np.shape[1]
+    B.moe_dispatch((n, d, E, k, 1, -1), idx, counts, offsets, perm, inv, x, act, xp)
     torch.cuda.synchronize()
     out = {key: t.cpu().numpy() for key, t in
            (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv", inv))}
