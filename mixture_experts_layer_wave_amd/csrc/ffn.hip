@@ -16,6 +16,7 @@
 // LDS (v_cvt_scalef32_pk_bf16_fp4: E2M1 x 2^(s-127) is exact in bf16), so
 // the MFMA loop is shared.  float32 weights take a plain FMA path.
 #include "common.h"
+#include "gemm_big.h"
 #include "kernels.h"
 
 namespace moe {
@@ -321,6 +322,46 @@ hipError_t launch_gemm(const GemmParams &gp, int m_tiles, bool gather, hipStream
 
 }  // namespace
 
+namespace {
+
+// The large-tile kernel addresses its operands with 32-bit buffer offsets.
+bool big_ok(const FfnArgs &a, size_t a_bytes, int N, int K) {
+  const size_t lim = (size_t)1 << 31;
+  if (a.w_dtype != 1 && a.w_dtype != 2) return false;
+  if (a_bytes >= lim || (size_t)N * K * 2 >= lim) return false;
+  return K % 8 == 0;
+}
+
+BigGemmParams big_params(const FfnArgs &a, bool up) {
+  BigGemmParams p{};
+  p.offsets = a.offsets;
+  p.E = a.E;
+  p.R = a.R;
+  if (up) {
+    p.a = (const uint16_t *)a.a;
+    p.a_bytes = (uint32_t)((size_t)(a.perm ? a.n : a.R) * a.d * 2);
+    p.perm = a.perm;
+    p.N = a.d_ff;
+    p.K = a.d;
+    p.b0 = a.w1;
+    p.b1 = a.w3;
+    p.s0 = a.s1;
+    p.s1 = a.s3;
+    p.out = a.h;
+  } else {
+    p.a = (const uint16_t *)a.h;
+    p.a_bytes = (uint32_t)((size_t)a.R * a.d_ff * 2);
+    p.N = a.d;
+    p.K = a.d_ff;
+    p.b0 = a.w2;
+    p.s0 = a.s2;
+    p.out = a.y_perm;
+  }
+  return p;
+}
+
+}  // namespace
+
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
   if (a.w_dtype == 0) {
@@ -329,6 +370,12 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
         (const float *)a.a, a.perm, a.offsets, a.E, a.R, a.d, a.d_ff, (const float *)a.w1,
         (const float *)a.w3, (float *)a.h);
     return hipGetLastError();
+  }
+  const size_t a_bytes = (size_t)(a.perm ? a.n : a.R) * a.d * 2;
+  if (big_ok(a, a_bytes, a.d_ff, a.d)) {
+    BigGemmParams p = big_params(a, true);
+    p.n_tiles = (a.d_ff + 127) / 128;
+    return launch_big_gemm(p, true, a.w_dtype == 2, a.perm != nullptr, false, 256, 256, st);
   }
   GemmParams up{};
   up.a = (const uint16_t *)a.a;
@@ -348,13 +395,39 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
                         : launch_gemm<true, false>(up, m_tiles, a.perm != nullptr, st);
 }
 
-hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st) {
+hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
+  if (fused) *fused = false;
   if (a.R == 0) return hipSuccess;
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d;
     ffn_down_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
         (const float *)a.h, a.offsets, a.E, a.R, a.d, a.d_ff, (const float *)a.w2, a.y_perm);
     return hipGetLastError();
+  }
+  if (big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff)) {
+    // Largest block tile that still gives every CU a tile (256 CUs).
+    static const int cfg[3][2] = {{256, 256}, {256, 128}, {128, 128}};
+    int bm = 128, bnb = 128;
+    for (int i = 0; i < 3; ++i) {
+      const long long blocks = (long long)((a.R + cfg[i][0] - 1) / cfg[i][0]) *
+                               ((a.d + cfg[i][1] - 1) / cfg[i][1]);
+      if (blocks >= 256) {
+        bm = cfg[i][0];
+        bnb = cfg[i][1];
+        break;
+      }
+    }
+    BigGemmParams p = big_params(a, false);
+    p.n_tiles = (a.d + bnb - 1) / bnb;
+    const bool fuse = a.fuse_y != nullptr && a.k == 1;
+    if (fuse) {
+      p.out = a.fuse_y;
+      p.perm_out = a.fuse_perm;
+      p.comb_w = a.fuse_w;
+    }
+    hipError_t err = launch_big_gemm(p, false, a.w_dtype == 2, false, fuse, bm, bnb, st);
+    if (err == hipSuccess && fused) *fused = fuse;
+    return err;
   }
   GemmParams dn{};
   dn.a = (const uint16_t *)a.h;
@@ -372,10 +445,10 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st) {
                         : launch_gemm<false, false>(dn, m_tiles, false, st);
 }
 
-hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st) {
+hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st, bool *fused) {
   hipError_t err = launch_expert_up(a, st);
   if (err != hipSuccess) return err;
-  return launch_expert_down(a, st);
+  return launch_expert_down(a, st, fused);
 }
 
 }  // namespace moe

@@ -1,0 +1,28 @@
+// Large-tile grouped expert GEMM (gemm_big.hip): host launch interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct BigGemmParams {
+  const uint16_t *a;        // bf16 activation rows (x gathered through perm, or contiguous)
+  uint32_t a_bytes;         // bytes of the whole activation buffer (< 2^31)
+  const int32_t *perm;      // up: pile row -> row of a (NULL = contiguous)
+  const int32_t *offsets;   // [E+1] pile boundaries (device)
+  int E, R, N, K, n_tiles;  // R = rows of the pile matrix; N, K of one expert matrix
+  const void *b0, *b1;      // [E][N][K] bf16 or [E][N][K/2] MXFP4; b1 (W3) for up only
+  const uint8_t *s0, *s1;   // MXFP4 E8M0 scales [E][N][K/32]
+  void *out;                // up: bf16 [R][N]; down: f32 [R][N]; fused: bf16 y [n][N]
+  const int32_t *perm_out;  // fused combine: pile row -> token
+  const float *comb_w;      // fused combine: token -> weight (one expert per token)
+};
+
+// up: H = silu(A W1^T) * (A W3^T); down: Yp = H W2^T (or the fused combine).
+// bm x bnb is the block tile (256x256 for up; 256x256, 256x128 or 128x128
+// for down).  Returns hipErrorInvalidValue for a combination not built.
+hipError_t launch_big_gemm(const BigGemmParams &p, bool up, bool mx, bool gather, bool fuse,
+                           int bm, int bnb, hipStream_t st);
+
+}  // namespace moe

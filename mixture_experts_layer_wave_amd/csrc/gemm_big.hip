@@ -1,0 +1,463 @@
+// Large-tile grouped expert GEMM for gfx950 (the prefill path of the
+// expert FFN; see ffn.hip for the operation and its sources).
+//
+//   up:   H[r]  = silu(A[r] . W1_e^T) * (A[r] . W3_e^T)   (bf16 out)
+//   down: Yp[r] = H[r] . W2_e^T                            (f32 out), or, when
+//         every token has one expert, Y[tok(r)] = w(tok) * (H[r] . W2_e^T)
+//         written straight into the layer output (combine fused).
+//
+// Block = 8 waves (two per SIMD, so one wave's MFMAs cover the other's
+// barrier and LDS waits) arranged 2 x 4.  Block tile BM rows x BNB B-rows
+// (the up kernel's B-rows are BNB/2 rows of W1 followed by the same BNB/2
+// rows of W3, so each wave holds matching gate and value accumulators).
+// Wave tile (BM/2) x (BNB/4) on v_mfma_f32_32x32x16_bf16.  At 256 x 256 the
+// block moves 64 KB from L2 per 64-deep K step for 8.4 MFLOP, i.e. 32 B per
+// clock per CU at the MFMA peak, about what L2 delivers to a CU: this tile
+// size is the smallest that is not load-bound.
+//
+// bf16 operands reach LDS by direct buffer loads (buffer_load_dwordx4 ...
+// lds): lane i of an instruction fills bytes [16 i, 16 i + 16) of a 1 KB run,
+// so the global address each lane fetches is chosen to produce the swizzled
+// layout (see swz()).  Loads past a buffer's record count return zero, which
+// fills ragged rows and the K tail.  K advances by BK (MOE_BF16_BK) through
+// NST (MOE_BF16_NST) LDS stages: NST - 1 steps of loads are in flight while
+// one is multiplied.
+// MXFP4 weights go through registers instead: 32 E2M1 codes and their E8M0
+// scale are converted to bf16 (v_cvt_scalef32_pk_bf16_fp4) and written to
+// LDS (BK = 64, two stages), so the MFMA loop is the same.
+//
+// Tiles are ordered expert-major, then N-tile, then M-tile, and the ordered
+// list is cut into 8 contiguous chunks, one per XCD (workgroup i runs on XCD
+// i mod 8), so the tiles that share an expert's weights share one L2.
+#include <atomic>
+
+#include "common.h"
+#include "gemm_big.h"
+
+namespace moe {
+namespace {
+
+// K step and LDS stage count of the bf16 path (MXFP4 uses 64 and 2).
+#ifndef MOE_BF16_BK
+#define MOE_BF16_BK 64
+#endif
+#ifndef MOE_BF16_NST
+#define MOE_BF16_NST 2
+#endif
+// Waves per block (4 = one per SIMD, 8 = two per SIMD), arranged 2 x NW/2.
+#ifndef MOE_BIG_WAVES
+#define MOE_BIG_WAVES 8
+#endif
+constexpr int kNW = MOE_BIG_WAVES;
+constexpr int kNT = kNW * 64;
+
+constexpr uint32_t kOOB = 0x80000000u;  // offset bit past every record count
+constexpr uint32_t kRsrcFlags = 0x00020000u;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kRsrcFlags);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_run, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_run, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS tile layout: rows of BK bf16 (BK * 2 bytes), 16-B chunks swizzled so
+// that the 16 consecutive rows read by one 16-lane pass of ds_read_b128 fall
+// in 16 distinct groups of 4 banks:
+//   BK = 64 (128-B rows): chunk c of row r at c ^ ((r / 2) % 8)
+//   BK = 32 ( 64-B rows): chunk c of row r at c ^ ((r / 4) % 4)
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if constexpr (BK == 64) return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+template <int BM, int BNB, int BK>
+struct Tile {
+  static constexpr int WM = BM / 2, WN = BNB / (kNW / 2);
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int ROWB = BK * 2, CPR = BK / 8, RPR = 1024 / ROWB;
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BNB * ROWB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_RUNS = BM / RPR / kNW;  // 1 KB DMA runs per wave per stage
+  static constexpr int B_RUNS = BNB / RPR / kNW;
+  static constexpr int SLICES = BK / 16;
+  static constexpr int MX_ALL = BNB * (BK / 32);               // (row, 32-K block) units
+  static constexpr int MX_UNITS = (MX_ALL + kNT - 1) / kNT;      // per thread
+};
+
+template <bool UP, bool MX, bool GATHER, bool FUSE, int BM, int BNB>
+__global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
+  constexpr int BK = MX ? 64 : MOE_BF16_BK;
+  constexpr int NST = MX ? 2 : MOE_BF16_NST;
+  using T = Tile<BM, BNB, BK>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ int s_e, s_row0, s_rows, s_nt;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases
+  const int N = p.N, K = p.K;
+
+  // ---- block -> tile ------------------------------------------------------
+  if (wave == 0) {
+    const int per = (p.E + MOE_WAVE - 1) / MOE_WAVE;
+    const int eb = lane * per, ee = min(p.E, eb + per);
+    int local = 0;
+    for (int x = eb; x < ee; ++x) local += (p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM;
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < MOE_WAVE; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    const int excl = incl - local;
+    const int total = __shfl(incl, MOE_WAVE - 1, 64) * p.n_tiles;  // tiles of work
+    const int b = blockIdx.x;
+    if (lane == 0 && b >= total) s_e = -1;
+    if (b < total) {
+      // XCD-contiguous remap of the ordered tile list.
+      const int xcd = b & 7, slot = b >> 3;
+      int base = 0;
+      for (int x = 0; x < xcd; ++x) base += (total - x + 7) >> 3;
+      const int L = base + slot;
+      const int lo = excl * p.n_tiles, hi = incl * p.n_tiles;
+      if (L >= lo && L < hi) {
+        int acc = lo;
+        for (int x = eb; x < ee; ++x) {
+          const int m = p.offsets[x + 1] - p.offsets[x];
+          const int te = (m + BM - 1) / BM;
+          if (L < acc + te * p.n_tiles) {
+            const int loc = L - acc;
+            const int mloc = loc % te;
+            s_e = x;
+            s_nt = loc / te;
+            s_row0 = p.offsets[x] + mloc * BM;
+            s_rows = min(BM, m - mloc * BM);
+            break;
+          }
+          acc += te * p.n_tiles;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int e = s_e;
+  if (e < 0) return;
+  const int row0 = s_row0, rows = s_rows;
+  const int n0 = s_nt * (UP ? BNB / 2 : BNB);
+
+  // ---- per-lane DMA offsets -----------------------------------------------
+  // Run j of wave w fills LDS chunks q = (4 j + w) * 64 + lane, i.e. row
+  // (4 j + w) * RPR + lane / CPR, stored chunk lane % CPR, which must hold
+  // global chunk c = stored ^ key(row).  key(row) is the same for every run
+  // of a wave: BK = 64: (4 (w % 2) + lane / 16) % 8;  BK = 32: lane / 16.
+  const int c = BK == 64 ? ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7))
+                         : ((lane & 3) ^ (lane >> 4));
+  const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, p.a_bytes);
+  // Valid offsets are < 2^31 (checked on the host); an invalid row carries
+  // bit 31 and the K tail ORs it in, so such lanes read zeros.
+  uint32_t a_off[T::A_RUNS];
+#pragma unroll
+  for (int j = 0; j < T::A_RUNS; ++j) {
+    const int r = (kNW * j + wave) * T::RPR + lane / T::CPR;
+    uint32_t off = kOOB;
+    if (r < rows) {
+      const int src = GATHER ? p.perm[row0 + r] : row0 + r;
+      off = ((uint32_t)src * (uint32_t)K + (uint32_t)c * 8u) * 2u;
+    }
+    a_off[j] = off;
+  }
+  const size_t mat_elems = (size_t)N * K;
+  __amdgpu_buffer_rsrc_t rb0, rb1;
+  uint32_t b_off[MX ? 1 : T::B_RUNS];
+  if constexpr (!MX) {
+    rb0 = rsrc((const uint16_t *)p.b0 + (size_t)e * mat_elems, (uint32_t)(mat_elems * 2));
+    rb1 = UP ? rsrc((const uint16_t *)p.b1 + (size_t)e * mat_elems, (uint32_t)(mat_elems * 2))
+             : rb0;
+#pragma unroll
+    for (int j = 0; j < T::B_RUNS; ++j) {
+      const int br = (kNW * j + wave) * T::RPR + lane / T::CPR;
+      const int n = UP ? n0 + (br % (BNB / 2)) : n0 + br;
+      b_off[j] = n < N ? ((uint32_t)n * (uint32_t)K + (uint32_t)c * 8u) * 2u : kOOB;
+    }
+  }
+  // MXFP4 units: thread owns (B-row, 32-K block) pairs u = tid + kNT i.
+  const uint8_t *q_src[MX ? T::MX_UNITS : 1];
+  const uint8_t *s_src[MX ? T::MX_UNITS : 1];
+  bool q_ok[MX ? T::MX_UNITS : 1];
+  if constexpr (MX) {
+#pragma unroll
+    for (int i = 0; i < T::MX_UNITS; ++i) {
+      const int u = min(tid + kNT * i, T::MX_ALL - 1);
+      const int br = u / (BK / 32), half = u % (BK / 32);
+      const bool second = UP && br >= BNB / 2;
+      const int n = UP ? n0 + (br % (BNB / 2)) : n0 + br;
+      q_ok[i] = n < N && tid + kNT * i < T::MX_ALL;
+      const size_t nr = (size_t)e * N + (q_ok[i] ? n : 0);
+      q_src[i] = (const uint8_t *)(second ? p.b1 : p.b0) + nr * (K / 2) + half * 16;
+      s_src[i] = (second ? p.s1 : p.s0) + nr * (K / 32) + half;
+    }
+  }
+
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  u32x4 mq[MX ? T::MX_UNITS : 1];
+  uint32_t ms[MX ? T::MX_UNITS : 1];
+
+  // Issue the loads of K step kt into LDS stage `stage` (a step at or past
+  // the end issues only zero loads, which keeps the count per step fixed).
+  auto issue = [&](int kt, int stage) {
+    const int k0 = kt * BK;
+    const uint32_t kpen = (k0 + c * 8 < K) ? 0u : kOOB;
+    const uint32_t k0b = (uint32_t)k0 * 2u;
+    uint8_t *sa = smem + stage * T::STAGE;
+#pragma unroll
+    for (int j = 0; j < T::A_RUNS; ++j) dma16(ra, sa + (kNW * j + wave) * 1024, (a_off[j] + k0b) | kpen);
+    if constexpr (!MX) {
+      uint8_t *sb = sa + T::A_BYTES;
+#pragma unroll
+      for (int j = 0; j < T::B_RUNS; ++j) {
+        const bool second = UP && (kNW * j + wave) * T::RPR >= BNB / 2;
+        dma16(second ? rb1 : rb0, sb + (kNW * j + wave) * 1024, (b_off[j] + k0b) | kpen);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::MX_UNITS; ++i) {
+        const int half = (tid + kNT * i) % (BK / 32);
+        const bool ok = q_ok[i] && (k0 + half * 32 < K);
+        mq[i] = ok ? *(const u32x4 *)(q_src[i] + k0 / 2) : zero4;
+        ms[i] = ok ? (uint32_t)s_src[i][k0 / 32] : 0u;
+      }
+    }
+  };
+  // MXFP4: dequantise the staged codes into the stage's B tile.
+  auto mx_store = [&](int stage) {
+    if constexpr (MX) {
+      uint8_t *sb = smem + stage * T::STAGE + T::A_BYTES;
+#pragma unroll
+      for (int i = 0; i < T::MX_UNITS; ++i) {
+        const int u = tid + kNT * i;
+        if (T::MX_ALL % kNT != 0 && u >= T::MX_ALL) continue;
+        const int br = u / (BK / 32), half = u % (BK / 32);
+        const float sc = e8m0_to_f32(ms[i]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t wv = mq[i][q];
+          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 0);
+          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 1);
+          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 2);
+          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 3);
+          const u32x4 o = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+          *(u32x4 *)(sb + swz<BK>(br, half * 4 + q)) = o;
+        }
+      }
+    }
+  };
+
+  const int wm = wave / (kNW / 2), wn = wave % (kNW / 2);
+  const int lr = lane & 31, lg = lane >> 5;
+  f32x16 acc[T::TM][T::TN];
+#pragma unroll
+  for (int a = 0; a < T::TM; ++a)
+#pragma unroll
+    for (int b = 0; b < T::TN; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  // B-row of wave-subtile j: up = gate rows then the matching value rows.
+  auto brow = [&](int j) {
+    if (UP)
+      return j < T::TN / 2 ? wn * (T::WN / 2) + j * 32 + lr
+                           : BNB / 2 + wn * (T::WN / 2) + (j - T::TN / 2) * 32 + lr;
+    return wn * T::WN + j * 32 + lr;
+  };
+
+  // One K step = SLICES MFMA k-slices of 16.  Fragments of slice kk + 1 are
+  // read while the MFMAs of slice kk run; scheduling groups pin the order
+  // "MFMA, LDS read, MFMA, LDS read, ..." inside a slice (and spread the DMA
+  // issue of a later step over slice 0), and slices do not mix.
+  auto read_frags = [&](const uint8_t *sa, const uint8_t *sb, int kk, bf16x8 *af, bf16x8 *bfr) {
+    const int ch = kk * 2 + lg;
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm)
+      af[tm] = *(const bf16x8 *)(sa + swz<BK>(wm * T::WM + tm * 32 + lr, ch));
+#pragma unroll
+    for (int tn = 0; tn < T::TN; ++tn) bfr[tn] = *(const bf16x8 *)(sb + swz<BK>(brow(tn), ch));
+  };
+  auto mfmas = [&](const bf16x8 *af, const bf16x8 *bfr) {
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < T::TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
+  };
+  constexpr int NF = T::TM + T::TN;                     // fragment reads per slice
+  constexpr int NM = T::TM * T::TN;                     // MFMAs per slice
+  constexpr int NV = T::A_RUNS + (MX ? 0 : T::B_RUNS);  // DMA issues per step
+  auto step = [&](int stage, int kt_issue, int stage_issue) {
+    const uint8_t *sa = smem + stage * T::STAGE;
+    const uint8_t *sb = sa + T::A_BYTES;
+    bf16x8 a0[T::TM], b0[T::TN], a1[T::TM], b1[T::TN];
+    read_frags(sa, sb, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < T::SLICES; ++kk) {
+      bf16x8 *ac = (kk & 1) ? a1 : a0, *bc = (kk & 1) ? b1 : b0;
+      bf16x8 *an = (kk & 1) ? a0 : a1, *bn = (kk & 1) ? b0 : b1;
+      if (kk + 1 < T::SLICES) read_frags(sa, sb, kk + 1, an, bn);
+      if (kk == 0) issue(kt_issue, stage_issue);
+      mfmas(ac, bc);
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (kk + 1 < T::SLICES && i < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (kk == 0 && i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s, s);
+  mx_store(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // Step kt's loads are done once at most NST - 2 later steps are pending.
+    wait_vmcnt<(NST - 2) * NV>();
+    __syncthreads();
+    step(kt % NST, kt + NST - 1, (kt + NST - 1) % NST);
+    if (MX && kt + 1 < nk) mx_store((kt + 1) % NST);
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue --------------------------------------------------------------
+  // 32x32 accumulator: element i of lane l is row (i/4)*8 + (l/32)*4 + i%4,
+  // column l % 32.
+  if constexpr (UP || FUSE) {
+    // bf16 output staged through LDS so that global stores are 16-B rows.
+    constexpr int OC = UP ? BNB / 2 : BNB;  // output columns of the tile
+    constexpr int PITCH = OC * 2 + 16;       // bytes per staged row (padded)
+    __syncthreads();  // every wave is done reading the stages
+    uint8_t *so = smem;
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) {
+#pragma unroll
+      for (int j = 0; j < (UP ? T::TN / 2 : T::TN); ++j) {
+        const int col = (UP ? wn * (T::WN / 2) : wn * T::WN) + j * 32 + lr;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm * T::WM + tm * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
+          float v;
+          if constexpr (UP) {
+            v = silu(acc[tm][j][i]) * acc[tm][j + T::TN / 2][i];
+          } else {
+            const int rr = row0 + min(r, rows - 1);
+            v = acc[tm][j][i] * p.comb_w[p.perm_out[rr]];
+          }
+          *(uint16_t *)(so + r * PITCH + col * 2) = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CH = OC / 8;  // 16-B chunks per row
+    for (int idx = tid; idx < BM * CH; idx += kNT) {
+      const int r = idx / CH, ch = idx % CH;
+      const int col = n0 + ch * 8;
+      if (r < rows && col < N) {
+        const u32x4 v = *(const u32x4 *)(so + r * PITCH + ch * 16);
+        uint16_t *dst;
+        if constexpr (UP)
+          dst = (uint16_t *)p.out + (size_t)(row0 + r) * N + col;
+        else
+          dst = (uint16_t *)p.out + (size_t)p.perm_out[row0 + r] * N + col;
+        if (col + 8 <= N) {
+          *(u32x4 *)dst = v;
+        } else {
+          const uint16_t *vs = (const uint16_t *)&v;
+          for (int t = 0; t < N - col; ++t) dst[t] = vs[t];
+        }
+      }
+    }
+  } else {
+    float *y = (float *)p.out;
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < T::TN; ++tn) {
+        const int col = n0 + wn * T::WN + tn * 32 + lr;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm * T::WM + tm * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
+          if (r < rows && col < N) y[(size_t)(row0 + r) * N + col] = acc[tm][tn][i];
+        }
+      }
+  }
+}
+
+template <bool UP, bool MX, bool GATHER, bool FUSE, int BM, int BNB>
+hipError_t launch_one(const BigGemmParams &p, int blocks, hipStream_t st) {
+  using T = Tile<BM, BNB, MX ? 64 : MOE_BF16_BK>;
+  constexpr int NST = MX ? 2 : MOE_BF16_NST;
+  constexpr int OC = UP ? BNB / 2 : BNB;
+  constexpr int EPI = (UP || FUSE) ? BM * (OC * 2 + 16) : 0;
+  constexpr int lds = NST * T::STAGE > EPI ? NST * T::STAGE : EPI;
+  auto kern = big_gemm_kernel<UP, MX, GATHER, FUSE, BM, BNB>;
+  // Dynamic LDS above 64 KB must be allowed once per device.
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_done.load(std::memory_order_acquire) & bit)) {
+    err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (err != hipSuccess) return err;
+    attr_done.fetch_or(bit, std::memory_order_release);
+  }
+  kern<<<blocks, kNT, lds, st>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_big_gemm(const BigGemmParams &p, bool up, bool mx, bool gather, bool fuse,
+                           int bm, int bnb, hipStream_t st) {
+  const int m_tiles = (p.R + bm - 1) / bm + (p.E < p.R ? p.E : p.R);
+  const int blocks = m_tiles * p.n_tiles;
+#define MOE_BIG(U, M, G, F, A, B)                                             \
+  if (up == U && mx == M && gather == G && fuse == F && bm == A && bnb == B) \
+    return launch_one<U, M, G, F, A, B>(p, blocks, st);
+  // up: gather from X or contiguous rows; bf16 or MXFP4 weights
+  MOE_BIG(true, false, true, false, 256, 256)
+  MOE_BIG(true, false, false, false, 256, 256)
+  MOE_BIG(true, true, true, false, 256, 256)
+  MOE_BIG(true, true, false, false, 256, 256)
+  // down: f32 pile outputs, or the combine fused for one expert per token
+  MOE_BIG(false, false, false, false, 256, 256)
+  MOE_BIG(false, false, false, false, 256, 128)
+  MOE_BIG(false, false, false, false, 128, 128)
+  MOE_BIG(false, false, false, true, 256, 256)
+  MOE_BIG(false, false, false, true, 256, 128)
+  MOE_BIG(false, false, false, true, 128, 128)
+  MOE_BIG(false, true, false, false, 256, 256)
+  MOE_BIG(false, true, false, false, 256, 128)
+  MOE_BIG(false, true, false, false, 128, 128)
+  MOE_BIG(false, true, false, true, 256, 256)
+  MOE_BIG(false, true, false, true, 256, 128)
+  MOE_BIG(false, true, false, true, 128, 128)
+#undef MOE_BIG
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

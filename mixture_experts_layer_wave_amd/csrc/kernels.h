@@ -35,10 +35,17 @@ struct FfnArgs {
   const uint8_t *s1, *s3, *s2;
   void *h;                // [R][d_ff] hidden (bf16, or f32 for f32 weights)
   float *y_perm;          // [R][d] f32
+  int n, k;               // tokens and experts per token
+  // Optional combine fused into the down-projection (used when k == 1):
+  // y[perm[r]] = w[perm[r]] * (h[r] W2^T), bf16 [n][d].
+  void *fuse_y;
+  const int32_t *fuse_perm;
+  const float *fuse_w;
 };
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st);    // A -> h
-hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st);  // h -> y_perm
-hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st);  // both
+// h -> y_perm, or straight into fuse_y; *fused (may be NULL) tells which.
+hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
+hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
 
 // ---- combine --------------------------------------------------------------
 hipError_t launch_combine(const float *y_perm, const int32_t *inv, const float *w,

@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/moe.h: argument validation,
 // workspace layout and the launch sequence on the caller's stream.  Nothing
 // here allocates device memory or synchronises with the host.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -99,6 +99,8 @@ moe::FfnArgs ffn_args(const moe_shape *s, const void *a, const int32_t *perm,
   f.s2 = w->s2;
   f.h = h;
   f.y_perm = yp;
+  f.n = s->n;
+  f.k = s->k;
   return f;
 }
 
@@ -254,9 +256,17 @@ int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, cons
     e = moe::launch_router_topk(logits, s->n, s->E, s->k, renorm_of(s), idx, wt, hs);
   if (e == hipSuccess)
     e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
-  if (e == hipSuccess)
-    e = moe::launch_grouped_ffn(ffn_args(s, x, perm, offsets, w, base + L.h, yp), hs);
-  if (e == hipSuccess)
+  bool fused = false;
+  if (e == hipSuccess) {
+    moe::FfnArgs f = ffn_args(s, x, perm, offsets, w, base + L.h, yp);
+    if (s->k == 1 && out == MOE_BF16) {  // one expert per token: scale-and-scatter in the down pass
+      f.fuse_y = y;
+      f.fuse_perm = perm;
+      f.fuse_w = wt;
+    }
+    e = moe::launch_grouped_ffn(f, hs, &fused);
+  }
+  if (e == hipSuccess && !fused)
     e = moe::launch_combine(yp, inv, wt, s->n, s->k, s->d, y, out == MOE_BF16, hs);
   return hip_status(e);
 }
