@@ -80,7 +80,8 @@ typedef struct {
  * For MXFP4, w1/w3 are [E][d_ff][d/2] bytes and w2 is [E][d][d_ff/2] bytes,
  * with scales s1/s3 [E][d_ff][d/32] and s2 [E][d][d_ff/32]; s* are NULL for
  * the other dtypes.  F32 weights require F32 activations; BF16 and MXFP4
- * weights require BF16 activations. */
+ * weights require BF16 activations.  BF16/MXFP4 weight and scale pointers
+ * must be 16-byte aligned (MOE_ERR_ALIGN otherwise). */
 typedef struct {
   int32_t dtype; /* moe_dtype */
   const void *w1, *w3, *w2;

@@ -59,6 +59,16 @@ __device__ __forceinline__ void wave_argmax(float &v, int &i) {
   }
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global access of the wave (stores and direct-to-LDS
+// copies share one counter), which would drain a copy pipeline; copies into
+// LDS are waited for explicitly with s_waitcnt vmcnt before this barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // E8M0 scale code -> float (2^(s-127)); 0 -> 2^-127 (subnormal), 255 -> NaN.

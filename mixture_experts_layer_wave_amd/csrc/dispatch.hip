@@ -5,23 +5,14 @@
 // out, in their original order, into that expert's input matrix; a pile can
 // be empty, and pile sizes depend on the data only.
 //
-// One workgroup of 1024 threads does the whole job deterministically:
-//   1. histogram of expert ids in LDS (integer atomics: order-independent),
-//   2. exclusive scan -> offsets,
-//   3. stable placement in chunks of 1024 pairs, in (token, slot) order.  A
-//      lane's rank among same-expert lanes of its wave comes from ballots on
-//      the bits of the expert id; ranks across the 16 waves of the chunk come
-//      from a per-wave count table; a per-expert cursor carries the count of
-//      earlier chunks.  No atomics decide positions, so the result is the
-//      unique stable grouping.
+// One workgroup of 1024 threads does the whole job deterministically (see
+// dispatch_block in route_dev.h).
 #include "common.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
-
-constexpr int kDispThreads = 1024;
-constexpr int kDispWaves = kDispThreads / MOE_WAVE;
 
 __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t *__restrict__ idx, int R,
                                                         int k, int E, int nbits,
@@ -30,73 +21,23 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t *__restric
                                                         int32_t *__restrict__ perm,
                                                         int32_t *__restrict__ inv) {
   extern __shared__ int smem[];
-  int *s_cnt = smem;               // [E]   histogram
-  int *s_cur = s_cnt + E;          // [E]   placement cursor (starts at offsets)
-  int *s_wc = s_cur + E;           // [16][E] per-wave counts of the current chunk
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  dispatch_block(idx, R, k, E, nbits, counts, offsets, perm, inv, smem);
+}
 
-  for (int e = tid; e < E; e += kDispThreads) s_cnt[e] = 0;
-  for (int i = tid; i < kDispWaves * E; i += kDispThreads) s_wc[i] = 0;
+// Small batches: top-k of every token (one wave per token, see topk_token)
+// and the dispatch in one workgroup, saving a launch on the decode path.
+__global__ __launch_bounds__(1024) void route_dispatch_kernel(
+    const float *__restrict__ part, int S, int n, int E, int k, int renorm, int nbits,
+    int32_t *__restrict__ idx, float *__restrict__ w, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ inv) {
+  extern __shared__ int smem[];
+  int *s_idx = smem + dispatch_lds_ints(E);  // [n * k] chosen experts
+  const int G = topk_group(E);
+  for (int t0 = 0; t0 < n; t0 += kDispThreads / G)  // uniform trip count
+    topk_token(part, S, (size_t)n * E, t0 + threadIdx.x / G, n, E, k, renorm, idx, w, nullptr,
+               s_idx);
   __syncthreads();
-  for (int r = tid; r < R; r += kDispThreads) {
-    const int e = idx[r];
-    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int carry = 0;
-    for (int base = 0; base < E; base += MOE_WAVE) {
-      const int e = base + lane;
-      const int c = e < E ? s_cnt[e] : 0;
-      int incl = c;
-#pragma unroll
-      for (int o = 1; o < MOE_WAVE; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      if (e < E) {
-        s_cur[e] = carry + incl - c;
-        counts[e] = c;
-        offsets[e] = carry + incl - c;
-      }
-      carry += __shfl(incl, MOE_WAVE - 1, 64);
-    }
-    if (lane == 0) offsets[E] = carry;
-  }
-  __syncthreads();
-
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < R; c0 += kDispThreads) {
-    const int r = c0 + tid;
-    int e = r < R ? idx[r] : -1;
-    const bool valid = e >= 0 && e < E;
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bal = __ballot(bit);
-      same &= bit ? bal : ~bal;
-    }
-    const int rank = __popcll(same & lt_mask);
-    if (valid && rank == 0) s_wc[wave * E + e] = __popcll(same);
-    __syncthreads();
-    if (valid) {
-      int base = s_cur[e];
-      for (int w = 0; w < wave; ++w) base += s_wc[w * E + e];
-      const int pos = base + rank;
-      perm[pos] = r / k;
-      inv[r] = pos;
-    }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += kDispThreads) {
-      int add = 0;
-      for (int w = 0; w < kDispWaves; ++w) {
-        add += s_wc[w * E + ee];
-        s_wc[w * E + ee] = 0;
-      }
-      s_cur[ee] += add;
-    }
-    __syncthreads();
-  }
+  dispatch_block(s_idx, n * k, k, E, nbits, counts, offsets, perm, inv, smem);
 }
 
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t *__restrict__ x,
@@ -118,18 +59,38 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t *__rest
 
 }  // namespace
 
-hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *counts,
-                           int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t st) {
+static int id_bits(int E) {
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-  const size_t lds = sizeof(int) * (size_t)E * (2 + kDispWaves);
-  if (lds > 64 * 1024) {
-    hipError_t err = hipFuncSetAttribute((const void *)dispatch_kernel,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-  }
-  dispatch_kernel<<<1, kDispThreads, lds, st>>>(idx, n * k, k, E, nbits, counts, offsets, perm,
-                                                inv);
+  return nbits;
+}
+
+template <typename K>
+static hipError_t allow_lds(K kern, size_t lds) {
+  if (lds <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds);
+}
+
+hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *counts,
+                           int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t st) {
+  const size_t lds = sizeof(int) * (size_t)dispatch_lds_ints(E);
+  hipError_t err = allow_lds(dispatch_kernel, lds);
+  if (err != hipSuccess) return err;
+  dispatch_kernel<<<1, kDispThreads, lds, st>>>(idx, n * k, k, E, id_bits(E), counts, offsets,
+                                                perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_dispatch(const float *part, int splits, int n, int E, int k, bool renorm,
+                                 int32_t *idx, float *w, int32_t *counts, int32_t *offsets,
+                                 int32_t *perm, int32_t *inv, hipStream_t st) {
+  const size_t lds = sizeof(int) * ((size_t)dispatch_lds_ints(E) + (size_t)n * k);
+  hipError_t err = allow_lds(route_dispatch_kernel, lds);
+  if (err != hipSuccess) return err;
+  route_dispatch_kernel<<<1, kDispThreads, lds, st>>>(part, splits, n, E, k, renorm ? 1 : 0,
+                                                      id_bits(E), idx, w, counts, offsets, perm,
+                                                      inv);
   return hipGetLastError();
 }
 

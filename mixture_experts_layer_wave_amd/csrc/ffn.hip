@@ -362,8 +362,17 @@ BigGemmParams big_params(const FfnArgs &a, bool up) {
 
 }  // namespace
 
+// Small batches of MXFP4 experts are bound by reading the weights: they take
+// the weight-streaming kernel instead of the large-tile GEMM.
+constexpr int kDecodeMaxRows = 1024;
+
+bool use_decode(const FfnArgs &a) {
+  return a.w_dtype == 2 && a.R <= kDecodeMaxRows && decode_ffn_fits(a.d, a.d_ff, a.E);
+}
+
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
+  if (use_decode(a)) return launch_decode_up(a, st);
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d_ff;
     ffn_up_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
@@ -398,6 +407,7 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
 hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
   if (fused) *fused = false;
   if (a.R == 0) return hipSuccess;
+  if (use_decode(a)) return launch_decode_down(a, st);
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d;
     ffn_down_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(

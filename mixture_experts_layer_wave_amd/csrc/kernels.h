@@ -8,18 +8,28 @@
 namespace moe {
 
 // ---- router ---------------------------------------------------------------
-// logits[n][E] = x[n][d] . wg[E][d] (+ bias[E]); x, wg are bf16 (is_bf16) or f32.
-hipError_t launch_router_logits(const void *x, const void *wg, const float *bias,
-                                float *logits, int n, int d, int E, bool is_bf16,
-                                hipStream_t st);
-// idx/w[n][k] from logits[n][E]: softmax over E, top-k, optional renorm.
-hipError_t launch_router_topk(const float *logits, int n, int E, int k, bool renorm,
-                              int32_t *idx, float *w, hipStream_t st);
+// Number of K splits the router logits use for this shape (>= 1; a function
+// of d alone).  Split s writes part[s][n][E]; the top-k pass sums the splits
+// in order.
+int router_splits(int n, int E, int d);
+// part[s][n][E] = x[n][d] . wg[E][d] over split s's K range (+ bias[E] in
+// split 0); x, wg are bf16 (is_bf16) or f32 (f32 always uses one split).
+hipError_t launch_router_logits(const void *x, const void *wg, const float *bias, float *part,
+                                int n, int d, int E, bool is_bf16, int splits, hipStream_t st);
+// idx/w[n][k] from the summed logits: softmax over E, top-k, optional
+// renorm; logits[n][E] (may be NULL) receives the summed logits.
+hipError_t launch_router_topk(const float *part, int splits, int n, int E, int k, bool renorm,
+                              int32_t *idx, float *w, float *logits, hipStream_t st);
 
 // ---- dispatch -------------------------------------------------------------
 hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *counts,
                            int32_t *offsets, int32_t *perm, int32_t *inv,
                            hipStream_t st);
+// Top-k and dispatch in one workgroup (small batches: n <= kRouteSmallN).
+constexpr int kRouteSmallN = 64;
+hipError_t launch_route_dispatch(const float *part, int splits, int n, int E, int k, bool renorm,
+                                 int32_t *idx, float *w, int32_t *counts, int32_t *offsets,
+                                 int32_t *perm, int32_t *inv, hipStream_t st);
 // x_perm[r] = x[perm[r]] for r < R, rows of row_bytes bytes (multiple of 4).
 hipError_t launch_gather_rows(const void *x, const int32_t *perm, void *x_perm, int R,
                               int row_bytes, hipStream_t st);
@@ -46,6 +56,13 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st);    // A -> h
 // h -> y_perm, or straight into fuse_y; *fused (may be NULL) tells which.
 hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
 hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
+
+// Small-batch MXFP4 path (decode.hip): persistent workgroups stream 16-row
+// weight tiles through an LDS ring.  decode_ffn_fits tells whether the
+// shape is supported.
+bool decode_ffn_fits(int d, int d_ff, int E);
+hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st);
+hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st);
 
 // ---- combine --------------------------------------------------------------
 hipError_t launch_combine(const float *y_perm, const int32_t *inv, const float *w,

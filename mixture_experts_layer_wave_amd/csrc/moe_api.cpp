@@ -45,6 +45,11 @@ int check_dtypes(const moe_shape *s, int act, int wdt) {
   return MOE_OK;
 }
 
+// K splits of the router logits (the bf16 MFMA router only).
+int splits_of(const moe_shape *s, int wdt) {
+  return (wdt == MOE_F32 || s->d % 8) ? 1 : moe::router_splits(s->n, s->E, s->d);
+}
+
 WsLayout layout(const moe_shape *s, int wdt) {
   WsLayout L{};
   size_t o = 0;
@@ -54,7 +59,7 @@ WsLayout layout(const moe_shape *s, int wdt) {
     return at;
   };
   const size_t n = (size_t)s->n, E = (size_t)s->E, R = n * (size_t)s->k;
-  L.logits = take(n * E * 4);
+  L.logits = take((size_t)splits_of(s, wdt) * n * E * 4);  // per-split partial logits
   L.idx = take(R * 4);
   L.w = take(R * 4);
   L.counts = take(E * 4);
@@ -74,6 +79,8 @@ int check_weights(const moe_shape *s, int act, const moe_expert_weights *w) {
   if (!w->w1 || !w->w3 || !w->w2) return MOE_ERR_NULL;
   if (w->dtype == MOE_MXFP4 && (!w->s1 || !w->s3 || !w->s2)) return MOE_ERR_NULL;
   if (w->dtype != MOE_F32 && (!aligned16(w->w1) || !aligned16(w->w3) || !aligned16(w->w2)))
+    return MOE_ERR_ALIGN;
+  if (w->dtype == MOE_MXFP4 && (!aligned16(w->s1) || !aligned16(w->s3) || !aligned16(w->s2)))
     return MOE_ERR_ALIGN;
   return MOE_OK;
 }
@@ -140,10 +147,10 @@ int moe_router_topk(const moe_shape *s, const void *x, int act, const void *wg,
     return MOE_ERR_ALIGN;
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = moe::launch_router_logits(x, wg, bias, logits, s->n, s->d, s->E,
-                                           act == MOE_BF16, hs);
+                                           act == MOE_BF16, 1, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_router_topk(logits, s->n, s->E, s->k, renorm_of(s), topk_idx,
-                                            topk_w, hs));
+  return hip_status(moe::launch_router_topk(logits, 1, s->n, s->E, s->k, renorm_of(s), topk_idx,
+                                            topk_w, nullptr, hs));
 }
 
 int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
@@ -250,12 +257,20 @@ int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, cons
   float *yp = (float *)(base + L.yp);
   hipStream_t hs = (hipStream_t)stream;
 
+  const int splits = splits_of(s, w->dtype);
   hipError_t e = moe::launch_router_logits(x, wg, bias, logits, s->n, s->d, s->E,
-                                           act == MOE_BF16, hs);
-  if (e == hipSuccess)
-    e = moe::launch_router_topk(logits, s->n, s->E, s->k, renorm_of(s), idx, wt, hs);
-  if (e == hipSuccess)
-    e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
+                                           act == MOE_BF16, splits, hs);
+  if (e == hipSuccess) {
+    if (s->n <= moe::kRouteSmallN) {  // top-k and dispatch in one workgroup
+      e = moe::launch_route_dispatch(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt,
+                                     counts, offsets, perm, inv, hs);
+    } else {
+      e = moe::launch_router_topk(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt,
+                                  nullptr, hs);
+      if (e == hipSuccess)
+        e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
+    }
+  }
   bool fused = false;
   if (e == hipSuccess) {
     moe::FfnArgs f = ffn_args(s, x, perm, offsets, w, base + L.h, yp);

@@ -1,0 +1,327 @@
+// Device-side building blocks shared by the router and dispatch kernels.
+//
+//   topk_token:   softmax over E logits, top-k selection and combine weights
+//                 for one token, executed by one wave ("How Mixture of Experts
+//                 Scales Model Parameters", sections "Routing: a router scores
+//                 the experts, and the top one runs" and "Top-K: several
+//                 experts, added up by weight"; the softmax subtracts the row
+//                 maximum first, "Why FlashAttention is So Fast", section "A
+//                 fused kernel, and an overflow problem").
+//   dispatch_block: stable regrouping of (token, slot) pairs into per-expert
+//                 piles by one 1024-thread workgroup (section "The forward
+//                 pass: dispatch, then combine").
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace moe {
+
+
+// Lane-group width for E experts: the next power of two >= E, at most 64.
+__host__ __device__ constexpr int topk_group(int E) {
+  int g = 1;
+  while (g < E && g < MOE_WAVE) g <<= 1;
+  return g;
+}
+
+// Reductions over aligned groups of G lanes (G a power of two <= 64), with
+// the result in every lane of the group.  Within a 16-lane row the steps are
+// DPP lane permutations (lane pairs 1 and 2 apart, then the 8- and 16-lane
+// mirrors), which cost a few cycles where a cross-lane shuffle through the
+// LDS crossbar costs a memory round trip; rows are then combined with
+// readlane.  The combination order is fixed, so results are deterministic.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
+
+template <typename T, typename Op>
+__device__ __forceinline__ T group_reduce(T v, int G, Op op) {
+  auto dpp = [](T x, auto ctrl_tag) {
+    constexpr int C = decltype(ctrl_tag)::value;
+    if constexpr (sizeof(T) == 4 && __is_same(T, float)) return dpp_f<C>(x);
+    else return (T)dpp_i<C>((int)x);
+  };
+  if (G >= 2) v = op(v, dpp(v, std::integral_constant<int, kDppXor1>{}));
+  if (G >= 4) v = op(v, dpp(v, std::integral_constant<int, kDppXor2>{}));
+  if (G >= 8) v = op(v, dpp(v, std::integral_constant<int, kDppHalfMirror>{}));
+  if (G >= 16) v = op(v, dpp(v, std::integral_constant<int, kDppMirror>{}));
+  if (G >= 32) {
+    const int lane = threadIdx.x & 63;
+    const T r0 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const T r1 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const T r2 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const T r3 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    if (G == 64) v = op(op(r0, r1), op(r2, r3));
+    else v = lane < 32 ? op(r0, r1) : op(r2, r3);
+  }
+  return v;
+}
+__device__ __forceinline__ float group_max(float v, int G) {
+  return group_reduce(v, G, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float group_sum(float v, int G) {
+  return group_reduce(v, G, [](float a, float b) { return a + b; });
+}
+__device__ __forceinline__ int group_min_i(int v, int G) {
+  return group_reduce(v, G, [](int a, int b) { return a < b ? a : b; });
+}
+// Best (value, lowest index) of the group: the maximum value, then the
+// smallest index among the lanes holding it.
+__device__ __forceinline__ void group_argmax(float &v, int &i, int G) {
+  const float m = group_max(v, G);
+  i = group_min_i(v == m ? i : 0x7fffffff, G);
+  v = m;
+}
+
+// One token per group of G = topk_group(E) lanes (64 / G tokens per wave;
+// every lane of the wave must call it, with t >= n marking idle groups).
+// The token's logits are the sum, in split order, of S partial rows
+// part[s * part_stride + t * E + e] (S = 1: the logits themselves).  Lane
+// l of a group owns experts l, l + G, ...; each of the k rounds takes the
+// group-wide best (value, lowest index) among experts not yet taken.
+// Weights: exp(z - max) over the sum for all E, or over the chosen k when
+// renormalising.  If logits_out is given the summed logits are stored too.
+// PER = expert slots per lane (a compile-time bound on ceil(E / G)).
+template <int PER>
+__device__ __forceinline__ void topk_token_t(const float *__restrict__ part, int S,
+                                             size_t part_stride, int t, int n, int E, int k,
+                                             int renorm, int32_t *__restrict__ idx,
+                                             float *__restrict__ w,
+                                             float *__restrict__ logits_out, int *lds_idx) {
+  constexpr int kTopkPer = PER;
+  const int G = topk_group(E);
+  const int gl = (threadIdx.x & 63) & (G - 1);  // lane within the group
+  const bool live = t < n;
+  const float NEG = -__builtin_inff();
+  float v[kTopkPer];
+  const float *pz = part + (size_t)t * E + gl;
+  // Split-major: each split's loads for all expert slots are independent,
+  // and every slot accumulates its splits in order (deterministic).
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) v[j] = (live && gl + G * j < E) ? pz[G * j] : NEG;
+  constexpr int kBatch = kTopkPer >= 32 ? 1 : 32 / kTopkPer;  // splits loaded per batch
+  for (int s0 = 1; s0 < S; s0 += kBatch) {
+    float q[kBatch][kTopkPer];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int j = 0; j < kTopkPer; ++j)
+        q[u][j] = (s0 + u < S && live && gl + G * j < E)
+                      ? pz[(size_t)(s0 + u) * part_stride + G * j] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int j = 0; j < kTopkPer; ++j)
+        if (s0 + u < S) v[j] += q[u][j];
+  }
+  float m = NEG;
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) {
+    if (logits_out && live && gl + G * j < E) logits_out[(size_t)t * E + gl + G * j] = v[j];
+    m = fmaxf(m, v[j]);
+  }
+  m = group_max(m, G);
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j)
+    if (live && gl + G * j < E) sum += expf(v[j] - m);
+  sum = group_sum(sum, G);
+
+  uint32_t taken = 0;
+  float my_v = NEG;
+  int my_i = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = NEG;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kTopkPer; ++j) {
+      const int e = gl + G * j;
+      const bool ok = e < E && !((taken >> j) & 1u);
+      if (ok && (v[j] > bv || (v[j] == bv && e < bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+    group_argmax(bv, bi, G);
+    if (bi < E && (bi & (G - 1)) == gl) taken |= 1u << (bi / G);
+    if (gl == r) {
+      my_v = bv;
+      my_i = bi;
+    }
+  }
+  // k <= G always (k <= E <= G, or G = 64 >= 32 >= k).
+  const float num = gl < k ? expf(my_v - m) : 0.f;
+  float den = sum;
+  if (renorm) den = group_sum(num, G);
+  if (live && gl < k) {
+    idx[(size_t)t * k + gl] = my_i;
+    w[(size_t)t * k + gl] = num / den;
+    if (lds_idx) lds_idx[t * k + gl] = my_i;
+  }
+}
+
+// lds_idx (may be NULL) receives a copy of the chosen experts.
+__device__ __forceinline__ void topk_token(const float *__restrict__ part, int S,
+                                           size_t part_stride, int t, int n, int E, int k,
+                                           int renorm, int32_t *__restrict__ idx,
+                                           float *__restrict__ w,
+                                           float *__restrict__ logits_out,
+                                           int *lds_idx = nullptr) {
+  if (E <= 2 * MOE_WAVE)
+    topk_token_t<2>(part, S, part_stride, t, n, E, k, renorm, idx, w, logits_out, lds_idx);
+  else if (E <= 4 * MOE_WAVE)
+    topk_token_t<4>(part, S, part_stride, t, n, E, k, renorm, idx, w, logits_out, lds_idx);
+  else
+    topk_token_t<MOE_MAX_E / MOE_WAVE>(part, S, part_stride, t, n, E, k, renorm, idx, w,
+                                       logits_out, lds_idx);
+}
+
+constexpr int kDispThreads = 1024;
+constexpr int kDispWaves = kDispThreads / MOE_WAVE;
+
+// LDS ints needed by dispatch_block.
+__host__ __device__ constexpr int dispatch_lds_ints(int E) { return E * (2 + 2 * kDispWaves); }
+
+// Whole workgroup of kDispThreads, deterministic:
+//   1. stable ranks: the pairs are taken in chunks of 1024 in (token, slot)
+//      order.  A lane's rank among same-expert lanes of its wave comes from
+//      ballots on the bits of the expert id; a per-wave count table, scanned
+//      per expert, gives each (wave, expert) its first rank in the chunk, and
+//      a per-expert cursor carries the earlier chunks;
+//   2. the cursors are now the pile sizes: exclusive scan -> offsets;
+//   3. every pair moves to offsets[e] + rank (perm, inv).
+// No atomics decide positions, so the result is the unique stable grouping.
+// Ids outside [0, E) are skipped.  The ids and ranks of up to kDispRegChunks
+// chunks stay in registers (a barrier waits for outstanding global stores,
+// so none are issued before the end); longer inputs park ranks in inv[].
+// `idx` may point to LDS or global memory.
+constexpr int kDispRegChunks = 16;
+
+__device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, int R, int k,
+                                               int E, int nbits, int32_t *__restrict__ counts,
+                                               int32_t *__restrict__ offsets,
+                                               int32_t *__restrict__ perm,
+                                               int32_t *__restrict__ inv, int *smem) {
+  int *s_cur = smem;                  // [E]     running count per expert
+  int *s_off = s_cur + E;             // [E]     offsets
+  int *s_wc = s_off + E;              // [16][E] per-wave counts of the current chunk
+  int *s_base = s_wc + kDispWaves * E;  // [16][E] first rank of (wave, expert) in the chunk
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool in_regs = R <= kDispRegChunks * kDispThreads;
+
+  for (int e = tid; e < E; e += kDispThreads) s_cur[e] = 0;
+  for (int i = tid; i < kDispWaves * E; i += kDispThreads) s_wc[i] = 0;
+  int ids[kDispRegChunks], rk[kDispRegChunks];
+#pragma unroll
+  for (int q = 0; q < kDispRegChunks; ++q) {
+    const int rq = q * kDispThreads + tid;
+    ids[q] = (in_regs && rq < R) ? idx[rq] : -1;
+    rk[q] = 0;
+  }
+  __syncthreads();
+
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < R; c0 += kDispThreads) {
+    const int ci = c0 / kDispThreads;
+    const int r = c0 + tid;
+    int e = -1;
+    if (in_regs) {
+#pragma unroll
+      for (int q = 0; q < kDispRegChunks; ++q) e = q == ci ? ids[q] : e;
+    } else {
+      e = r < R ? idx[r] : -1;
+    }
+    const bool valid = e >= 0 && e < E;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(same & lt_mask);
+    if (valid && rank == 0) s_wc[wave * E + e] = __popcll(same);
+    __syncthreads();
+    // Per expert: exclusive prefix of the 16 wave counts (independent LDS
+    // loads), cursor advance, and the counts cleared for the next chunk.
+    for (int ee = tid; ee < E; ee += kDispThreads) {
+      int cw[kDispWaves];
+#pragma unroll
+      for (int wv = 0; wv < kDispWaves; ++wv) cw[wv] = s_wc[wv * E + ee];
+      int run = s_cur[ee];
+#pragma unroll
+      for (int wv = 0; wv < kDispWaves; ++wv) {
+        s_base[wv * E + ee] = run;
+        run += cw[wv];
+        s_wc[wv * E + ee] = 0;
+      }
+      s_cur[ee] = run;
+    }
+    __syncthreads();
+    if (valid) {
+      const int pos = s_base[wave * E + e] + rank;  // rank within the expert's pile
+      if (in_regs) {
+#pragma unroll
+        for (int q = 0; q < kDispRegChunks; ++q) rk[q] = q == ci ? pos : rk[q];
+      } else {
+        inv[r] = pos;
+      }
+    }
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    int carry = 0;
+    for (int base = 0; base < E; base += MOE_WAVE) {
+      const int e = base + lane;
+      const int c = e < E ? s_cur[e] : 0;
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < MOE_WAVE; o <<= 1) {
+        const int vv = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += vv;
+      }
+      if (e < E) s_off[e] = carry + incl - c;
+      carry += __shfl(incl, MOE_WAVE - 1, 64);
+    }
+    if (lane == 0) offsets[E] = carry;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kDispThreads) {
+    counts[e] = s_cur[e];
+    offsets[e] = s_off[e];
+  }
+  if (in_regs) {
+#pragma unroll
+    for (int q = 0; q < kDispRegChunks; ++q) {
+      const int r = q * kDispThreads + tid;
+      const int e = ids[q];
+      if (r < R && e >= 0 && e < E) {
+        const int pos = s_off[e] + rk[q];
+        perm[pos] = r / k;
+        inv[r] = pos;
+      }
+    }
+  } else {
+    for (int r = tid; r < R; r += kDispThreads) {
+      const int e = idx[r];
+      if (e >= 0 && e < E) {
+        const int pos = s_off[e] + inv[r];
+        perm[pos] = r / k;
+        inv[r] = pos;
+      }
+    }
+  }
+}
+
+}  // namespace moe

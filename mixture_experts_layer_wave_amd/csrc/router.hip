@@ -8,32 +8,36 @@
 // Fast", section "A fused kernel, and an overflow problem").
 #include "common.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
 
 // bf16 logits on MFMA.  One wave owns a 16-token x 16-expert tile and walks
-// K = d in steps of 32 with v_mfma_f32_16x16x32_bf16 (bf16 products are exact
-// in the fp32 accumulator).  Lane l holds tokens/experts (l % 16) and the 8
-// consecutive K values (l / 16) * 8 of each 32-wide step for both operands;
-// any fixed K order is valid as long as A and B agree.
-// Grid: x = token tiles (16), y = groups of 4 expert tiles.
+// its K range in steps of 32 with v_mfma_f32_16x16x32_bf16 (bf16 products
+// are exact in the fp32 accumulator).  Lane l holds tokens/experts (l % 16)
+// and the 8 consecutive K values (l / 16) * 8 of each 32-wide step for both
+// operands; any fixed K order is valid as long as A and B agree.
+// Grid: x = token tiles (16), y = groups of 4 expert tiles, z = K splits.
+// Split z writes part[z][n][E] over K range [z * kc, (z + 1) * kc); split 0
+// adds the bias.  The top-k pass sums the splits in order.
 __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg,
-    const float *__restrict__ bias, float *__restrict__ logits, int n, int d, int E) {
+    const float *__restrict__ bias, float *__restrict__ part, int n, int d, int E, int kc) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t0 = blockIdx.x * 16;
   const int e0 = (blockIdx.y * 4 + wave) * 16;
   if (e0 >= E) return;  // no barriers in this kernel
+  const int kbeg = blockIdx.z * kc, kend = min(d, kbeg + kc);
   const int row = lane & 15, kg = lane >> 4;
   const int t = t0 + row, e = e0 + row;
   const bool tv = t < n, ev = e < E;
   const uint16_t *xr = x + (size_t)(tv ? t : 0) * d + kg * 8;
   const uint16_t *wr = wg + (size_t)(ev ? e : 0) * d + kg * 8;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  int k0 = 0;
+  int k0 = kbeg;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (; k0 + 64 <= d; k0 += 64) {
+  for (; k0 + 64 <= kend; k0 += 64) {
     u32x4 a0 = tv ? *(const u32x4 *)(xr + k0) : zero;
     u32x4 b0 = ev ? *(const u32x4 *)(wr + k0) : zero;
     u32x4 a1 = tv ? *(const u32x4 *)(xr + k0 + 32) : zero;
@@ -43,8 +47,8 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
                                                    __builtin_bit_cast(bf16x8, b1), acc1, 0, 0, 0);
   }
-  for (; k0 < d; k0 += 32) {
-    const bool kv = k0 + kg * 8 < d;  // d % 8 == 0: a chunk is all in or all out
+  for (; k0 < kend; k0 += 32) {
+    const bool kv = k0 + kg * 8 < kend;  // d % 8 == 0: a chunk is all in or all out
     u32x4 a0 = (tv && kv) ? *(const u32x4 *)(xr + k0) : zero;
     u32x4 b0 = (ev && kv) ? *(const u32x4 *)(wr + k0) : zero;
     acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a0),
@@ -52,11 +56,12 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
   }
   // Output layout of the 16x16 tile: lane l holds rows (l / 16) * 4 + i, column l % 16.
   if (ev) {
-    const float bb = bias ? bias[e] : 0.f;
+    const float bb = (bias && blockIdx.z == 0) ? bias[e] : 0.f;
+    float *out = part + (size_t)blockIdx.z * n * E;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tt = t0 + kg * 4 + i;
-      if (tt < n) logits[(size_t)tt * E + e] = acc0[i] + acc1[i] + bb;
+      if (tt < n) out[(size_t)tt * E + e] = acc0[i] + acc1[i] + bb;
     }
   }
 }
@@ -87,90 +92,60 @@ __global__ __launch_bounds__(256) void router_logits_valu_kernel(
   logits[i] = acc + (bias ? bias[e] : 0.f);
 }
 
-// Softmax + top-k: one wave per token.  Lane l owns experts l, l + 64, ...
-// Each of the k rounds takes the wave-wide best (value, lowest index) of the
-// experts not taken yet.  Selection is on the float32 logits; the weights
-// are exp(z - max) over the full-row sum, or over the sum of the chosen k.
-constexpr int kPer = MOE_MAX_E / MOE_WAVE;  // experts per lane at most
-
-__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int n,
-                                                          int E, int k, int renorm,
+// Softmax + top-k: one token per group of topk_group(E) lanes (see
+// topk_token in route_dev.h); a block of 4 waves covers 4 * 64 / G tokens.
+__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ part, int S,
+                                                          int n, int E, int k, int renorm,
                                                           int32_t *__restrict__ idx,
-                                                          float *__restrict__ w) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= n) return;
-  const float *z = logits + (size_t)t * E;
-  const float NEG = -__builtin_inff();
-  float v[kPer];
-  float m = NEG;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + MOE_WAVE * j;
-    v[j] = e < E ? z[e] : NEG;
-    m = fmaxf(m, v[j]);
-  }
-  m = wave_max(m);
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (lane + MOE_WAVE * j < E) s += expf(v[j] - m);
-  s = wave_sum(s);
-
-  uint32_t taken = 0;
-  float my_v = NEG;
-  int my_i = 0;
-  for (int r = 0; r < k; ++r) {
-    float bv = NEG;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = lane + MOE_WAVE * j;
-      const bool ok = e < E && !((taken >> j) & 1u);
-      if (ok && (v[j] > bv || (v[j] == bv && e < bi))) {
-        bv = v[j];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
-    if (bi < E && (bi & (MOE_WAVE - 1)) == lane) taken |= 1u << (bi / MOE_WAVE);
-    if (lane == r) {
-      my_v = bv;
-      my_i = bi;
-    }
-  }
-  const float num = lane < k ? expf(my_v - m) : 0.f;
-  float den = s;
-  if (renorm) den = wave_sum(num);
-  if (lane < k) {
-    idx[(size_t)t * k + lane] = my_i;
-    w[(size_t)t * k + lane] = num / den;
-  }
+                                                          float *__restrict__ w,
+                                                          float *__restrict__ logits) {
+  const int G = topk_group(E);
+  const int t = (blockIdx.x * 256 + threadIdx.x) / G;
+  if ((blockIdx.x * 256 + (threadIdx.x & ~63)) / G >= n) return;  // whole wave idle
+  topk_token(part, S, (size_t)n * E, t, n, E, k, renorm, idx, w, logits);
 }
 
 }  // namespace
 
-hipError_t launch_router_logits(const void *x, const void *wg, const float *bias, float *logits,
-                                int n, int d, int E, bool is_bf16, hipStream_t st) {
+// K range of one split: a multiple of 32 (one MFMA K step).
+static int split_kc(int d, int splits) { return ((d + splits - 1) / splits + 31) / 32 * 32; }
+
+// The split count depends on d only, so a token's logits are summed in the
+// same order whatever the batch it arrives in (outputs are batch-invariant).
+int router_splits(int n, int E, int d) {
+  (void)n;
+  (void)E;
+  constexpr int kSplitK = 256;
+  const int s = (d + kSplitK - 1) / kSplitK;
+  const int kc = split_kc(d, s);
+  return (d + kc - 1) / kc;  // splits that the rounded K range actually yields
+}
+
+hipError_t launch_router_logits(const void *x, const void *wg, const float *bias, float *part,
+                                int n, int d, int E, bool is_bf16, int splits, hipStream_t st) {
   if (is_bf16 && d % 8 == 0) {
-    dim3 grid((n + 15) / 16, (E + 63) / 64);
+    const int kc = split_kc(d, splits);
+    dim3 grid((n + 15) / 16, (E + 63) / 64, (d + kc - 1) / kc);
     router_logits_bf16_kernel<<<grid, 256, 0, st>>>((const uint16_t *)x, (const uint16_t *)wg,
-                                                    bias, logits, n, d, E);
+                                                    bias, part, n, d, E, kc);
   } else if (is_bf16) {
     const long long tot = (long long)n * E;
     router_logits_valu_kernel<uint16_t><<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
-        (const uint16_t *)x, (const uint16_t *)wg, bias, logits, n, d, E);
+        (const uint16_t *)x, (const uint16_t *)wg, bias, part, n, d, E);
   } else {
     const long long tot = (long long)n * E;
     router_logits_valu_kernel<float><<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
-        (const float *)x, (const float *)wg, bias, logits, n, d, E);
+        (const float *)x, (const float *)wg, bias, part, n, d, E);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float *logits, int n, int E, int k, bool renorm, int32_t *idx,
-                              float *w, hipStream_t st) {
-  router_topk_kernel<<<(n + 3) / 4, 256, 0, st>>>(logits, n, E, k, renorm ? 1 : 0, idx, w);
+hipError_t launch_router_topk(const float *part, int splits, int n, int E, int k, bool renorm,
+                              int32_t *idx, float *w, float *logits, hipStream_t st) {
+  const int per_block = 256 / topk_group(E);
+  router_topk_kernel<<<(n + per_block - 1) / per_block, 256, 0, st>>>(part, splits, n, E, k,
+                                                                      renorm ? 1 : 0, idx, w,
+                                                                      logits);
   return hipGetLastError();
 }
 
