@@ -59,6 +59,20 @@ __device__ __forceinline__ void wave_argmax(float &v, int &i) {
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: four shifted
+// adds inside each 16-lane row (lanes without a source add 0), then the
+// totals of rows 0 and 2 are broadcast into rows 1 and 3 (row_bcast:15)
+// and the total of rows 0-1 into rows 2-3 (row_bcast:31).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for
 // every outstanding global access of the wave (stores and direct-to-LDS
 // copies share one counter), which would drain a copy pipeline; copies into

@@ -8,22 +8,26 @@
 // time >= weight bytes / HBM bandwidth.  MXFP4 storage (the minseoc03.com
 // note "What is MXFP4?": 4-bit values, one scale per 32) is read once.
 //
-// One block owns 16 consecutive weight rows of one non-empty expert (the up
-// kernel also the same 16 rows of W3).  At entry it issues every byte of
-// its rows -- codes and E8M0 scales, contiguous in memory -- as direct
-// global-to-LDS copies, and right behind them the activations of its first
-// 16 pile rows into registers, so both are in flight together and a CU
-// keeps over 100 KB of HBM reads outstanding (three blocks fit in its LDS).
-// Then the waves multiply on v_mfma_f32_16x16x32_bf16 with tokens as M (16
-// per group, zero-padded) and the 16 weight rows as N.  Each lane converts a
+// Tile = the weight rows feeding one 16-column MFMA output: 16 rows of W2
+// (down), or 8 rows of W1 next to the same 8 rows of W3 (up, so that the
+// SwiGLU pair meets in one accumulator).  Work item = (pile, group of 16
+// pile rows, tile).  The items of all non-empty experts form one list, cut
+// into equal contiguous ranges, one per workgroup; two persistent
+// workgroups share a CU.  Each streams its tiles through a ring of S LDS
+// stages: every byte of a tile (codes and E8M0 scales, contiguous in
+// memory) is copied by direct global-to-LDS loads S-1 tiles ahead of the
+// tile being multiplied, so a workgroup's compute overlaps its own copies
+// and the CU keeps about 100 KB of reads in flight.  Activations of a pile group
+// stay in registers for all of its tiles.
+//
+// The multiply runs on v_mfma_f32_16x16x32_bf16 with pile rows as M (zero-
+// padded to 16) and the tile's 16 weight rows as N.  Each lane converts a
 // whole 32-element block (16 B of codes + its scale) with
-// v_cvt_scalef32_pk_bf16_fp4 and feeds it to 4 MFMAs: for MFMA q of a
-// 128-deep K step, lane group g supplies K indices 32 (4 s + g) + 8 q + i,
-// and the activations are read in the same order (any fixed K order is
-// valid when both operands agree).  The four waves split K; each wave does
-// both matrices of the up projection on its K range, so one activation
-// register file feeds both.  Partial sums meet in LDS in a fixed order
-// (deterministic).
+// v_cvt_scalef32_pk_bf16_fp4 and feeds it to 4 MFMAs: for MFMA q of 128-deep
+// K step s, lane group g supplies K indices 32 (4 s + g) + 8 q + i, and the
+// activations are read in the same order (any fixed K order is valid when
+// both operands agree).  The four waves split K; partial sums meet in LDS
+// in a fixed order (deterministic).
 #include <atomic>
 
 #include "common.h"
@@ -32,17 +36,13 @@
 namespace moe {
 namespace {
 
-constexpr int kRows = 16;   // weight rows per block
-constexpr int kWaves = 4;   // waves per block, splitting K
-constexpr int kMaxSteps = 8;  // 128-deep K steps per wave: K <= 32 * 4 * 4 * 8 = 4096
+constexpr int kWaves = 4;      // waves per workgroup, splitting K
+constexpr int kMaxSteps = 8;   // 128-deep K steps per wave: K <= 32 * 4 * 4 * 8 = 4096
+constexpr int kBlocksPerCu = 2;  // persistent workgroups per CU
+constexpr int kMaxStages = 8;    // LDS ring depth per workgroup
+constexpr int kCuLds = 160 * 1024;
 
 typedef __attribute__((address_space(3))) void lds_void;
-
-// LDS of one block: per matrix the codes [16][K/2] and the scales [16][K/32]
-// of its rows, then 2 KB per matrix for the cross-wave reduction.
-size_t decode_lds_bytes(int K, int mats) {
-  return (size_t)mats * kRows * (K / 2 + K / 32) + 2 * (size_t)mats * 64 * sizeof(float) * 4;
-}
 
 // 128-deep K steps each wave needs for K.
 int decode_steps(int K) {
@@ -50,195 +50,312 @@ int decode_steps(int K) {
   return (per_wave + 3) / 4;
 }
 
+// Rows of each matrix in one tile: 8 of W1 and 8 of W3 (up), 16 of W2 (down).
+__host__ __device__ constexpr int tile_rows(bool up) { return up ? 8 : 16; }
+
+// LDS plan of one workgroup.  A stage holds one tile as four regions (two
+// for down): the codes of each matrix's rows, then the scales of each
+// matrix's rows; each region is copied in 1 KB pieces that never cross a
+// region boundary (the last piece of a region is partial).
+struct StagePlan {
+  int stage_bytes;  // codes + scales of one tile (a multiple of 16)
+  int copies;       // 1 KB copies per tile, all waves
+  int table_bytes;  // per-expert pile offsets and group prefix
+  int stages;       // LDS ring depth
+  int lds_bytes;    // total per workgroup
+};
+
+constexpr int kRedBytes = kWaves * 64 * 16;  // one f32x4 per lane per wave
+
+StagePlan stage_plan(int K, bool up, int E) {
+  StagePlan s{};
+  const int mats = up ? 2 : 1;
+  const int code_bytes = tile_rows(up) * (K / 2), scale_bytes = tile_rows(up) * (K / 32);
+  s.stage_bytes = mats * (code_bytes + scale_bytes);
+  s.copies = mats * ((code_bytes + 1023) / 1024 + (scale_bytes + 1023) / 1024);
+  s.table_bytes = ((2 * (E + 1) * 4) + 15) & ~15;
+  const int avail = kCuLds / kBlocksPerCu - kRedBytes - s.table_bytes;
+  s.stages = avail > 0 ? avail / s.stage_bytes : 0;
+  if (s.stages > kMaxStages) s.stages = kMaxStages;
+  // Copies a wave may leave in flight: (stages - 1) tiles, < 64.
+  const int per_wave = (s.copies + kWaves - 1) / kWaves;
+  while (s.stages > 1 && (s.stages - 1) * per_wave > 63) --s.stages;
+  s.lds_bytes = s.stages * s.stage_bytes + kRedBytes + s.table_bytes;
+  return s;
+}
+
 struct DecodeParams {
   const uint16_t *a;       // up: x [n][K] (through perm) or x_perm [R][K]; down: h [R][K]
   const int32_t *perm;     // pile row -> row of a, or NULL for contiguous rows
   const int32_t *offsets;  // [E+1]
-  int E, N, K;             // one expert matrix is N x K (N % 16 == 0)
+  int E, N, K;             // one expert matrix is N x K (N % 16 == 0; K % 64 == 0 up, % 32 down)
   const uint8_t *w0, *w1;  // codes [E][N][K/2] (w1 = W3 for up)
   const uint8_t *s0, *s1;  // scales [E][N][K/32]
   void *out;               // up: bf16 h [R][N]; down: f32 y_perm [R][N]
+  StagePlan plan;
 };
 
-// Block b works on the (b / tiles)-th non-empty expert, rows 16 (b % tiles).
+// Direct copy of 16 B per lane from global memory (wave-uniform base plus
+// the lane's 32-bit offset) to LDS bytes lds + 16 * lane
+// (global_load_lds_dwordx4, non-temporal).  It is written as inline
+// assembly so that the compiler does not order later LDS accesses of the
+// other stages behind it (it would wait for every copy in flight before any
+// LDS access): completion is awaited explicitly with vm_wait before the
+// barrier that publishes a stage.  No other code of the kernel uses M0.
+__device__ __forceinline__ void copy16_to_lds(const uint8_t *base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(base), "s"(lds)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait until at most n (wave-uniform, 0..63) vector memory operations of
+// this wave are outstanding.
+template <int N = 0>
+__device__ __forceinline__ void vm_wait_dyn(int n) {
+  if constexpr (N >= 63) {
+    vm_wait<63>();
+  } else {
+    if (n <= N) {
+      vm_wait<N>();
+      return;
+    }
+    vm_wait_dyn<N + 1>(n);
+  }
+}
+
 // KS = 128-deep K steps per wave (decode_steps(K)).
 template <bool UP, int KS>
-__global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p, int tiles) {
+__global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   constexpr int NMAT = UP ? 2 : 1;
+  constexpr int ROWS = tile_rows(UP);  // rows of each matrix per tile
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_e;
+  const StagePlan &P = p.plan;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int K = p.K, N = p.N;
-  const int KB = K / 32;                  // 32-element blocks per row
-  const int rowb = K / 2;                 // code bytes per row
-  const int code_bytes = kRows * rowb;    // per matrix
-  const int mat_bytes = code_bytes + kRows * KB;
-  const int stage_bytes = NMAT * mat_bytes;
-  const int slot = blockIdx.x / tiles, tile = blockIdx.x % tiles;
-  const int n0 = tile * kRows;
+  const int K = p.K, N = p.N, E = p.E;
+  const int KB = K / 32;                 // 32-element blocks per row
+  const int rowb = K / 2;                // code bytes per row
+  const int code_bytes = ROWS * rowb;    // per matrix
+  const int scale_bytes = ROWS * KB;     // per matrix
+  const int T = N / ROWS;                // tiles per expert
+  const int S = P.stages;
+  float *red = (float *)(smem + S * P.stage_bytes);  // [4 waves][64][4]
+  int *s_off = (int *)((uint8_t *)red + kRedBytes);         // [E+1] pile offsets
+  int *s_gpre = s_off + (E + 1);                            // [E+1] groups before expert e
 
-  // ---- the slot-th non-empty expert ---------------------------------------
-  // Wave 0 reads the offsets of up to 256 experts per round with all loads
-  // in flight together, then ranks the non-empty ones with ballots.
-  if (wave == 0) {
-    int found = -1, before = 0;
-    for (int base = 0; base < p.E && found < 0; base += 4 * 64) {
-      int lo[4], hi[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = base + j * 64 + lane;
-        lo[j] = e < p.E ? p.offsets[e] : 0;
-        hi[j] = e < p.E ? p.offsets[e + 1] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = base + j * 64 + lane;
-        const bool ne = hi[j] > lo[j];
-        const uint64_t msk = __ballot(ne);
-        const int rank = before + __popcll(msk & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-        const uint64_t hm = __ballot(ne && rank == slot);
-        if (found < 0 && hm) found = base + j * 64 + __ffsll((long long)hm) - 1;
-        before += __popcll(msk);
-        (void)e;
-      }
-    }
-    if (lane == 0) s_e = found;
-  }
+  // ---- work list: groups of 16 pile rows, prefix over experts ---------------
+  for (int e = tid; e <= E; e += kWaves * 64) s_off[e] = p.offsets[e];
   __syncthreads();
-  const int e = s_e;
-  if (e < 0) return;
-  const int row0 = p.offsets[e], m = p.offsets[e + 1] - row0;
-
-  // ---- issue all weight bytes of the tile ---------------------------------
-  // The stage holds, per matrix, the 16 rows' codes then their scales; both
-  // are contiguous in memory (N % 16 == 0, so every row exists).  1 KB chunk
-  // c goes to wave c % 4; lane l copies stage bytes c * 1024 + 16 l.
   {
-    const size_t wrow = (size_t)e * N + n0;
-    for (int c = wave; c * 1024 < stage_bytes; c += kWaves) {
-      const int o = c * 1024 + lane * 16;
-      if (o < stage_bytes) {
-        const int mat = (NMAT == 2 && o >= mat_bytes) ? 1 : 0;
-        const int r = o - mat * mat_bytes;
-        const uint8_t *src = r < code_bytes
-                                 ? (mat ? p.w1 : p.w0) + wrow * rowb + r
-                                 : (mat ? p.s1 : p.s0) + wrow * KB + (r - code_bytes);
-        __builtin_amdgcn_global_load_lds(src, (lds_void *)(smem + c * 1024), 16, 0, 2);
-      }
+    // Thread tid sums experts [lo, hi); a block scan gives each run's base.
+    const int per = (E + kWaves * 64 - 1) / (kWaves * 64);
+    const int lo = min(E, tid * per), hi = min(E, lo + per);
+    int run = 0;
+    for (int e = lo; e < hi; ++e) run += (s_off[e + 1] - s_off[e] + 15) >> 4;
+    const int incl = wave_incl_scan(run);
+    int *s_wsum = (int *)red;  // wave totals (red is free until the first tile)
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int base = incl - run;
+    for (int w = 0; w < wave; ++w) base += s_wsum[w];
+    for (int e = lo; e < hi; ++e) {
+      s_gpre[e] = base;
+      base += (s_off[e + 1] - s_off[e] + 15) >> 4;
+    }
+    if (tid == kWaves * 64 - 1) s_gpre[E] = base;
+    __syncthreads();
+  }
+  const int W = s_gpre[E] * T;  // work items
+  const int G = gridDim.x;
+  const int w_lo = (int)(((long long)blockIdx.x * W) / G);
+  const int w_hi = (int)(((long long)(blockIdx.x + 1) * W) / G);
+  const int n_my = w_hi - w_lo;
+  if (n_my <= 0) return;
+
+  // Expert of group index gidx < s_gpre[E]: the e with s_gpre[e] <= gidx <
+  // s_gpre[e + 1], by a forward walk from an earlier answer (gidx only grows).
+  auto expert_of = [&](int gidx, int from) {
+    int e = from;
+    while (s_gpre[e + 1] <= gidx) ++e;
+    return e;
+  };
+  // The first item's expert: binary search for the largest e with
+  // s_gpre[e] <= g0, then the walk skips empty experts.
+  int e_first;
+  {
+    const int g0 = w_lo / T;
+    int lo = 0, hi = E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_gpre[mid] <= g0) lo = mid;
+      else hi = mid - 1;
+    }
+    e_first = expert_of(g0, lo);
+  }
+
+  // ---- copy of one tile into stage st -------------------------------------
+  // Stage layout: codes of matrix 0 [ROWS][K/2], (up) codes of matrix 1,
+  // scales of matrix 0 [ROWS][K/32], (up) scales of matrix 1; each region is
+  // contiguous in memory.  Copy q of a tile (regions in that order, 1 KB
+  // pieces) belongs to wave q % 4; lane l moves bytes 16 l of the piece.
+  const uint32_t lds_base = (uint32_t)(size_t)(lds_void *)smem;
+  const uint32_t voff = lane * 16;
+  const int code_pieces = (code_bytes + 1023) >> 10, scale_pieces = (scale_bytes + 1023) >> 10;
+  auto issue_region = [&](const uint8_t *src, int bytes, int pieces, uint32_t lds, int q0) {
+    for (int j = (wave - q0) & (kWaves - 1); j < pieces; j += kWaves) {
+      const uint32_t at = (uint32_t)j << 10;
+      if (at + voff < (uint32_t)bytes)
+        copy16_to_lds(src + at, voff, __builtin_amdgcn_readfirstlane(lds + at));
+    }
+  };
+  auto issue_tile = [&](int e, int tile, int st) {
+    const size_t wrow = (size_t)e * N + (size_t)tile * ROWS;
+    const uint32_t dst = lds_base + st * P.stage_bytes;
+    issue_region(p.w0 + wrow * rowb, code_bytes, code_pieces, dst, 0);
+    if constexpr (UP) issue_region(p.w1 + wrow * rowb, code_bytes, code_pieces, dst + code_bytes,
+                                   code_pieces);
+    issue_region(p.s0 + wrow * KB, scale_bytes, scale_pieces, dst + NMAT * code_bytes,
+                 NMAT * code_pieces);
+    if constexpr (UP)
+      issue_region(p.s1 + wrow * KB, scale_bytes, scale_pieces,
+                   dst + NMAT * code_bytes + scale_bytes, NMAT * code_pieces + scale_pieces);
+  };
+  // Copies this wave issues per tile.
+  int my_copies = 0;
+  for (int q = wave; q < P.copies; q += kWaves) ++my_copies;
+
+  // Prologue: the first S tiles in flight.
+  {
+    int e = e_first;
+    for (int j = 0; j < S && j < n_my; ++j) {
+      const int w = w_lo + j;
+      e = expert_of(w / T, e);
+      issue_tile(e, w % T, j);
     }
   }
 
+  // Lane (r, g): B column r is row r of W2 (down), or row r & 7 of W1 (r < 8)
+  // or W3 (r >= 8) (up); A row r is pile row t0 + r.
   const int r = lane & 15, g = lane >> 4;
+  const int bmat = UP ? (r >> 3) : 0, brow = UP ? (r & 7) : r;
   const int kb_lo = (KB * wave) / kWaves, kb_hi = (KB * (wave + 1)) / kWaves;
-  float *red = (float *)(smem + stage_bytes);  // [2 waves][NMAT][64 lanes][4]
   const u32x4 z4 = {0u, 0u, 0u, 0u};
+  u32x4 act[KS][4];
+  int cur_group = -1, e_cur = e_first, row0 = 0, m = 0, t0 = 0;
 
-  for (int t0 = 0; t0 < m; t0 += 16) {
-    // ---- activations of pile rows t0..t0+15 on this wave's K range ------
-    // Pile rows are gathered from the token matrix when perm is given (the
-    // fused forward), else read in place (x_perm, or h for down).
-    const int t = t0 + r;
-    const bool tv = t < m;
-    const int arow = tv ? (p.perm ? p.perm[row0 + t] : row0 + t) : 0;
-    const uint16_t *ap = p.a + (size_t)arow * K;
-    u32x4 act[KS][4];
+  for (int i = 0; i < n_my; ++i) {
+    const int w = w_lo + i, gidx = w / T, tile = w % T, st = i % S;
+    // This wave's copies of tile i have landed once at most the copies of
+    // the tiles issued after it are outstanding (loads and stores complete
+    // in order).
+    vm_wait_dyn(min(S - 1, n_my - 1 - i) * my_copies);
+    if (gidx != cur_group) {
+      // ---- activations of the new group (rows t0..t0+15 of the pile) ----
+      // Pile rows are gathered from the token matrix when perm is given
+      // (the fused forward), else read in place (x_perm, or h for down).
+      e_cur = expert_of(gidx, e_cur);
+      cur_group = gidx;
+      row0 = s_off[e_cur];
+      m = s_off[e_cur + 1] - row0;
+      t0 = (gidx - s_gpre[e_cur]) * 16;
+      const int t = t0 + r;
+      const bool tv = t < m;
+      const int arow = tv ? (p.perm ? p.perm[row0 + t] : row0 + t) : 0;
+      const uint16_t *ap = p.a + (size_t)arow * K;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int b = kb_lo + 4 * s + g;
-      const bool ok = tv && b < kb_hi;
+      for (int s = 0; s < KS; ++s) {
+        const int b = kb_lo + 4 * s + g;
+        const bool ok = tv && b < kb_hi;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) act[s][q] = ok ? *(const u32x4 *)(ap + b * 32 + q * 8) : z4;
+        for (int q = 0; q < 4; ++q) act[s][q] = ok ? *(const u32x4 *)(ap + b * 32 + q * 8) : z4;
+      }
+      vm_wait<0>();
     }
-    if (t0 == 0) {
-      __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // own copies landed
-      __syncthreads();                                        // everyone's
-    }
+    lds_barrier();  // every wave's copies of tile i have landed
 
-    // ---- MFMA over this wave's K range ----------------------------------
-    // Two accumulators per matrix (even and odd MFMAs of a step) keep
-    // independent MFMA chains in flight; they are summed in a fixed order.
-    f32x4 acc2[NMAT][2];
-#pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat)
-#pragma unroll
-      for (int q = 0; q < 2; ++q) acc2[mat][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- MFMA over this wave's K range (two independent chains) ---------
+    const uint8_t *lw = smem + st * P.stage_bytes + bmat * code_bytes;  // this lane's codes
+    const uint8_t *ls = smem + st * P.stage_bytes + NMAT * code_bytes + bmat * scale_bytes;
+    f32x4 acc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int b = kb_lo + 4 * s + g;
       const bool bv = b < kb_hi;
+      const u32x4 codes = bv ? *(const u32x4 *)(lw + brow * rowb + b * 16) : z4;
+      const float sc = bv ? e8m0_to_f32(ls[brow * KB + b]) : 0.f;
 #pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat) {
-        const uint8_t *lw = smem + mat * mat_bytes;
-        const u32x4 codes = bv ? *(const u32x4 *)(lw + r * rowb + b * 16) : z4;
-        const float sc = bv ? e8m0_to_f32(lw[code_bytes + r * KB + b]) : 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t wv = codes[q];
-          const bf16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 0);
-          const bf16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 1);
-          const bf16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 2);
-          const bf16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 3);
-          const u32x4 bw = {__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
-                            __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3)};
-          acc2[mat][q & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, act[s][q]), __builtin_bit_cast(bf16x8, bw),
-              acc2[mat][q & 1], 0, 0, 0);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t wv = codes[q];
+        const bf16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 0);
+        const bf16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 1);
+        const bf16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 2);
+        const bf16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 3);
+        const u32x4 bw = {__builtin_bit_cast(uint32_t, q0), __builtin_bit_cast(uint32_t, q1),
+                          __builtin_bit_cast(uint32_t, q2), __builtin_bit_cast(uint32_t, q3)};
+        acc2[q & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, act[s][q]), __builtin_bit_cast(bf16x8, bw), acc2[q & 1], 0,
+            0, 0);
       }
     }
-    f32x4 acc[NMAT];
-#pragma unroll
-    for (int mat = 0; mat < NMAT; ++mat)
-      acc[mat] = acc2[mat][0] + acc2[mat][1];
+    *(f32x4 *)(red + (wave * 64 + lane) * 4) = acc2[0] + acc2[1];
+    lds_barrier();  // stage st is free; all partial sums are in LDS
 
-    // ---- fixed-order reduction: (w0 + w2) + (w1 + w3) -------------------
-    if (wave >= 2) {
-#pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat)
-        *(f32x4 *)(red + (((wave - 2) * NMAT + mat) * 64 + lane) * 4) = acc[mat];
-    }
-    lds_barrier();
-    if (wave < 2) {
-#pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat)
-        acc[mat] += *(const f32x4 *)(red + ((wave * NMAT + mat) * 64 + lane) * 4);
-    }
-    lds_barrier();
-    if (wave == 1) {
-#pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat)
-        *(f32x4 *)(red + (mat * 64 + lane) * 4) = acc[mat];
-    }
-    lds_barrier();
+    // ---- wave 0: fixed-order sum (w0 + w1) + (w2 + w3), epilogue ---------
+    // Its stores are issued before its next copies, so the in-order wait
+    // above covers them.
     if (wave == 0) {
+      auto column_sum = [&](int l) {
+        return (*(const f32x4 *)(red + (0 * 64 + l) * 4) + *(const f32x4 *)(red + (1 * 64 + l) * 4)) +
+               (*(const f32x4 *)(red + (2 * 64 + l) * 4) + *(const f32x4 *)(red + (3 * 64 + l) * 4));
+      };
+      const f32x4 v = column_sum(lane);
+      // Up: columns 0-7 are W1 rows (gate), 8-15 the same W3 rows (up); the
+      // partner column c + 8 is summed from the LDS partials of lane l + 8.
+      const f32x4 u = UP ? column_sum(lane ^ 8) : v;
+      // 16x16 output: lane l holds pile rows t0 + (l / 16) * 4 + i, column l % 16.
 #pragma unroll
-      for (int mat = 0; mat < NMAT; ++mat)
-        acc[mat] += *(const f32x4 *)(red + (mat * 64 + lane) * 4);
-      // 16x16 output: lane l holds tokens (l / 16) * 4 + i, weight row l % 16.
-      const int col = n0 + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tt = t0 + (lane >> 4) * 4 + i;
-        if (tt < m) {
-          if constexpr (UP) {
-            ((uint16_t *)p.out)[(size_t)(row0 + tt) * N + col] =
-                (uint16_t)f32_to_bf16_bits(silu(acc[0][i]) * acc[1][i]);
-          } else {
-            ((float *)p.out)[(size_t)(row0 + tt) * N + col] = acc[0][i];
-          }
+      for (int ii = 0; ii < 4; ++ii) {
+        const int tt = t0 + (lane >> 4) * 4 + ii;
+        if constexpr (UP) {
+          if (tt < m && r < 8)
+            ((uint16_t *)p.out)[(size_t)(row0 + tt) * N + tile * ROWS + r] =
+                (uint16_t)f32_to_bf16_bits(silu(v[ii]) * u[ii]);
+        } else {
+          if (tt < m) ((float *)p.out)[(size_t)(row0 + tt) * N + tile * ROWS + r] = v[ii];
         }
       }
     }
-    if (t0 + 16 < m) lds_barrier();  // the reduction area is reused
+    if (i + S < n_my) {
+      const int wn = w_lo + i + S;
+      issue_tile(expert_of(wn / T, e_cur), wn % T, st);
+    }
   }
 }
 
+int cu_count() {
+  static std::atomic<int> cached{0};
+  int c = cached.load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    c = 256;
+  cached.store(c, std::memory_order_relaxed);
+  return c;
+}
+
 template <bool UP, int KS>
-hipError_t launch_decode_ks(const DecodeParams &p, int grid, size_t lds, hipStream_t st) {
+hipError_t launch_decode_ks(const DecodeParams &p, hipStream_t st) {
   auto kern = mx_decode_kernel<UP, KS>;
+  const int lds = p.plan.lds_bytes;
   if (lds > 64 * 1024) {
-    // Set once per device (the attribute is per device and kernel).
+    // The LDS limit is raised once per device (a per-device kernel attribute).
     static std::atomic<uint64_t> attr_done{0};
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
@@ -246,41 +363,40 @@ hipError_t launch_decode_ks(const DecodeParams &p, int grid, size_t lds, hipStre
     const uint64_t bit = 1ull << (dev & 63);
     if (!(attr_done.load(std::memory_order_acquire) & bit)) {
       err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                160 * 1024);
+                                kCuLds);
       if (err != hipSuccess) return err;
       attr_done.fetch_or(bit, std::memory_order_release);
     }
   }
-  kern<<<grid, kWaves * 64, lds, st>>>(p, (p.N + kRows - 1) / kRows);
+  kern<<<kBlocksPerCu * cu_count(), kWaves * 64, lds, st>>>(p);
   return hipGetLastError();
 }
 
 template <bool UP>
-hipError_t launch_decode(const DecodeParams &p, int max_active, hipStream_t st) {
-  const int tiles = p.N / kRows;
-  const size_t lds = decode_lds_bytes(p.K, UP ? 2 : 1);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  const int grid = max_active * tiles;
+hipError_t launch_decode(DecodeParams p, hipStream_t st) {
+  p.plan = stage_plan(p.K, UP, p.E);
+  if (p.plan.stages < 1) return hipErrorInvalidValue;
   switch (decode_steps(p.K)) {
-    case 1: return launch_decode_ks<UP, 1>(p, grid, lds, st);
-    case 2: return launch_decode_ks<UP, 2>(p, grid, lds, st);
-    case 3: return launch_decode_ks<UP, 3>(p, grid, lds, st);
-    case 4: return launch_decode_ks<UP, 4>(p, grid, lds, st);
-    case 5: return launch_decode_ks<UP, 5>(p, grid, lds, st);
-    case 6: return launch_decode_ks<UP, 6>(p, grid, lds, st);
-    case 7: return launch_decode_ks<UP, 7>(p, grid, lds, st);
-    case 8: return launch_decode_ks<UP, 8>(p, grid, lds, st);
+    case 1: return launch_decode_ks<UP, 1>(p, st);
+    case 2: return launch_decode_ks<UP, 2>(p, st);
+    case 3: return launch_decode_ks<UP, 3>(p, st);
+    case 4: return launch_decode_ks<UP, 4>(p, st);
+    case 5: return launch_decode_ks<UP, 5>(p, st);
+    case 6: return launch_decode_ks<UP, 6>(p, st);
+    case 7: return launch_decode_ks<UP, 7>(p, st);
+    case 8: return launch_decode_ks<UP, 8>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
+// Regions are copied in 16 B pieces: the up tile's 8 rows of scales need
+// d % 64 == 0; the down tile has 16 rows, so d_ff % 32 == 0 suffices.
 bool decode_ffn_fits(int d, int d_ff, int E) {
-  (void)E;
-  return d % 32 == 0 && d_ff % 32 == 0 && decode_steps(d) <= kMaxSteps &&
-         decode_steps(d_ff) <= kMaxSteps && decode_lds_bytes(d, 2) <= 160 * 1024 &&
-         decode_lds_bytes(d_ff, 1) <= 160 * 1024;
+  return d % 64 == 0 && d_ff % 32 == 0 && decode_steps(d) <= kMaxSteps &&
+         decode_steps(d_ff) <= kMaxSteps && stage_plan(d, true, E).stages >= 1 &&
+         stage_plan(d_ff, false, E).stages >= 1;
 }
 
 hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st) {
@@ -296,8 +412,7 @@ hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st) {
   p.s0 = a.s1;
   p.s1 = a.s3;
   p.out = a.h;
-  const int max_active = a.E < a.R ? a.E : a.R;
-  return launch_decode<true>(p, max_active, st);
+  return launch_decode<true>(p, st);
 }
 
 hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st) {
@@ -311,8 +426,7 @@ hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st) {
   p.w0 = (const uint8_t *)a.w2;
   p.s0 = a.s2;
   p.out = a.y_perm;
-  const int max_active = a.E < a.R ? a.E : a.R;
-  return launch_decode<false>(p, max_active, st);
+  return launch_decode<false>(p, st);
 }
 
 }  // namespace moe

@@ -21,11 +21,14 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t *__restric
                                                         int32_t *__restrict__ perm,
                                                         int32_t *__restrict__ inv) {
   extern __shared__ int smem[];
-  dispatch_block(idx, R, k, E, nbits, counts, offsets, perm, inv, smem);
+  dispatch_block<16>(idx, R, k, E, nbits, counts, offsets, perm, inv, smem);
 }
 
-// Small batches: top-k of every token (one wave per token, see topk_token)
-// and the dispatch in one workgroup, saving a launch on the decode path.
+// Small batches: top-k of every token (one group of lanes per token, see
+// topk_token_t) and the dispatch in one workgroup, saving a launch on the
+// decode path.  n <= kRouteSmallN, so n * k <= 2048 pairs: two register
+// chunks.
+template <int PER>
 __global__ __launch_bounds__(1024) void route_dispatch_kernel(
     const float *__restrict__ part, int S, int n, int E, int k, int renorm, int nbits,
     int32_t *__restrict__ idx, float *__restrict__ w, int32_t *__restrict__ counts,
@@ -34,10 +37,10 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(
   int *s_idx = smem + dispatch_lds_ints(E);  // [n * k] chosen experts
   const int G = topk_group(E);
   for (int t0 = 0; t0 < n; t0 += kDispThreads / G)  // uniform trip count
-    topk_token(part, S, (size_t)n * E, t0 + threadIdx.x / G, n, E, k, renorm, idx, w, nullptr,
-               s_idx);
-  __syncthreads();
-  dispatch_block(s_idx, n * k, k, E, nbits, counts, offsets, perm, inv, smem);
+    topk_token_t<PER>(part, S, (size_t)n * E, t0 + threadIdx.x / G, n, E, k, renorm, idx, w,
+                      nullptr, s_idx);
+  lds_barrier();
+  dispatch_block<2>(s_idx, n * k, k, E, nbits, counts, offsets, perm, inv, smem);
 }
 
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t *__restrict__ x,
@@ -82,16 +85,31 @@ hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *cou
   return hipGetLastError();
 }
 
+template <int PER>
+static hipError_t route_dispatch_per(const float *part, int splits, int n, int E, int k,
+                                     bool renorm, int32_t *idx, float *w, int32_t *counts,
+                                     int32_t *offsets, int32_t *perm, int32_t *inv,
+                                     hipStream_t st) {
+  const size_t lds = sizeof(int) * ((size_t)dispatch_lds_ints(E) + (size_t)n * k);
+  hipError_t err = allow_lds(route_dispatch_kernel<PER>, lds);
+  if (err != hipSuccess) return err;
+  route_dispatch_kernel<PER><<<1, kDispThreads, lds, st>>>(part, splits, n, E, k, renorm ? 1 : 0,
+                                                           id_bits(E), idx, w, counts, offsets,
+                                                           perm, inv);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_dispatch(const float *part, int splits, int n, int E, int k, bool renorm,
                                  int32_t *idx, float *w, int32_t *counts, int32_t *offsets,
                                  int32_t *perm, int32_t *inv, hipStream_t st) {
-  const size_t lds = sizeof(int) * ((size_t)dispatch_lds_ints(E) + (size_t)n * k);
-  hipError_t err = allow_lds(route_dispatch_kernel, lds);
-  if (err != hipSuccess) return err;
-  route_dispatch_kernel<<<1, kDispThreads, lds, st>>>(part, splits, n, E, k, renorm ? 1 : 0,
-                                                      id_bits(E), idx, w, counts, offsets, perm,
-                                                      inv);
-  return hipGetLastError();
+  if (n > kRouteSmallN || n * k > 2 * kDispThreads) return hipErrorInvalidValue;
+  switch (topk_per(E)) {
+    case 2: return route_dispatch_per<2>(part, splits, n, E, k, renorm, idx, w, counts, offsets, perm, inv, st);
+    case 4: return route_dispatch_per<4>(part, splits, n, E, k, renorm, idx, w, counts, offsets, perm, inv, st);
+    default:
+      return route_dispatch_per<MOE_MAX_E / MOE_WAVE>(part, splits, n, E, k, renorm, idx, w,
+                                                       counts, offsets, perm, inv, st);
+  }
 }
 
 hipError_t launch_gather_rows(const void *x, const int32_t *perm, void *x_perm, int R,

@@ -116,14 +116,9 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
     const int eb = lane * per, ee = min(p.E, eb + per);
     int local = 0;
     for (int x = eb; x < ee; ++x) local += (p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM;
-    int incl = local;
-#pragma unroll
-    for (int o = 1; o < MOE_WAVE; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
+    const int incl = wave_incl_scan(local);
     const int excl = incl - local;
-    const int total = __shfl(incl, MOE_WAVE - 1, 64) * p.n_tiles;  // tiles of work
+    const int total = __builtin_amdgcn_readlane(incl, MOE_WAVE - 1) * p.n_tiles;  // tiles of work
     const int b = blockIdx.x;
     if (lane == 0 && b >= total) s_e = -1;
     if (b < total) {

@@ -138,25 +138,34 @@ __device__ __forceinline__ void topk_token_t(const float *__restrict__ part, int
     if (live && gl + G * j < E) sum += expf(v[j] - m);
   sum = group_sum(sum, G);
 
+  // Rounds: the group maximum over experts not yet taken (round 0 reuses the
+  // softmax maximum), then the lowest expert index holding it, found with
+  // ballots in index order (slot j covers experts j G .. j G + G - 1).
+  const int lane = threadIdx.x & 63;
+  const int gbase = lane & ~(G - 1);
+  const uint64_t gmask = G == 64 ? ~0ull : (((1ull << G) - 1) << gbase);
   uint32_t taken = 0;
   float my_v = NEG;
   int my_i = 0;
   for (int r = 0; r < k; ++r) {
-    float bv = NEG;
+    float mx = m;
+    if (r > 0) {
+      float bv = NEG;
+#pragma unroll
+      for (int j = 0; j < kTopkPer; ++j)
+        if (gl + G * j < E && !((taken >> j) & 1u)) bv = fmaxf(bv, v[j]);
+      mx = group_max(bv, G);
+    }
     int bi = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < kTopkPer; ++j) {
-      const int e = gl + G * j;
-      const bool ok = e < E && !((taken >> j) & 1u);
-      if (ok && (v[j] > bv || (v[j] == bv && e < bi))) {
-        bv = v[j];
-        bi = e;
-      }
+      const bool hit = live && gl + G * j < E && !((taken >> j) & 1u) && v[j] == mx;
+      const uint64_t bits = __ballot(hit) & gmask;
+      if (bi == 0x7fffffff && bits) bi = G * j + (__ffsll((long long)bits) - 1 - gbase);
     }
-    group_argmax(bv, bi, G);
     if (bi < E && (bi & (G - 1)) == gl) taken |= 1u << (bi / G);
     if (gl == r) {
-      my_v = bv;
+      my_v = mx;
       my_i = bi;
     }
   }
@@ -171,20 +180,10 @@ __device__ __forceinline__ void topk_token_t(const float *__restrict__ part, int
   }
 }
 
-// lds_idx (may be NULL) receives a copy of the chosen experts.
-__device__ __forceinline__ void topk_token(const float *__restrict__ part, int S,
-                                           size_t part_stride, int t, int n, int E, int k,
-                                           int renorm, int32_t *__restrict__ idx,
-                                           float *__restrict__ w,
-                                           float *__restrict__ logits_out,
-                                           int *lds_idx = nullptr) {
-  if (E <= 2 * MOE_WAVE)
-    topk_token_t<2>(part, S, part_stride, t, n, E, k, renorm, idx, w, logits_out, lds_idx);
-  else if (E <= 4 * MOE_WAVE)
-    topk_token_t<4>(part, S, part_stride, t, n, E, k, renorm, idx, w, logits_out, lds_idx);
-  else
-    topk_token_t<MOE_MAX_E / MOE_WAVE>(part, S, part_stride, t, n, E, k, renorm, idx, w,
-                                       logits_out, lds_idx);
+// Expert slots per lane for E experts: the compile-time bound that
+// topk_token_t is instantiated with (2, 4 or 16).
+__host__ __device__ constexpr int topk_per(int E) {
+  return E <= 2 * MOE_WAVE ? 2 : (E <= 4 * MOE_WAVE ? 4 : MOE_MAX_E / MOE_WAVE);
 }
 
 constexpr int kDispThreads = 1024;
@@ -202,12 +201,11 @@ __host__ __device__ constexpr int dispatch_lds_ints(int E) { return E * (2 + 2 *
 //   2. the cursors are now the pile sizes: exclusive scan -> offsets;
 //   3. every pair moves to offsets[e] + rank (perm, inv).
 // No atomics decide positions, so the result is the unique stable grouping.
-// Ids outside [0, E) are skipped.  The ids and ranks of up to kDispRegChunks
-// chunks stay in registers (a barrier waits for outstanding global stores,
-// so none are issued before the end); longer inputs park ranks in inv[].
-// `idx` may point to LDS or global memory.
-constexpr int kDispRegChunks = 16;
-
+// Ids outside [0, E) are skipped.  The ids and ranks of up to RC chunks
+// stay in registers; longer inputs park ranks in inv[] (each thread reads
+// back only its own entries).  Barriers order LDS only.  `idx` may point to
+// LDS or global memory.
+template <int RC>
 __device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, int R, int k,
                                                int E, int nbits, int32_t *__restrict__ counts,
                                                int32_t *__restrict__ offsets,
@@ -218,18 +216,18 @@ __device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, 
   int *s_wc = s_off + E;              // [16][E] per-wave counts of the current chunk
   int *s_base = s_wc + kDispWaves * E;  // [16][E] first rank of (wave, expert) in the chunk
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool in_regs = R <= kDispRegChunks * kDispThreads;
+  const bool in_regs = R <= RC * kDispThreads;
 
   for (int e = tid; e < E; e += kDispThreads) s_cur[e] = 0;
   for (int i = tid; i < kDispWaves * E; i += kDispThreads) s_wc[i] = 0;
-  int ids[kDispRegChunks], rk[kDispRegChunks];
+  int ids[RC], rk[RC];
 #pragma unroll
-  for (int q = 0; q < kDispRegChunks; ++q) {
+  for (int q = 0; q < RC; ++q) {
     const int rq = q * kDispThreads + tid;
     ids[q] = (in_regs && rq < R) ? idx[rq] : -1;
     rk[q] = 0;
   }
-  __syncthreads();
+  lds_barrier();
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int c0 = 0; c0 < R; c0 += kDispThreads) {
@@ -238,7 +236,7 @@ __device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, 
     int e = -1;
     if (in_regs) {
 #pragma unroll
-      for (int q = 0; q < kDispRegChunks; ++q) e = q == ci ? ids[q] : e;
+      for (int q = 0; q < RC; ++q) e = q == ci ? ids[q] : e;
     } else {
       e = r < R ? idx[r] : -1;
     }
@@ -251,7 +249,7 @@ __device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, 
     }
     const int rank = __popcll(same & lt_mask);
     if (valid && rank == 0) s_wc[wave * E + e] = __popcll(same);
-    __syncthreads();
+    lds_barrier();
     // Per expert: exclusive prefix of the 16 wave counts (independent LDS
     // loads), cursor advance, and the counts cleared for the next chunk.
     for (int ee = tid; ee < E; ee += kDispThreads) {
@@ -267,43 +265,38 @@ __device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, 
       }
       s_cur[ee] = run;
     }
-    __syncthreads();
+    lds_barrier();
     if (valid) {
       const int pos = s_base[wave * E + e] + rank;  // rank within the expert's pile
       if (in_regs) {
 #pragma unroll
-        for (int q = 0; q < kDispRegChunks; ++q) rk[q] = q == ci ? pos : rk[q];
+        for (int q = 0; q < RC; ++q) rk[q] = q == ci ? pos : rk[q];
       } else {
         inv[r] = pos;
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   if (wave == 0) {
     int carry = 0;
     for (int base = 0; base < E; base += MOE_WAVE) {
       const int e = base + lane;
       const int c = e < E ? s_cur[e] : 0;
-      int incl = c;
-#pragma unroll
-      for (int o = 1; o < MOE_WAVE; o <<= 1) {
-        const int vv = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += vv;
-      }
+      const int incl = wave_incl_scan(c);
       if (e < E) s_off[e] = carry + incl - c;
-      carry += __shfl(incl, MOE_WAVE - 1, 64);
+      carry += __builtin_amdgcn_readlane(incl, MOE_WAVE - 1);
     }
     if (lane == 0) offsets[E] = carry;
   }
-  __syncthreads();
+  lds_barrier();
   for (int e = tid; e < E; e += kDispThreads) {
     counts[e] = s_cur[e];
     offsets[e] = s_off[e];
   }
   if (in_regs) {
 #pragma unroll
-    for (int q = 0; q < kDispRegChunks; ++q) {
+    for (int q = 0; q < RC; ++q) {
       const int r = q * kDispThreads + tid;
       const int e = ids[q];
       if (r < R && e >= 0 && e < E) {

@@ -94,6 +94,7 @@ __global__ __launch_bounds__(256) void router_logits_valu_kernel(
 
 // Softmax + top-k: one token per group of topk_group(E) lanes (see
 // topk_token in route_dev.h); a block of 4 waves covers 4 * 64 / G tokens.
+template <int PER>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ part, int S,
                                                           int n, int E, int k, int renorm,
                                                           int32_t *__restrict__ idx,
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
   const int G = topk_group(E);
   const int t = (blockIdx.x * 256 + threadIdx.x) / G;
   if ((blockIdx.x * 256 + (threadIdx.x & ~63)) / G >= n) return;  // whole wave idle
-  topk_token(part, S, (size_t)n * E, t, n, E, k, renorm, idx, w, logits);
+  topk_token_t<PER>(part, S, (size_t)n * E, t, n, E, k, renorm, idx, w, logits, nullptr);
 }
 
 }  // namespace
@@ -143,9 +144,19 @@ hipError_t launch_router_logits(const void *x, const void *wg, const float *bias
 hipError_t launch_router_topk(const float *part, int splits, int n, int E, int k, bool renorm,
                               int32_t *idx, float *w, float *logits, hipStream_t st) {
   const int per_block = 256 / topk_group(E);
-  router_topk_kernel<<<(n + per_block - 1) / per_block, 256, 0, st>>>(part, splits, n, E, k,
-                                                                      renorm ? 1 : 0, idx, w,
-                                                                      logits);
+  const int grid = (n + per_block - 1) / per_block;
+  const int rn = renorm ? 1 : 0;
+  switch (topk_per(E)) {
+    case 2:
+      router_topk_kernel<2><<<grid, 256, 0, st>>>(part, splits, n, E, k, rn, idx, w, logits);
+      break;
+    case 4:
+      router_topk_kernel<4><<<grid, 256, 0, st>>>(part, splits, n, E, k, rn, idx, w, logits);
+      break;
+    default:
+      router_topk_kernel<MOE_MAX_E / MOE_WAVE><<<grid, 256, 0, st>>>(part, splits, n, E, k, rn,
+                                                                      idx, w, logits);
+  }
   return hipGetLastError();
 }
 
