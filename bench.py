@@ -12,7 +12,9 @@ Printed (one JSON line on stdout): tokens/s of the layer, plus
   roofline     -- the dominant kernel (the grouped up-projection with the
                   SwiGLU epilogue, 2/3 of the FLOPs) timed with HIP events
                   on its stream over K launches, against the bf16 dense MFMA
-                  peak (decode workloads: against HBM bandwidth),
+                  peak (decode workloads: against HBM bandwidth); traffic is
+                  the HBM bytes per launch from the committed rocprofv3
+                  counter summary under profiles/,
   cpu_baseline -- the float64 CPU oracle on a bounded token sample of the
                   same workload, on this host's cores.
 """
@@ -86,6 +88,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times) and exit; "
+                         "run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -94,8 +99,19 @@ def main():
 
     import torch
 
+    if args.copy_calibration_mib:
+        nbytes = args.copy_calibration_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {nbytes} bytes 3 times")
+        return
+
     from mixture_experts_layer_wave_amd import binding as B
     from mixture_experts_layer_wave_amd import workloads as W
+    from mixture_experts_layer_wave_amd.profiling import read_traffic
     from mixture_experts_layer_wave_amd.device import DeviceLayer, to_device
 
     name = args.workload or W.SWITCH
@@ -167,8 +183,13 @@ def main():
         achieved = work["flops_up"] / (up_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "grouped_gemm_kernel<up, gather> (moe_expert_up)"
+    # HBM bytes per launch of this kernel from the committed rocprofv3
+    # FETCH_SIZE / WRITE_SIZE summary (null once the kernel's sources change).
+    fam = "mx_decode_kernel" if decode else "big_gemm_kernel"
+    traffic, src = read_traffic(name, fam)
+    roof["traffic"] = traffic
+    roof["traffic_source"] = src
+    roof["kernel"] = f"{fam}<up> (moe_expert_up)"
     roof["kernel_us"] = up_ms * 1e3
     log(f"[bench] up kernel {up_ms * 1e3:.1f} us -> {roof['achieved']:.1f} {roof['unit']} ({100 * roof['frac']:.1f}% of peak)")
     layer_tflops = work["flops"] / (ms_per_step * 1e-3) / 1e12

@@ -1,0 +1,180 @@
+"""Summaries of rocprofv3 output for the files under profiles/.
+
+    python -m mixture_experts_layer_wave_amd.profiling stats \
+        --csv DIR/run_kernel_stats.csv --title T --command CMD --out profiles/X.md
+    python -m mixture_experts_layer_wave_amd.profiling traffic --workload NAME \
+        --kernel SUBSTRING --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
+        --copy-bytes N --command CMD --out profiles/Y.md
+
+`traffic` turns two counter runs (FETCH_SIZE, then WRITE_SIZE; rocprofv3
+reports KiB per dispatch) into HBM bytes per launch of one kernel.  Each
+counter is scaled by what it reads for a plain device copy of known size
+(copy bytes / counter bytes), measured in the same way.  The summary records
+a digest of the sources that define the kernel; bench.py reports the
+traffic only while those sources are unchanged.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")
+
+# Sources that define each profiled kernel family (relative to the package).
+KERNEL_SOURCES = {
+    "big_gemm_kernel": ["csrc/gemm_big.hip", "csrc/gemm_big.h", "csrc/common.h"],
+    "mx_decode_kernel": ["csrc/decode.hip", "csrc/common.h"],
+}
+
+
+def family(kernel: str) -> str:
+    for fam in KERNEL_SOURCES:
+        if fam in kernel:
+            return fam
+    raise KeyError(f"no source list for kernel {kernel!r}")
+
+
+def sources_digest(fam: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[fam]:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def _csv(path_or_dir: str, suffix: str) -> str:
+    if os.path.isdir(path_or_dir):
+        hits = sorted(glob.glob(os.path.join(path_or_dir, "**", f"*{suffix}"), recursive=True))
+        if not hits:
+            raise FileNotFoundError(f"no *{suffix} under {path_or_dir}")
+        return hits[0]
+    return path_or_dir
+
+
+def short_name(name: str) -> str:
+    name = name.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+    if name.endswith(")"):  # drop the parameter list (the last balanced group)
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                name = name[:i]
+                break
+    return name
+
+
+def kernel_stats(path: str):
+    rows = list(csv.DictReader(open(_csv(path, "kernel_stats.csv"))))
+    out = []
+    for r in rows:
+        out.append({"name": short_name(r["Name"]), "calls": int(r["Calls"]),
+                    "avg_us": float(r["AverageNs"]) / 1e3, "total_us": float(r["TotalDurationNs"]) / 1e3,
+                    "pct": float(r["Percentage"])})
+    return out
+
+
+def counter_means(path: str, counter: str):
+    """Mean counter value per dispatch, per kernel name."""
+    acc = defaultdict(list)
+    for r in csv.DictReader(open(_csv(path, "counter_collection.csv"))):
+        if r["Counter_Name"] == counter:
+            acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def _pick(means, substring):
+    hits = [(k, v) for k, v in means.items() if substring in k]
+    if len(hits) != 1:
+        raise ValueError(f"{len(hits)} kernels match {substring!r}: {[short_name(k) for k, _ in hits]}")
+    return hits[0]
+
+
+def cmd_stats(a):
+    rows = kernel_stats(a.csv)
+    lines = [f"# {a.title}", "", "Command:", "", "```", a.command, "```", "",
+             "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
+    for r in rows[: a.top]:
+        lines.append(f"| `{r['name']}` | {r['calls']} | {r['avg_us']:.2f} | {r['total_us']:.1f} | {r['pct']:.1f} |")
+    if a.note:
+        lines += ["", a.note]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {a.out}")
+
+
+def cmd_traffic(a):
+    copy_kib_f = max(v for v, _ in counter_means(a.copy_fetch, "FETCH_SIZE").values())
+    copy_kib_w = max(v for v, _ in counter_means(a.copy_write, "WRITE_SIZE").values())
+    f_scale = a.copy_bytes / (copy_kib_f * 1024.0)
+    w_scale = a.copy_bytes / (copy_kib_w * 1024.0)
+    kname, (fetch_kib, nf) = _pick(counter_means(a.fetch, "FETCH_SIZE"), a.kernel)
+    _, (write_kib, nw) = _pick(counter_means(a.write, "WRITE_SIZE"), a.kernel)
+    fetch_b = fetch_kib * 1024.0 * f_scale
+    write_b = write_kib * 1024.0 * w_scale
+    fam = family(kname)
+    lines = [
+        f"# HBM traffic of `{short_name(kname)}` ({a.workload})", "",
+        "Commands (counters in separate passes, then this summary):", "", "```", a.command, "```", "",
+        "| quantity | value |", "|---|---:|",
+        f"| copy calibration: bytes copied | {a.copy_bytes} |",
+        f"| copy FETCH_SIZE (KiB) | {copy_kib_f:.1f} |",
+        f"| copy WRITE_SIZE (KiB) | {copy_kib_w:.1f} |",
+        f"| FETCH scale (bytes per counted byte) | {f_scale:.4f} |",
+        f"| WRITE scale (bytes per counted byte) | {w_scale:.4f} |",
+        f"| kernel FETCH_SIZE per dispatch (KiB, mean of {nf}) | {fetch_kib:.1f} |",
+        f"| kernel WRITE_SIZE per dispatch (KiB, mean of {nw}) | {write_kib:.1f} |",
+        f"| HBM bytes read per launch (scaled) | {fetch_b:.0f} |",
+        f"| HBM bytes written per launch (scaled) | {write_b:.0f} |",
+        "",
+        f"workload: {a.workload}",
+        f"kernel: {short_name(kname)}",
+        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"sources_sha256: {sources_digest(fam)}",
+    ]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {a.out}: {fetch_b + write_b:.0f} bytes per launch")
+
+
+def read_traffic(workload: str, kernel_family: str):
+    """(bytes per launch, path) from profiles/ if its sources digest still
+    matches the current sources of the kernel, else (None, reason)."""
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*traffic*.md"))):
+        kv = {}
+        for line in open(path):
+            if ":" in line and not line.startswith(("|", "#", " ")):
+                k, _, v = line.partition(":")
+                kv[k.strip()] = v.strip()
+        if kv.get("workload") != workload or kernel_family not in kv.get("kernel", ""):
+            continue
+        if kv.get("sources_sha256") != sources_digest(kernel_family):
+            return None, f"{os.path.relpath(path, ROOT)}: kernel sources changed since measured"
+        return float(kv["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    return None, "no traffic profile for this workload"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    s.add_argument("--top", type=int, default=12)
+    s.add_argument("--note", default="")
+    t = sub.add_parser("traffic")
+    for k in ("workload", "kernel", "fetch", "write", "copy_fetch", "copy_write", "command", "out"):
+        t.add_argument("--" + k.replace("_", "-"), required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    a = ap.parse_args()
+    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()
