@@ -60,7 +60,9 @@ def algorithmic_work(L, counts):
 
 
 def cpu_baseline(L, budget_s=15.0, threads=16):
-    """Time the float64 oracle on a token sample (about budget_s seconds)."""
+    """Time the float64 oracle on a token sample: a probe on 64 tokens sizes
+    the sample to about budget_s seconds; a sample that is the whole batch is
+    repeated until about 10 s of work have been timed."""
     import oracle
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -71,13 +73,16 @@ def cpu_baseline(L, budget_s=15.0, threads=16):
         dt = time.perf_counter() - t0
         if dt < budget_s / 3 and m < L["n"]:
             m = int(min(L["n"], max(m, m * budget_s / max(dt, 1e-3))))
+        runs, total = 0, 0.0
+        while runs == 0 or total < 10.0:
             t0 = time.perf_counter()
             oracle.forward(L, L["k"], L["renorm"], rows=np.arange(m))
-            dt = time.perf_counter() - t0
+            total += time.perf_counter() - t0
+            runs += 1
         used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": m / dt, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+    return {"value": m * runs / total, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
             "sample": f"float64 dense-then-masked oracle on the first {m} of {L['n']} tokens "
-                      f"(all {L['E']} experts per token), one run, {dt:.2f} s"}
+                      f"(all {L['E']} experts per token), {runs} run(s), {total:.2f} s"}
 
 
 def main():
@@ -137,16 +142,19 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # One event per step boundary on the launch stream: the K steps run back
+    # to back, and the per-step spread (p10/p50/p90) comes from the same run.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     wall0 = time.perf_counter()
-    t_start.record(stream)
+    marks[0].record(stream)
     for i in range(args.steps):
         step(i)
-    t_end.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
 
     # Routing of this batch (for the work model and the dominant-kernel loop).
@@ -211,6 +219,7 @@ def main():
         "config": {"workload": name, "n": wl.n, "d": wl.d, "E": wl.E, "k": wl.k, "d_ff": wl.d_ff,
                    "weights": wl.wdt, "activations": wl.act, "weight_copies": len(copies),
                    "layer_tflops": layer_tflops},
+        "step_ms": pct,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -115,6 +115,25 @@ size_t moe_workspace_bytes(const moe_shape *s, int w_dtype);
 int moe_router_topk(const moe_shape *s, const void *x, int act, const void *wg,
                     const float *bias, float *logits, int32_t *topk_idx,
                     float *topk_w, void *stream);
+
+/* Router statistics and the load-balancing loss (load-balancing section of
+ * the MoE page): P_i, the router probability of expert i averaged over the
+ * n tokens; f_i, the fraction of tokens whose highest-scoring expert (the
+ * first of its k) is i; and alpha * E * sum_i f_i P_i, which is 1 (times
+ * alpha) when routing is uniform and E * P_1 when every token picks one
+ * expert.  Per-expert counts over all k slots are moe_dispatch's counts.
+ *   logits   [n][E] f32 input (as written by moe_router_topk; bias included)
+ *   topk_idx [n][k] int32 input (every value in [0, E))
+ *   P, f     [E] f32 outputs; loss: one f32 output
+ *   ws / ws_bytes: device workspace of at least
+ *           moe_router_stats_workspace_bytes(s) bytes (per-token softmax
+ *           normalisers), 16-byte aligned.
+ * Sums run in a fixed order (deterministic); the softmax subtracts each
+ * row's maximum. */
+size_t moe_router_stats_workspace_bytes(const moe_shape *s);
+int moe_router_stats(const moe_shape *s, const float *logits, const int32_t *topk_idx,
+                     float alpha, float *P, float *f, float *loss, void *ws, size_t ws_bytes,
+                     void *stream);
 
 /* Dispatch (forward-pass section of the MoE page): regroup the n*k
  * (token, slot) pairs into per-expert piles, expert by expert, each pile in

@@ -58,6 +58,10 @@ lib.moe_workspace_bytes.restype = _SZ
 lib.moe_workspace_bytes.argtypes = [_SP, _I]
 lib.moe_router_topk.restype = _I
 lib.moe_router_topk.argtypes = [_SP, _P, _I, _P, _P, _P, _P, _P, _P]
+lib.moe_router_stats_workspace_bytes.restype = _SZ
+lib.moe_router_stats_workspace_bytes.argtypes = [_SP]
+lib.moe_router_stats.restype = _I
+lib.moe_router_stats.argtypes = [_SP, _P, _P, ctypes.c_float, _P, _P, _P, _P, _SZ, _P]
 lib.moe_dispatch.restype = _I
 lib.moe_dispatch.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _I, _P, _P, _SZ, _P]
 lib.moe_grouped_ffn.restype = _I
@@ -72,6 +76,7 @@ lib.moe_forward.restype = _I
 lib.moe_forward.argtypes = [_SP, _P, _I, _P, _P, _WP, _P, _I, _P, _P, _P, _SZ, _P]
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_bytes", "moe_router_topk",
+           "moe_router_stats_workspace_bytes", "moe_router_stats",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
            "moe_forward")
 
@@ -132,6 +137,16 @@ def moe_router_topk(shape, x, act, wg, bias, logits, topk_idx, topk_w, stream=No
     _check("moe_router_topk", lib.moe_router_topk(
         ctypes.byref(_shape(shape)), _ptr(x), _dt(act), _ptr(wg), _ptr(bias), _ptr(logits),
         _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
+
+
+def moe_router_stats_workspace_bytes(shape) -> int:
+    return int(lib.moe_router_stats_workspace_bytes(ctypes.byref(_shape(shape))))
+
+
+def moe_router_stats(shape, logits, topk_idx, alpha, P, f, loss, ws, ws_bytes, stream=None):
+    _check("moe_router_stats", lib.moe_router_stats(
+        ctypes.byref(_shape(shape)), _ptr(logits), _ptr(topk_idx), float(alpha), _ptr(P), _ptr(f),
+        _ptr(loss), _ptr(ws), int(ws_bytes), _stream(stream)))
 
 
 def moe_dispatch(shape, topk_idx, counts, offsets, perm, inv, x=None, act="bf16", x_perm=None,

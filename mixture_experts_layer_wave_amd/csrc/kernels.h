@@ -25,6 +25,12 @@ hipError_t launch_router_topk(const float *part, int splits, int n, int E, int k
 hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *counts,
                            int32_t *offsets, int32_t *perm, int32_t *inv,
                            hipStream_t st);
+// Router statistics (stats.hip): P [E], f [E], loss [1]; norm is [n]
+// scratch for the per-token softmax normalisers.
+hipError_t launch_router_stats(const float *logits, const int32_t *idx, int n, int E, int k,
+                               float alpha, float *P, float *f, float *loss, float2 *norm,
+                               hipStream_t st);
+
 // Top-k and dispatch in one workgroup (small batches: n <= kRouteSmallN).
 constexpr int kRouteSmallN = 64;
 hipError_t launch_route_dispatch(const float *part, int splits, int n, int E, int k, bool renorm,

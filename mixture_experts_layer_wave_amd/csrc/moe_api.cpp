@@ -153,6 +153,23 @@ int moe_router_topk(const moe_shape *s, const void *x, int act, const void *wg,
                                             topk_w, nullptr, hs));
 }
 
+size_t moe_router_stats_workspace_bytes(const moe_shape *s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return align_up((size_t)s->n * sizeof(float2));
+}
+
+int moe_router_stats(const moe_shape *s, const float *logits, const int32_t *topk_idx,
+                     float alpha, float *P, float *f, float *loss, void *ws, size_t ws_bytes,
+                     void *stream) {
+  int st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_idx || !P || !f || !loss) return MOE_ERR_NULL;
+  if (!ws || ws_bytes < moe_router_stats_workspace_bytes(s)) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_router_stats(logits, topk_idx, s->n, s->E, s->k, alpha, P, f,
+                                             loss, (float2 *)ws, (hipStream_t)stream));
+}
+
 int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
                  int32_t *offsets, int32_t *perm, int32_t *inv, const void *x, int act,
                  void *x_perm, void *ws, size_t ws_bytes, void *stream) {

@@ -103,3 +103,22 @@ def test_product_path_fails_loudly_without_library(tmp_path):
     code = "import mixture_experts_layer_wave_amd.binding"
     r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "not built" in r.stderr
+
+
+def test_router_stats_errors_before_launch():
+    import ctypes
+
+    from mixture_experts_layer_wave_amd import binding as B
+
+    shape = (100, 64, 8, 2, 64)
+    sp = ctypes.byref(B._shape(shape))
+    need = B.moe_router_stats_workspace_bytes(shape)
+    assert need >= 100 * 8 and need % 256 == 0
+    assert B.moe_router_stats_workspace_bytes((0, 64, 8, 2, 64)) == 0
+    fake = 1 << 20  # never dereferenced: every check below fails before a launch
+    assert B.lib.moe_router_stats(None, fake, fake, 1.0, fake, fake, fake, fake, need, None) == -1
+    assert B.lib.moe_router_stats(sp, None, fake, 1.0, fake, fake, fake, fake, need, None) == -1
+    assert B.lib.moe_router_stats(sp, fake, fake, 1.0, fake, fake, None, fake, need, None) == -1
+    assert B.lib.moe_router_stats(sp, fake, fake, 1.0, fake, fake, fake, None, need, None) == -5
+    assert B.lib.moe_router_stats(sp, fake, fake, 1.0, fake, fake, fake, fake, need - 1, None) == -5
+    assert B.lib.moe_router_stats(sp, fake, fake, 1.0, fake, fake, fake, fake + 4, need, None) == -4
