@@ -15,6 +15,8 @@
 // accumulate).  MXFP4 tiles are dequantised to bf16 as they are written to
 // LDS (v_cvt_scalef32_pk_bf16_fp4: E2M1 x 2^(s-127) is exact in bf16), so
 // the MFMA loop is shared.  float32 weights take a plain FMA path.
+#include <cmath>
+
 #include "common.h"
 #include "gemm_big.h"
 #include "kernels.h"
@@ -327,6 +329,39 @@ bool big_ok(const FfnArgs &a, size_t a_bytes, int N, int K) {
   return K % 8 == 0;
 }
 
+// Block-tile choice for the large-tile kernel.  Pile sizes live on the
+// device, so the host estimates them: R rows over min(E, R) piles, each pile
+// at most its mean plus two binomial standard deviations (uniform routing).
+// A candidate's cost is the number of rounds of blocks over the 256 CUs
+// times the bytes one block loads per K step times the K steps: the kernel
+// is bound by loading its tiles, and a round lasts as long as its slowest
+// block.
+struct TileChoice {
+  int bm, bnb;
+};
+
+TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_cand) {
+  const int N = up ? a.d_ff : a.d, K = up ? a.d : a.d_ff;
+  const int piles = a.E < a.R ? a.E : a.R;
+  const double avg = (double)a.R / piles;
+  const double big = avg + 2.0 * sqrt(avg * (1.0 - 1.0 / a.E));
+  const long long nk = (K + 63) / 64;
+  TileChoice best = cand[0];
+  double best_cost = 0;
+  for (int i = 0; i < n_cand; ++i) {
+    const int cols = up ? cand[i].bnb / 2 : cand[i].bnb;
+    const long long mt = (long long)piles * (long long)ceil(fmin(big, (double)a.R) / cand[i].bm);
+    const long long nt = (N + cols - 1) / cols;
+    const long long rounds = (mt * nt + 255) / 256;
+    const double cost = (double)rounds * nk * (cand[i].bm + cand[i].bnb);
+    if (i == 0 || cost < best_cost) {
+      best = cand[i];
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 BigGemmParams big_params(const FfnArgs &a, bool up) {
   BigGemmParams p{};
   p.offsets = a.offsets;
@@ -377,9 +412,11 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   }
   const size_t a_bytes = (size_t)(a.perm ? a.n : a.R) * a.d * 2;
   if (big_ok(a, a_bytes, a.d_ff, a.d)) {
+    static const TileChoice cand[2] = {{256, 256}, {320, 256}};
+    const TileChoice t = choose_tile(a, true, cand, a.w_dtype == 2 ? 1 : 2);
     BigGemmParams p = big_params(a, true);
-    p.n_tiles = (a.d_ff + 127) / 128;
-    return launch_big_gemm(p, true, a.w_dtype == 2, a.perm != nullptr, false, 256, 256, st);
+    p.n_tiles = (a.d_ff + t.bnb / 2 - 1) / (t.bnb / 2);
+    return launch_big_gemm(p, true, a.w_dtype == 2, a.perm != nullptr, false, t.bm, t.bnb, st);
   }
   GemmParams up{};
   up.a = (const uint16_t *)a.a;
@@ -410,18 +447,11 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
     return hipGetLastError();
   }
   if (big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff)) {
-    // Largest block tile that still gives every CU a tile (256 CUs).
-    static const int cfg[3][2] = {{256, 256}, {256, 128}, {128, 128}};
-    int bm = 128, bnb = 128;
-    for (int i = 0; i < 3; ++i) {
-      const long long blocks = (long long)((a.R + cfg[i][0] - 1) / cfg[i][0]) *
-                               ((a.d + cfg[i][1] - 1) / cfg[i][1]);
-      if (blocks >= 256) {
-        bm = cfg[i][0];
-        bnb = cfg[i][1];
-        break;
-      }
-    }
+    static const TileChoice cand_bf16[4] = {{256, 256}, {320, 256}, {256, 128}, {128, 128}};
+    static const TileChoice cand_mx[3] = {{256, 256}, {256, 128}, {128, 128}};
+    const TileChoice t = a.w_dtype == 2 ? choose_tile(a, false, cand_mx, 3)
+                                        : choose_tile(a, false, cand_bf16, 4);
+    const int bm = t.bm, bnb = t.bnb;
     BigGemmParams p = big_params(a, false);
     p.n_tiles = (a.d + bnb - 1) / bnb;
     const bool fuse = a.fuse_y != nullptr && a.k == 1;

@@ -30,6 +30,7 @@
 // list is cut into 8 contiguous chunks, one per XCD (workgroup i runs on XCD
 // i mod 8), so the tiles that share an expert's weights share one L2.
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 #include "gemm_big.h"
@@ -283,37 +284,48 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   // read while the MFMAs of slice kk run; scheduling groups pin the order
   // "MFMA, LDS read, MFMA, LDS read, ..." inside a slice (and spread the DMA
   // issue of a later step over slice 0), and slices do not mix.
-  auto read_frags = [&](const uint8_t *sa, const uint8_t *sb, int kk, bf16x8 *af, bf16x8 *bfr) {
+  //
+  // ACT (a compile-time count) is the number of this wave's 32-row groups
+  // that hold pile rows: the last row tile of a pile is usually ragged, and
+  // its empty groups are neither read from LDS nor multiplied.  A wave with
+  // ACT = 0 still issues its share of the copies and meets every barrier.
+  constexpr int NV = T::A_RUNS + (MX ? 0 : T::B_RUNS);  // DMA issues per step
+  auto read_frags = [&](auto actc, const uint8_t *sa, const uint8_t *sb, int kk, bf16x8 *af,
+                        bf16x8 *bfr) {
+    constexpr int ACT = decltype(actc)::value;
     const int ch = kk * 2 + lg;
 #pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm)
+    for (int tm = 0; tm < ACT; ++tm)
       af[tm] = *(const bf16x8 *)(sa + swz<BK>(wm * T::WM + tm * 32 + lr, ch));
+    if constexpr (ACT > 0) {
 #pragma unroll
-    for (int tn = 0; tn < T::TN; ++tn) bfr[tn] = *(const bf16x8 *)(sb + swz<BK>(brow(tn), ch));
+      for (int tn = 0; tn < T::TN; ++tn) bfr[tn] = *(const bf16x8 *)(sb + swz<BK>(brow(tn), ch));
+    }
   };
-  auto mfmas = [&](const bf16x8 *af, const bf16x8 *bfr) {
+  auto mfmas = [&](auto actc, const bf16x8 *af, const bf16x8 *bfr) {
+    constexpr int ACT = decltype(actc)::value;
 #pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm)
+    for (int tm = 0; tm < ACT; ++tm)
 #pragma unroll
       for (int tn = 0; tn < T::TN; ++tn)
         acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
   };
-  constexpr int NF = T::TM + T::TN;                     // fragment reads per slice
-  constexpr int NM = T::TM * T::TN;                     // MFMAs per slice
-  constexpr int NV = T::A_RUNS + (MX ? 0 : T::B_RUNS);  // DMA issues per step
-  auto step = [&](int stage, int kt_issue, int stage_issue) {
+  auto step = [&](auto actc, int stage, int kt_issue, int stage_issue) {
+    constexpr int ACT = decltype(actc)::value;
+    constexpr int NF = ACT > 0 ? ACT + T::TN : 0;  // fragment reads per slice
+    constexpr int NM = ACT * T::TN;                // MFMAs per slice
     const uint8_t *sa = smem + stage * T::STAGE;
     const uint8_t *sb = sa + T::A_BYTES;
     bf16x8 a0[T::TM], b0[T::TN], a1[T::TM], b1[T::TN];
-    read_frags(sa, sb, 0, a0, b0);
+    read_frags(actc, sa, sb, 0, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < T::SLICES; ++kk) {
       bf16x8 *ac = (kk & 1) ? a1 : a0, *bc = (kk & 1) ? b1 : b0;
       bf16x8 *an = (kk & 1) ? a0 : a1, *bn = (kk & 1) ? b0 : b1;
-      if (kk + 1 < T::SLICES) read_frags(sa, sb, kk + 1, an, bn);
+      if (kk + 1 < T::SLICES) read_frags(actc, sa, sb, kk + 1, an, bn);
       if (kk == 0) issue(kt_issue, stage_issue);
-      mfmas(ac, bc);
+      mfmas(actc, ac, bc);
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -325,15 +337,36 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   };
 
   const int nk = (K + BK - 1) / BK;
+  auto kloop = [&](auto actc) {
+    for (int kt = 0; kt < nk; ++kt) {
+      // Step kt's loads are done once at most NST - 2 later steps are pending.
+      wait_vmcnt<(NST - 2) * NV>();
+      __syncthreads();
+      step(actc, kt % NST, kt + NST - 1, (kt + NST - 1) % NST);
+      if (MX && kt + 1 < nk) mx_store((kt + 1) % NST);
+    }
+  };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue(s, s);
   mx_store(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // Step kt's loads are done once at most NST - 2 later steps are pending.
-    wait_vmcnt<(NST - 2) * NV>();
-    __syncthreads();
-    step(kt % NST, kt + NST - 1, (kt + NST - 1) % NST);
-    if (MX && kt + 1 < nk) mx_store((kt + 1) % NST);
+  const int act = __builtin_amdgcn_readfirstlane(min(T::TM, max(0, (rows - wm * T::WM + 31) / 32)));
+  static_assert(T::TM >= 2 && T::TM <= 5, "row groups per wave");
+  if (act == T::TM) {
+    kloop(std::integral_constant<int, T::TM>{});
+  } else if (act == 0) {
+    kloop(std::integral_constant<int, 0>{});
+  } else if (act == 1) {
+    kloop(std::integral_constant<int, 1>{});
+  } else if constexpr (T::TM >= 3) {
+    if (act == 2) {
+      kloop(std::integral_constant<int, 2>{});
+    } else if constexpr (T::TM >= 4) {
+      if (act == 3) {
+        kloop(std::integral_constant<int, 3>{});
+      } else if constexpr (T::TM >= 5) {
+        kloop(std::integral_constant<int, 4>{});
+      }
+    }
   }
   wait_vmcnt<0>();
 
@@ -436,6 +469,10 @@ hipError_t launch_big_gemm(const BigGemmParams &p, bool up, bool mx, bool gather
   // up: gather from X or contiguous rows; bf16 or MXFP4 weights
   MOE_BIG(true, false, true, false, 256, 256)
   MOE_BIG(true, false, false, false, 256, 256)
+  MOE_BIG(true, false, true, false, 320, 256)
+  MOE_BIG(true, false, false, false, 320, 256)
+  MOE_BIG(false, false, false, false, 320, 256)
+  MOE_BIG(false, false, false, true, 320, 256)
   MOE_BIG(true, true, true, false, 256, 256)
   MOE_BIG(true, true, false, false, 256, 256)
   // down: f32 pile outputs, or the combine fused for one expert per token
