@@ -159,7 +159,8 @@ int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
  *   offsets [E+1]    int32, device, as produced by moe_dispatch
  *   y_perm  [n*k][d] float32 output (out must be MOE_F32)
  *   ws      device workspace of at least moe_workspace_bytes(s, w->dtype).
- * offsets is read on the device only; empty experts cost nothing. */
+ * offsets is read on the device only; empty experts cost nothing.
+ * With BF16/MXFP4 weights, x_perm and y_perm must be 16-byte aligned. */
 int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act,
                     const int32_t *offsets, const moe_expert_weights *w,
                     void *y_perm, int out, void *ws, size_t ws_bytes,
@@ -175,7 +176,8 @@ int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act,
  *   even), f32 for F32 weights.
  * moe_expert_down: y_perm[r] = h[r] W2_e^T ("Dense models" section:
  *   down-projection), y_perm [n*k][d] f32.
- * offsets [E+1] as produced by moe_dispatch; read on the device only. */
+ * offsets [E+1] as produced by moe_dispatch; read on the device only.
+ * With BF16/MXFP4 weights, a, h and y_perm must be 16-byte aligned. */
 int moe_expert_up(const moe_shape *s, const void *a, int act, const int32_t *perm,
                   const int32_t *offsets, const moe_expert_weights *w, void *h,
                   void *stream);

@@ -22,16 +22,15 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// float32 -> bfloat16 bits, round to nearest even; NaN stays NaN.
+// float32 -> bfloat16 bits, round to nearest even (v_cvt_pk_bf16_f32 on
+// gfx950); NaN stays NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -83,7 +82,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigma(g) = g / (1 + e^-g), with the hardware exp2 and
+// reciprocal (about 1 ulp each) in place of a correctly rounded division.
+// g -> -inf gives e^-g = inf and a reciprocal of 0, so the limit 0 holds.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
+}
 
 // E8M0 scale code -> float (2^(s-127)); 0 -> 2^-127 (subnormal), 255 -> NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {

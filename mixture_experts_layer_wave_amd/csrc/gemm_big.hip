@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
     for (int tm = 0; tm < ACT; ++tm)
 #pragma unroll
       for (int tn = 0; tn < T::TN; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[tn], af[tm], acc[tm][tn], 0, 0, 0);
   };
   auto step = [&](auto actc, int stage, int kt_issue, int stage_issue) {
     constexpr int ACT = decltype(actc)::value;
@@ -371,30 +371,37 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   wait_vmcnt<0>();
 
   // ---- epilogue --------------------------------------------------------------
-  // 32x32 accumulator: element i of lane l is row (i/4)*8 + (l/32)*4 + i%4,
-  // column l % 32.
+  // The MFMA takes the weight rows as its first operand, so accumulator
+  // element i of lane l is pile row l % 32 of the 32-row group and output
+  // column (i/4)*8 + (l/32)*4 + i%4 of the 32-column group: every lane holds
+  // runs of four consecutive columns of one row.
   if constexpr (UP || FUSE) {
-    // bf16 output staged through LDS so that global stores are 16-B rows.
+    // bf16 output staged through LDS (8-B writes of four columns) so that
+    // global stores are 16-B pieces of rows.
     constexpr int OC = UP ? BNB / 2 : BNB;  // output columns of the tile
     constexpr int PITCH = OC * 2 + 16;       // bytes per staged row (padded)
     __syncthreads();  // every wave is done reading the stages
     uint8_t *so = smem;
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) {
+      const int r = wm * T::WM + tm * 32 + lr;
+      float scale = 1.f;
+      if constexpr (!UP) scale = p.comb_w[p.perm_out[row0 + min(r, rows - 1)]];
 #pragma unroll
       for (int j = 0; j < (UP ? T::TN / 2 : T::TN); ++j) {
-        const int col = (UP ? wn * (T::WN / 2) : wn * T::WN) + j * 32 + lr;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = wm * T::WM + tm * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
-          float v;
-          if constexpr (UP) {
-            v = silu(acc[tm][j][i]) * acc[tm][j + T::TN / 2][i];
-          } else {
-            const int rr = row0 + min(r, rows - 1);
-            v = acc[tm][j][i] * p.comb_w[p.perm_out[rr]];
+        for (int g = 0; g < 4; ++g) {
+          const int col = (UP ? wn * (T::WN / 2) : wn * T::WN) + j * 32 + g * 8 + lg * 4;
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if constexpr (UP)
+              v[q] = silu(acc[tm][j][g * 4 + q]) * acc[tm][j + T::TN / 2][g * 4 + q];
+            else
+              v[q] = acc[tm][j][g * 4 + q] * scale;
           }
-          *(uint16_t *)(so + r * PITCH + col * 2) = (uint16_t)f32_to_bf16_bits(v);
+          const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *(u32x2 *)(so + r * PITCH + col * 2) = pk;
         }
       }
     }
@@ -419,18 +426,23 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
       }
     }
   } else {
+    // f32 pile outputs: 16-B stores of four columns (N is a multiple of 8).
     float *y = (float *)p.out;
 #pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm)
+    for (int tm = 0; tm < T::TM; ++tm) {
+      const int r = wm * T::WM + tm * 32 + lr;
 #pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn) {
-        const int col = n0 + wn * T::WN + tn * 32 + lr;
+      for (int tn = 0; tn < T::TN; ++tn)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = wm * T::WM + tm * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
-          if (r < rows && col < N) y[(size_t)(row0 + r) * N + col] = acc[tm][tn][i];
+        for (int g = 0; g < 4; ++g) {
+          const int col = n0 + wn * T::WN + tn * 32 + g * 8 + lg * 4;
+          if (r < rows && col < N) {
+            const f32x4 v = {acc[tm][tn][g * 4], acc[tm][tn][g * 4 + 1], acc[tm][tn][g * 4 + 2],
+                             acc[tm][tn][g * 4 + 3]};
+            *(f32x4 *)(y + (size_t)(row0 + r) * N + col) = v;
+          }
         }
-      }
+    }
   }
 }
 

@@ -204,7 +204,7 @@ int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act, const int32
   if (st != MOE_OK) return st;
   if (!x_perm || !offsets || !y_perm) return MOE_ERR_NULL;
   if (out != MOE_F32) return MOE_ERR_DTYPE;
-  if (act == MOE_BF16 && !aligned16(x_perm)) return MOE_ERR_ALIGN;
+  if (act == MOE_BF16 && (!aligned16(x_perm) || !aligned16(y_perm))) return MOE_ERR_ALIGN;
   const WsLayout L = layout(s, w->dtype);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
@@ -233,7 +233,7 @@ int moe_expert_down(const moe_shape *s, const void *h, const int32_t *offsets,
   st = check_weights(s, w->dtype == MOE_F32 ? MOE_F32 : MOE_BF16, w);
   if (st != MOE_OK) return st;
   if (!h || !offsets || !y_perm) return MOE_ERR_NULL;
-  if (w->dtype != MOE_F32 && !aligned16(h)) return MOE_ERR_ALIGN;
+  if (w->dtype != MOE_F32 && (!aligned16(h) || !aligned16(y_perm))) return MOE_ERR_ALIGN;
   const moe::FfnArgs f = ffn_args(s, nullptr, nullptr, offsets, w, (void *)h, y_perm);
   return hip_status(moe::launch_expert_down(f, (hipStream_t)stream));
 }
