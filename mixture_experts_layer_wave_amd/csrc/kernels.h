@@ -22,6 +22,9 @@ hipError_t launch_router_topk(const float *part, int splits, int n, int E, int k
                               int32_t *idx, float *w, float *logits, hipStream_t st);
 
 // ---- dispatch -------------------------------------------------------------
+// Up to kDispSmallR pairs one wave builds the piles (dispatch_wave), else one
+// 1024-thread workgroup does (dispatch_block); both give the same piles.
+constexpr int kDispSmallR = 256;
 hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *counts,
                            int32_t *offsets, int32_t *perm, int32_t *inv,
                            hipStream_t st);
@@ -31,11 +34,6 @@ hipError_t launch_router_stats(const float *logits, const int32_t *idx, int n, i
                                float alpha, float *P, float *f, float *loss, float2 *norm,
                                hipStream_t st);
 
-// Top-k and dispatch in one workgroup (small batches: n <= kRouteSmallN).
-constexpr int kRouteSmallN = 64;
-hipError_t launch_route_dispatch(const float *part, int splits, int n, int E, int k, bool renorm,
-                                 int32_t *idx, float *w, int32_t *counts, int32_t *offsets,
-                                 int32_t *perm, int32_t *inv, hipStream_t st);
 // x_perm[r] = x[perm[r]] for r < R, rows of row_bytes bytes (multiple of 4).
 hipError_t launch_gather_rows(const void *x, const int32_t *perm, void *x_perm, int R,
                               int row_bytes, hipStream_t st);

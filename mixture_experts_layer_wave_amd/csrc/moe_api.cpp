@@ -278,15 +278,10 @@ int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, cons
   hipError_t e = moe::launch_router_logits(x, wg, bias, logits, s->n, s->d, s->E,
                                            act == MOE_BF16, splits, hs);
   if (e == hipSuccess) {
-    if (s->n <= moe::kRouteSmallN) {  // top-k and dispatch in one workgroup
-      e = moe::launch_route_dispatch(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt,
-                                     counts, offsets, perm, inv, hs);
-    } else {
-      e = moe::launch_router_topk(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt,
-                                  nullptr, hs);
-      if (e == hipSuccess)
-        e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
-    }
+    e = moe::launch_router_topk(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt,
+                                nullptr, hs);
+    if (e == hipSuccess)
+      e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
   }
   bool fused = false;
   if (e == hipSuccess) {

@@ -317,4 +317,57 @@ __device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, 
   }
 }
 
+// Stable piles of R <= 4 * 64 (token, slot) pairs built by one wave in LDS
+// (the small-batch dispatch).  Pairs are taken in (token, slot) order in
+// chunks of 64; a lane's rank among same-expert lanes of its chunk comes
+// from ballots on the bits of the expert id, and a per-expert cursor s_cnt
+// carries the earlier chunks.  Outputs: s_cnt [E] pile sizes, s_off [E+1]
+// pile offsets, s_perm [R] token of each pile row, s_inv [R] pile row of
+// each pair.  The LDS accesses of one wave complete in order, so a chunk's
+// cursor reads see the previous chunk's updates.  Ids outside [0, E) are
+// skipped.
+__device__ __forceinline__ void dispatch_wave(const int32_t *__restrict__ idx, int R, int k,
+                                              int E, int nbits, int *s_cnt, int *s_off,
+                                              int *s_perm, int *s_inv) {
+  const int lane = threadIdx.x & 63;
+  for (int e = lane; e < E; e += MOE_WAVE) s_cnt[e] = 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int ids[4], rk[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int r = c * MOE_WAVE + lane;
+    const int e = r < R ? idx[r] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(same & lt_mask);
+    const int base = valid ? s_cnt[e] : 0;
+    if (valid && rank == 0) s_cnt[e] = base + __popcll(same);
+    ids[c] = valid ? e : -1;
+    rk[c] = base + rank;
+  }
+  int carry = 0;
+  for (int b0 = 0; b0 < E; b0 += MOE_WAVE) {
+    const int e = b0 + lane;
+    const int cnt = e < E ? s_cnt[e] : 0;
+    const int incl = wave_incl_scan(cnt);
+    if (e < E) s_off[e] = carry + incl - cnt;
+    carry += __builtin_amdgcn_readlane(incl, MOE_WAVE - 1);
+  }
+  if (lane == 0) s_off[E] = carry;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int r = c * MOE_WAVE + lane;
+    if (ids[c] >= 0) {
+      const int pos = s_off[ids[c]] + rk[c];
+      s_perm[pos] = r / k;
+      s_inv[r] = pos;
+    }
+  }
+}
+
 }  // namespace moe

@@ -56,7 +56,8 @@ def test_dispatch_of_routed_workloads(name):
     assert np.array_equal(xp.view(want.dtype) if xp.dtype != want.dtype else xp, want)
 
 
-@pytest.mark.parametrize("case", ["one-expert", "empty-experts", "many-chunks", "n1", "e1", "dup-slots"])
+@pytest.mark.parametrize("case", ["one-expert", "empty-experts", "many-chunks", "n1", "e1", "dup-slots",
+                                  "small-256", "small-dups", "small-e1024", "small-257"])
 def test_dispatch_edge_cases(case):
     say(f"[dispatch-edge] {case}")
     rng = np.random.default_rng(sum(map(ord, case)))
@@ -72,6 +73,14 @@ def test_dispatch_edge_cases(case):
         E, idx = 128, np.array([[127, 0, 64, 63]])
     elif case == "e1":
         E, idx = 1, np.zeros((50, 1))
+    elif case == "small-256":  # the one-wave path at its largest: 4 chunks of 64 pairs
+        E, idx = 128, rng.integers(0, 128, size=(64, 4))
+    elif case == "small-dups":  # one-wave path, few experts, repeated slots
+        E, idx = 3, rng.integers(0, 3, size=(70, 3))
+    elif case == "small-e1024":  # one-wave path, offsets scanned over 16 chunks of experts
+        E, idx = 1024, rng.integers(0, 1024, size=(25, 4))
+    elif case == "small-257":  # one pair past the one-wave path
+        E, idx = 16, rng.integers(0, 16, size=(257, 1))
     else:  # a token may list the same expert twice: still a valid grouping input
         E = 4
         idx = rng.integers(0, E, size=(1500, 3))
