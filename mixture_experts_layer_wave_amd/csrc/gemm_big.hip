@@ -189,31 +189,55 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
       b_off[j] = n < N ? ((uint32_t)n * (uint32_t)K + (uint32_t)c * 8u) * 2u : kOOB;
     }
   }
-  // MXFP4 units: thread owns (B-row, 32-K block) pairs u = tid + kNT i.
-  const uint8_t *q_src[MX ? T::MX_UNITS : 1];
-  const uint8_t *s_src[MX ? T::MX_UNITS : 1];
-  bool q_ok[MX ? T::MX_UNITS : 1];
+  // MXFP4 units: thread owns (B-row, 32-K block) pairs u = tid + kNT i, read
+  // with buffer loads from the expert's code and scale matrices (32-bit
+  // offsets; an invalid unit carries kOOB and reads zeros).  Whether a unit
+  // is in W1 or W3 (up) depends on its wave only.
+  __amdgpu_buffer_rsrc_t rq0, rq1, rs0, rs1;
+  uint32_t q_off[MX ? T::MX_UNITS : 1], s_off[MX ? T::MX_UNITS : 1];
   if constexpr (MX) {
+    const size_t qn = (size_t)N * (K / 2), sn = (size_t)N * (K / 32);
+    rq0 = rsrc((const uint8_t *)p.b0 + (size_t)e * qn, (uint32_t)qn);
+    rs0 = rsrc(p.s0 + (size_t)e * sn, (uint32_t)sn);
+    rq1 = UP ? rsrc((const uint8_t *)p.b1 + (size_t)e * qn, (uint32_t)qn) : rq0;
+    rs1 = UP ? rsrc(p.s1 + (size_t)e * sn, (uint32_t)sn) : rs0;
 #pragma unroll
     for (int i = 0; i < T::MX_UNITS; ++i) {
-      const int u = min(tid + kNT * i, T::MX_ALL - 1);
+      const int u = tid + kNT * i;
       const int br = u / (BK / 32), half = u % (BK / 32);
-      const bool second = UP && br >= BNB / 2;
       const int n = UP ? n0 + (br % (BNB / 2)) : n0 + br;
-      q_ok[i] = n < N && tid + kNT * i < T::MX_ALL;
-      const size_t nr = (size_t)e * N + (q_ok[i] ? n : 0);
-      q_src[i] = (const uint8_t *)(second ? p.b1 : p.b0) + nr * (K / 2) + half * 16;
-      s_src[i] = (second ? p.s1 : p.s0) + nr * (K / 32) + half;
+      const bool ok = n < N && u < T::MX_ALL;
+      q_off[i] = ok ? (uint32_t)n * (uint32_t)(K / 2) + half * 16u : kOOB;
+      s_off[i] = ok ? (uint32_t)n * (uint32_t)(K / 32) + half : kOOB;
     }
   }
-
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  u32x4 mq[MX ? T::MX_UNITS : 1];
-  uint32_t ms[MX ? T::MX_UNITS : 1];
+  // MXFP4 codes and scales are loaded into registers one step ahead of the
+  // activation copies (two register slots, by step parity), so a load has
+  // about two steps of compute to land before it is dequantised.
+  u32x4 mq[2][MX ? T::MX_UNITS : 1];
+  uint32_t ms[2][MX ? T::MX_UNITS : 1];
+  auto load_b = [&](int kt, u32x4 *q, uint32_t *sv) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < T::MX_UNITS; ++i) {
+      const int half = (tid + kNT * i) % (BK / 32);
+      const uint32_t pen = (k0 + half * 32 < K) ? 0u : kOOB;
+      // Units u >= (BNB / 2) * (BK / 32) (a multiple of 64) are W3 rows, so
+      // the choice follows the wave index (uniform: one buffer resource).
+      static_assert((BNB / 2) * (BK / 32) % 64 == 0, "W1/W3 split at a wave boundary");
+      const bool second = UP && (wave * 64 + kNT * i) >= (BNB / 2) * (BK / 32);
+      q[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            second ? rq1 : rq0, (q_off[i] + k0 / 2) | pen, 0, 0));
+      sv[i] = __builtin_amdgcn_raw_buffer_load_b8(second ? rs1 : rs0, (s_off[i] + k0 / 32) | pen, 0, 0);
+    }
+  };
 
   // Issue the loads of K step kt into LDS stage `stage` (a step at or past
-  // the end issues only zero loads, which keeps the count per step fixed).
-  auto issue = [&](int kt, int stage) {
+  // the end issues only zero loads, which keeps the count per step fixed),
+  // then (MXFP4) the register loads of step kt + 1 into slot SL = (kt+1) & 1
+  // (a compile-time index: the K loop is unrolled by two).
+  auto issue = [&](int kt, int stage, auto slc) {
+    constexpr int SL = decltype(slc)::value;
     const int k0 = kt * BK;
     const uint32_t kpen = (k0 + c * 8 < K) ? 0u : kOOB;
     const uint32_t k0b = (uint32_t)k0 * 2u;
@@ -228,17 +252,12 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
         dma16(second ? rb1 : rb0, sb + (kNW * j + wave) * 1024, (b_off[j] + k0b) | kpen);
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < T::MX_UNITS; ++i) {
-        const int half = (tid + kNT * i) % (BK / 32);
-        const bool ok = q_ok[i] && (k0 + half * 32 < K);
-        mq[i] = ok ? *(const u32x4 *)(q_src[i] + k0 / 2) : zero4;
-        ms[i] = ok ? (uint32_t)s_src[i][k0 / 32] : 0u;
-      }
+      load_b(kt + 1, mq[SL], ms[SL]);
     }
   };
-  // MXFP4: dequantise the staged codes into the stage's B tile.
-  auto mx_store = [&](int stage) {
+  // MXFP4: dequantise the codes of step kt (register slot kt & 1) into the
+  // B tile of LDS stage `stage`.
+  auto mx_store_slot = [&](int stage, const u32x4 *mqs, const uint32_t *mss) {
     if constexpr (MX) {
       uint8_t *sb = smem + stage * T::STAGE + T::A_BYTES;
 #pragma unroll
@@ -246,10 +265,10 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
         const int u = tid + kNT * i;
         if (T::MX_ALL % kNT != 0 && u >= T::MX_ALL) continue;
         const int br = u / (BK / 32), half = u % (BK / 32);
-        const float sc = e8m0_to_f32(ms[i]);
+        const float sc = e8m0_to_f32(mss[i]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t wv = mq[i][q];
+          const uint32_t wv = mqs[i][q];
           const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 0);
           const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 1);
           const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 2);
@@ -261,6 +280,7 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
       }
     }
   };
+
 
   const int wm = wave / (kNW / 2), wn = wave % (kNW / 2);
   const int lr = lane & 31, lg = lane >> 5;
@@ -310,7 +330,7 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
       for (int tn = 0; tn < T::TN; ++tn)
         acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[tn], af[tm], acc[tm][tn], 0, 0, 0);
   };
-  auto step = [&](auto actc, int stage, int kt_issue, int stage_issue) {
+  auto step = [&](auto actc, int stage, int kt_issue, int stage_issue, auto slc) {
     constexpr int ACT = decltype(actc)::value;
     constexpr int NF = ACT > 0 ? ACT + T::TN : 0;  // fragment reads per slice
     constexpr int NM = ACT * T::TN;                // MFMAs per slice
@@ -324,7 +344,7 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
       bf16x8 *ac = (kk & 1) ? a1 : a0, *bc = (kk & 1) ? b1 : b0;
       bf16x8 *an = (kk & 1) ? a0 : a1, *bn = (kk & 1) ? b0 : b1;
       if (kk + 1 < T::SLICES) read_frags(actc, sa, sb, kk + 1, an, bn);
-      if (kk == 0) issue(kt_issue, stage_issue);
+      if (kk == 0) issue(kt_issue, stage_issue, slc);
       mfmas(actc, ac, bc);
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
@@ -337,18 +357,35 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   };
 
   const int nk = (K + BK - 1) / BK;
+  // Vector memory operations issued after a step's copies: NST - 2 later
+  // steps of copies, or (MXFP4) the register loads of the following step.
+  constexpr int NAFTER = MX ? 2 * T::MX_UNITS : (NST - 2) * NV;
+  // Step kt (parity P = kt & 1): its copies are done once only the later
+  // operations are pending; it issues step kt + 1 (and the MXFP4 registers
+  // of step kt + 2, slot P) and dequantises step kt + 1 (slot 1 - P).
+  auto kstep = [&](auto actc, int kt, auto parc) {
+    constexpr int P = decltype(parc)::value;
+    wait_vmcnt<NAFTER>();
+    __syncthreads();
+    step(actc, kt % NST, kt + NST - 1, (kt + NST - 1) % NST, parc);
+    if (MX && kt + 1 < nk) mx_store_slot((kt + 1) % NST, mq[1 - P], ms[1 - P]);
+  };
   auto kloop = [&](auto actc) {
-    for (int kt = 0; kt < nk; ++kt) {
-      // Step kt's loads are done once at most NST - 2 later steps are pending.
-      wait_vmcnt<(NST - 2) * NV>();
-      __syncthreads();
-      step(actc, kt % NST, kt + NST - 1, (kt + NST - 1) % NST);
-      if (MX && kt + 1 < nk) mx_store((kt + 1) % NST);
+    if constexpr (MX) {
+      for (int kt = 0; kt < nk; kt += 2) {
+        kstep(actc, kt, std::integral_constant<int, 0>{});
+        if (kt + 1 < nk) kstep(actc, kt + 1, std::integral_constant<int, 1>{});
+      }
+    } else {
+      for (int kt = 0; kt < nk; ++kt) kstep(actc, kt, std::integral_constant<int, 0>{});
     }
   };
+  static_assert(NST == 2 || !MX, "MXFP4 register slots assume two LDS stages");
+  if constexpr (MX) load_b(0, mq[0], ms[0]);
+  issue(0, 0, std::integral_constant<int, 1>{});
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue(s, s);
-  mx_store(0);
+  for (int s = 1; s < NST - 1; ++s) issue(s, s, std::integral_constant<int, 0>{});
+  mx_store_slot(0, mq[0], ms[0]);
   const int act = __builtin_amdgcn_readfirstlane(min(T::TM, max(0, (rows - wm * T::WM + 31) / 32)));
   static_assert(T::TM >= 2 && T::TM <= 5, "row groups per wave");
   if (act == T::TM) {
