@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -86,6 +86,16 @@ typedef struct {
   int32_t dtype; /* moe_dtype */
   const void *w1, *w3, *w2;
   const uint8_t *s1, *s3, *s2;
+  /* Logical -> physical expert slots (the hook for a partly resident expert
+   * pool): with slot = NULL the arrays above hold E experts and expert e is
+   * slot e.  Otherwise they hold n_slots physical slots ([n_slots][...] in
+   * every layout above), slot is a DEVICE int32 [E] table read on the
+   * device, and logical expert e (what the router scores and the piles are
+   * keyed by) uses the weights of slot[e].  Entries outside [0, n_slots)
+   * are clamped into it (the kernels never read outside the arrays).
+   * n_slots >= 1 is required when slot is given. */
+  const int32_t *slot;
+  int32_t n_slots;
 } moe_expert_weights;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION). */
@@ -151,6 +161,21 @@ int moe_router_stats(const moe_shape *s, const float *logits, const int32_t *top
 int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
                  int32_t *offsets, int32_t *perm, int32_t *inv, const void *x,
                  int act, void *x_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* Active experts: the deduplicated, ascending list of the experts that a
+ * batch routes at least one row to, read from moe_dispatch's counts.  It is
+ * the set an expert cache must hold for the batch (the minseoc03.com feed's
+ * review of FreeToken, sections "Decode: Exploit Expert Locality" and
+ * "Dynamic Scheduling Without Giving Up CUDA Graphs": deduplicate the
+ * experts and rewrite logical ids to physical cache slots on the GPU; the
+ * slot table of moe_expert_weights is the second half).
+ *   counts   [E] int32 input (device)
+ *   active   [E] int32 output (device): active[j] for j < *n_active is the
+ *            j-th expert with counts[e] > 0; the rest are set to -1
+ *   n_active one int32 output (device)
+ * One workgroup, no host synchronisation. */
+int moe_active_experts(const moe_shape *s, const int32_t *counts, int32_t *active,
+                       int32_t *n_active, void *stream);
 
 /* Grouped expert FFN (forward-pass section): for every expert e, the rows
  * offsets[e] .. offsets[e+1] of x_perm go through expert e:

@@ -33,9 +33,12 @@ class Shape(ctypes.Structure):
 
 
 class ExpertWeights(ctypes.Structure):
+    # slot (device int32 [E]) / n_slots: logical -> physical expert slots;
+    # left at NULL / 0, expert e is slot e.
     _fields_ = [("dtype", ctypes.c_int32),
                 ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p)]
+                ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p),
+                ("slot", ctypes.c_void_p), ("n_slots", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -62,6 +65,8 @@ lib.moe_router_stats_workspace_bytes.restype = _SZ
 lib.moe_router_stats_workspace_bytes.argtypes = [_SP]
 lib.moe_router_stats.restype = _I
 lib.moe_router_stats.argtypes = [_SP, _P, _P, ctypes.c_float, _P, _P, _P, _P, _SZ, _P]
+lib.moe_active_experts.restype = _I
+lib.moe_active_experts.argtypes = [_SP, _P, _P, _P, _P]
 lib.moe_dispatch.restype = _I
 lib.moe_dispatch.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _I, _P, _P, _SZ, _P]
 lib.moe_grouped_ffn.restype = _I
@@ -76,7 +81,7 @@ lib.moe_forward.restype = _I
 lib.moe_forward.argtypes = [_SP, _P, _I, _P, _P, _WP, _P, _I, _P, _P, _P, _SZ, _P]
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_bytes", "moe_router_topk",
-           "moe_router_stats_workspace_bytes", "moe_router_stats",
+           "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_active_experts",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
            "moe_forward")
 
@@ -118,7 +123,8 @@ def _weights(w) -> ExpertWeights:
     if isinstance(w, ExpertWeights):
         return w
     return ExpertWeights(_dt(w["dtype"]), _ptr(w["w1"]), _ptr(w["w3"]), _ptr(w["w2"]),
-                         _ptr(w.get("s1")), _ptr(w.get("s3")), _ptr(w.get("s2")))
+                         _ptr(w.get("s1")), _ptr(w.get("s3")), _ptr(w.get("s2")),
+                         _ptr(w.get("slot")), int(w.get("n_slots", 0)))
 
 
 def moe_abi_version() -> int:
@@ -154,6 +160,11 @@ def moe_dispatch(shape, topk_idx, counts, offsets, perm, inv, x=None, act="bf16"
     _check("moe_dispatch", lib.moe_dispatch(
         ctypes.byref(_shape(shape)), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(perm),
         _ptr(inv), _ptr(x), _dt(act), _ptr(x_perm), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_active_experts(shape, counts, active, n_active, stream=None):
+    _check("moe_active_experts", lib.moe_active_experts(
+        ctypes.byref(_shape(shape)), _ptr(counts), _ptr(active), _ptr(n_active), _stream(stream)))
 
 
 def moe_grouped_ffn(shape, x_perm, act, offsets, weights, y_perm, out, ws, ws_bytes, stream=None):

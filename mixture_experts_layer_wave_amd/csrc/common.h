@@ -82,6 +82,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Physical weight slot of logical expert e: slot[e] clamped into
+// [0, n_slots), or e itself without a table.
+__device__ __forceinline__ int phys_slot(const int32_t *slot, int n_slots, int e) {
+  if (!slot) return e;
+  const int s = slot[e];
+  return s < 0 ? 0 : (s >= n_slots ? n_slots - 1 : s);
+}
+
 // silu(g) = g * sigma(g) = g / (1 + e^-g), with the hardware exp2 and
 // reciprocal (about 1 ulp each) in place of a correctly rounded division.
 // g -> -inf gives e^-g = inf and a reciprocal of 0, so the limit 0 holds.

@@ -91,6 +91,8 @@ struct DecodeParams {
   int E, N, K;             // one expert matrix is N x K (N % 16 == 0; K % 64 == 0 up, % 32 down)
   const uint8_t *w0, *w1;  // codes [E][N][K/2] (w1 = W3 for up)
   const uint8_t *s0, *s1;  // scales [E][N][K/32]
+  const int32_t *slot;     // [E] logical -> physical weight slot, or NULL
+  int n_slots;
   void *out;               // up: bf16 h [R][N]; down: f32 y_perm [R][N]
   StagePlan plan;
 };
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
     }
   };
   auto issue_tile = [&](int e, int tile, int st) {
-    const size_t wrow = (size_t)e * N + (size_t)tile * ROWS;
+    const size_t wrow = (size_t)phys_slot(p.slot, p.n_slots, e) * N + (size_t)tile * ROWS;
     const uint32_t dst = lds_base + st * P.stage_bytes;
     issue_region(p.w0 + wrow * rowb, code_bytes, code_pieces, dst, 0);
     if constexpr (UP) issue_region(p.w1 + wrow * rowb, code_bytes, code_pieces, dst + code_bytes,
@@ -411,6 +413,8 @@ hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st) {
   p.w1 = (const uint8_t *)a.w3;
   p.s0 = a.s1;
   p.s1 = a.s3;
+  p.slot = a.slot;
+  p.n_slots = a.n_slots;
   p.out = a.h;
   return launch_decode<true>(p, st);
 }
@@ -425,6 +429,8 @@ hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st) {
   p.K = a.d_ff;
   p.w0 = (const uint8_t *)a.w2;
   p.s0 = a.s2;
+  p.slot = a.slot;
+  p.n_slots = a.n_slots;
   p.out = a.y_perm;
   return launch_decode<false>(p, st);
 }

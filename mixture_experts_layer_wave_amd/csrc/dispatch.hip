@@ -46,6 +46,25 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t *__re
   }
 }
 
+// Compaction of the experts with a non-empty pile, in expert order: per
+// chunk of 64 experts a ballot gives each active expert its rank.
+__global__ __launch_bounds__(64) void active_experts_kernel(const int32_t *__restrict__ counts,
+                                                            int E, int32_t *__restrict__ active,
+                                                            int32_t *__restrict__ n_active) {
+  const int lane = threadIdx.x;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int base = 0;
+  for (int e0 = 0; e0 < E; e0 += MOE_WAVE) {
+    const int e = e0 + lane;
+    const bool on = e < E && counts[e] > 0;
+    const uint64_t bits = __ballot(on);
+    if (on) active[base + __popcll(bits & lt_mask)] = e;
+    base += __popcll(bits);
+  }
+  for (int j = base + lane; j < E; j += MOE_WAVE) active[j] = -1;
+  if (lane == 0) *n_active = base;
+}
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t *__restrict__ x,
                                                           const int32_t *__restrict__ perm,
                                                           uint32_t *__restrict__ xp, int R,
@@ -93,6 +112,12 @@ hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *cou
   if (err != hipSuccess) return err;
   dispatch_kernel<<<1, kDispThreads, lds, st>>>(idx, n * k, k, E, id_bits(E), counts, offsets,
                                                 perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_active_experts(const int32_t *counts, int E, int32_t *active,
+                                 int32_t *n_active, hipStream_t st) {
+  active_experts_kernel<<<1, MOE_WAVE, 0, st>>>(counts, E, active, n_active);
   return hipGetLastError();
 }
 

@@ -43,12 +43,13 @@ __global__ __launch_bounds__(256) void ffn_up_f32_kernel(const float *__restrict
                                                          int R, int d, int f,
                                                          const float *__restrict__ w1,
                                                          const float *__restrict__ w3,
-                                                         float *__restrict__ h) {
+                                                         const int32_t *__restrict__ slot,
+                                                         int n_slots, float *__restrict__ h) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (long long)R * f) return;
   const int r = (int)(i / f), c = (int)(i % f);
   if (r >= off[E]) return;
-  const int e = expert_of_row(off, E, r);
+  const int e = phys_slot(slot, n_slots, expert_of_row(off, E, r));
   const float *ar = a + (size_t)(perm ? perm[r] : r) * d;
   const float *g1 = w1 + ((size_t)e * f + c) * d;
   const float *g3 = w3 + ((size_t)e * f + c) * d;
@@ -64,12 +65,13 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float *__restri
                                                            const int32_t *__restrict__ off, int E,
                                                            int R, int d, int f,
                                                            const float *__restrict__ w2,
-                                                           float *__restrict__ yp) {
+                                                           const int32_t *__restrict__ slot,
+                                                           int n_slots, float *__restrict__ yp) {
   const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= (long long)R * d) return;
   const int r = (int)(i / d), c = (int)(i % d);
   if (r >= off[E]) return;
-  const int e = expert_of_row(off, E, r);
+  const int e = phys_slot(slot, n_slots, expert_of_row(off, E, r));
   const float *hr = h + (size_t)r * f;
   const float *wr = w2 + ((size_t)e * d + c) * f;
   float acc = 0.f;
@@ -101,6 +103,8 @@ struct GemmParams {
   int E, N, K, n_tiles;
   const void *b0, *b1;      // [E][N][K] (bf16) or [E][N][K/2] (MXFP4); b1 only for up
   const uint8_t *s0, *s1;   // [E][N][K/32] MXFP4 scales
+  const int32_t *slot;      // [E] logical -> physical slot, or NULL
+  int n_slots;
   void *out;                // up: bf16 [R][N]; down: f32 [R][N]
 };
 
@@ -163,6 +167,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
   }
   // B (bf16): same chunk pattern over 128 B-rows.  B (MXFP4): one 32-element
   // half-row (16 B + 1 scale byte) per thread: row tid >> 1, half tid & 1.
+  const int pe = phys_slot(p.slot, p.n_slots, e);  // physical weight slot
   const uint16_t *b_src[4];
   bool b_ok[4];
   const uint8_t *q_src = nullptr, *sc_src = nullptr;
@@ -175,14 +180,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
       const int n = UP ? n0 + (br & 63) : n0 + br;
       const uint16_t *mat = (const uint16_t *)((UP && br >= 64) ? p.b1 : p.b0);
       b_ok[i] = n < N;
-      b_src[i] = mat + ((size_t)e * N + (b_ok[i] ? n : 0)) * K + kc * 8;
+      b_src[i] = mat + ((size_t)pe * N + (b_ok[i] ? n : 0)) * K + kc * 8;
     }
   } else {
     const int n = UP ? n0 + (mrow & 63) : n0 + mrow;
     const uint8_t *mat = (const uint8_t *)((UP && mrow >= 64) ? p.b1 : p.b0);
     const uint8_t *smat = (UP && mrow >= 64) ? p.s1 : p.s0;
     q_ok = n < N;
-    const size_t nr = (size_t)e * N + (q_ok ? n : 0);
+    const size_t nr = (size_t)pe * N + (q_ok ? n : 0);
     q_src = mat + nr * (K / 2) + half * 16;
     sc_src = smat + nr * (K / 32) + half;
   }
@@ -365,6 +370,8 @@ TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_
 BigGemmParams big_params(const FfnArgs &a, bool up) {
   BigGemmParams p{};
   p.offsets = a.offsets;
+  p.slot = a.slot;
+  p.n_slots = a.n_slots;
   p.E = a.E;
   p.R = a.R;
   if (up) {
@@ -407,7 +414,7 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
     const long long tot = (long long)a.R * a.d_ff;
     ffn_up_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
         (const float *)a.a, a.perm, a.offsets, a.E, a.R, a.d, a.d_ff, (const float *)a.w1,
-        (const float *)a.w3, (float *)a.h);
+        (const float *)a.w3, a.slot, a.n_slots, (float *)a.h);
     return hipGetLastError();
   }
   const size_t a_bytes = (size_t)(a.perm ? a.n : a.R) * a.d * 2;
@@ -430,6 +437,8 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   up.b1 = a.w3;
   up.s0 = a.s1;
   up.s1 = a.s3;
+  up.slot = a.slot;
+  up.n_slots = a.n_slots;
   up.out = a.h;
   const int m_tiles = (a.R + kBM - 1) / kBM + (a.E < a.R ? a.E : a.R);
   return a.w_dtype == 2 ? launch_gemm<true, true>(up, m_tiles, a.perm != nullptr, st)
@@ -443,7 +452,8 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d;
     ffn_down_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
-        (const float *)a.h, a.offsets, a.E, a.R, a.d, a.d_ff, (const float *)a.w2, a.y_perm);
+        (const float *)a.h, a.offsets, a.E, a.R, a.d, a.d_ff, (const float *)a.w2, a.slot,
+        a.n_slots, a.y_perm);
     return hipGetLastError();
   }
   if (big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff)) {
@@ -474,6 +484,8 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
   dn.n_tiles = (a.d + 127) / 128;
   dn.b0 = a.w2;
   dn.s0 = a.s2;
+  dn.slot = a.slot;
+  dn.n_slots = a.n_slots;
   dn.out = a.y_perm;
   const int m_tiles = (a.R + kBM - 1) / kBM + (a.E < a.R ? a.E : a.R);
   return a.w_dtype == 2 ? launch_gemm<false, true>(dn, m_tiles, false, st)

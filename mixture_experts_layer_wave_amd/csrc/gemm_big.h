@@ -14,6 +14,8 @@ struct BigGemmParams {
   int E, R, N, K, n_tiles;  // R = rows of the pile matrix; N, K of one expert matrix
   const void *b0, *b1;      // [E][N][K] bf16 or [E][N][K/2] MXFP4; b1 (W3) for up only
   const uint8_t *s0, *s1;   // MXFP4 E8M0 scales [E][N][K/32]
+  const int32_t *slot;      // [E] logical -> physical weight slot, or NULL
+  int n_slots;
   void *out;                // up: bf16 [R][N]; down: f32 [R][N]; fused: bf16 y [n][N]
   const int32_t *perm_out;  // fused combine: pile row -> token
   const float *comb_w;      // fused combine: token -> weight (one expert per token)

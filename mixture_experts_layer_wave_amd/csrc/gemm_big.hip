@@ -175,12 +175,13 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
     }
     a_off[j] = off;
   }
+  const int pe = phys_slot(p.slot, p.n_slots, e);  // physical weight slot
   const size_t mat_elems = (size_t)N * K;
   __amdgpu_buffer_rsrc_t rb0, rb1;
   uint32_t b_off[MX ? 1 : T::B_RUNS];
   if constexpr (!MX) {
-    rb0 = rsrc((const uint16_t *)p.b0 + (size_t)e * mat_elems, (uint32_t)(mat_elems * 2));
-    rb1 = UP ? rsrc((const uint16_t *)p.b1 + (size_t)e * mat_elems, (uint32_t)(mat_elems * 2))
+    rb0 = rsrc((const uint16_t *)p.b0 + (size_t)pe * mat_elems, (uint32_t)(mat_elems * 2));
+    rb1 = UP ? rsrc((const uint16_t *)p.b1 + (size_t)pe * mat_elems, (uint32_t)(mat_elems * 2))
              : rb0;
 #pragma unroll
     for (int j = 0; j < T::B_RUNS; ++j) {
@@ -197,10 +198,10 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   uint32_t q_off[MX ? T::MX_UNITS : 1], s_off[MX ? T::MX_UNITS : 1];
   if constexpr (MX) {
     const size_t qn = (size_t)N * (K / 2), sn = (size_t)N * (K / 32);
-    rq0 = rsrc((const uint8_t *)p.b0 + (size_t)e * qn, (uint32_t)qn);
-    rs0 = rsrc(p.s0 + (size_t)e * sn, (uint32_t)sn);
-    rq1 = UP ? rsrc((const uint8_t *)p.b1 + (size_t)e * qn, (uint32_t)qn) : rq0;
-    rs1 = UP ? rsrc(p.s1 + (size_t)e * sn, (uint32_t)sn) : rs0;
+    rq0 = rsrc((const uint8_t *)p.b0 + (size_t)pe * qn, (uint32_t)qn);
+    rs0 = rsrc(p.s0 + (size_t)pe * sn, (uint32_t)sn);
+    rq1 = UP ? rsrc((const uint8_t *)p.b1 + (size_t)pe * qn, (uint32_t)qn) : rq0;
+    rs1 = UP ? rsrc(p.s1 + (size_t)pe * sn, (uint32_t)sn) : rs0;
 #pragma unroll
     for (int i = 0; i < T::MX_UNITS; ++i) {
       const int u = tid + kNT * i;

@@ -34,6 +34,9 @@ hipError_t launch_router_stats(const float *logits, const int32_t *idx, int n, i
                                float alpha, float *P, float *f, float *loss, float2 *norm,
                                hipStream_t st);
 
+// active[j] = j-th expert with counts > 0 (ascending), -1 after; *n_active.
+hipError_t launch_active_experts(const int32_t *counts, int E, int32_t *active,
+                                 int32_t *n_active, hipStream_t st);
 // x_perm[r] = x[perm[r]] for r < R, rows of row_bytes bytes (multiple of 4).
 hipError_t launch_gather_rows(const void *x, const int32_t *perm, void *x_perm, int R,
                               int row_bytes, hipStream_t st);
@@ -47,6 +50,8 @@ struct FfnArgs {
   int w_dtype;            // 0 f32, 1 bf16, 2 mxfp4
   const void *w1, *w3, *w2;
   const uint8_t *s1, *s3, *s2;
+  const int32_t *slot;    // [E] logical -> physical expert slot, or NULL
+  int n_slots;            // physical slots when slot is given
   void *h;                // [R][d_ff] hidden (bf16, or f32 for f32 weights)
   float *y_perm;          // [R][d] f32
   int n, k;               // tokens and experts per token

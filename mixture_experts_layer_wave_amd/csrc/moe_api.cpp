@@ -77,6 +77,7 @@ int check_weights(const moe_shape *s, int act, const moe_expert_weights *w) {
   const int st = check_dtypes(s, act, w->dtype);
   if (st != MOE_OK) return st;
   if (!w->w1 || !w->w3 || !w->w2) return MOE_ERR_NULL;
+  if (w->slot && w->n_slots < 1) return MOE_ERR_SHAPE;
   if (w->dtype == MOE_MXFP4 && (!w->s1 || !w->s3 || !w->s2)) return MOE_ERR_NULL;
   if (w->dtype != MOE_F32 && (!aligned16(w->w1) || !aligned16(w->w3) || !aligned16(w->w2)))
     return MOE_ERR_ALIGN;
@@ -104,6 +105,8 @@ moe::FfnArgs ffn_args(const moe_shape *s, const void *a, const int32_t *perm,
   f.s1 = w->s1;
   f.s3 = w->s3;
   f.s2 = w->s2;
+  f.slot = w->slot;
+  f.n_slots = w->slot ? w->n_slots : s->E;
   f.h = h;
   f.y_perm = yp;
   f.n = s->n;
@@ -193,6 +196,15 @@ int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
+}
+
+int moe_active_experts(const moe_shape *s, const int32_t *counts, int32_t *active,
+                       int32_t *n_active, void *stream) {
+  const int st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!counts || !active || !n_active) return MOE_ERR_NULL;
+  return hip_status(
+      moe::launch_active_experts(counts, s->E, active, n_active, (hipStream_t)stream));
 }
 
 int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act, const int32_t *offsets,

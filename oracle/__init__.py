@@ -25,4 +25,6 @@ from .moe_oracle import (  # noqa: F401
     forward,
     dispatch,
     aux_loss,
+    active_experts,
+    resolve_slots,
 )

@@ -24,6 +24,9 @@ Sources, cited by page title and section:
     check": the equations for P_i, f_i and the auxiliary loss.
 * [FA] "Why FlashAttention is So Fast", section "A fused kernel, and an
   overflow problem": safe softmax subtracts the row maximum before exp.
+* [FT] minseoc03.com feed, review of the FreeToken paper: the GPU-side
+  bookkeeping of an expert cache (deduplicated expert sets, logical ids
+  rewritten to physical slots).
 * [MX] minseoc03.com feed, note "What is MXFP4?": 4-bit floats in blocks of
   32 that share one scale.  The bit layout (e2m1 element, e8m0 scale) is not
   on the pages; it is read from the OCP Microscaling Formats v1.0
@@ -325,3 +328,31 @@ def aux_loss(p: np.ndarray, idx: np.ndarray, alpha: float = 1.0) -> dict:
     top1 = np.asarray(idx)[:, 0]
     f = np.bincount(top1, minlength=E).astype(np.float64) / n
     return {"P": P, "f": f, "loss": alpha * E * float(np.sum(f * P))}
+
+
+def active_experts(idx: np.ndarray, E: int) -> np.ndarray:
+    """The distinct experts a batch is routed to, ascending.
+
+    [FT] minseoc03.com feed, review of FreeToken, sections "Decode: Exploit
+    Expert Locality" and "Dynamic Scheduling Without Giving Up CUDA Graphs":
+    the experts a batch needs are the deduplicated set of its routing
+    choices.  Written as a set over the (token, slot) choices.
+    """
+    seen = set(int(e) for e in np.asarray(idx).reshape(-1) if 0 <= int(e) < E)
+    return np.array(sorted(seen), dtype=np.int32)
+
+
+def resolve_slots(phys: dict, slot: np.ndarray) -> dict:
+    """Logical expert weights from physical slots: expert e's matrices are
+    those of slot[e].
+
+    [FT] same review, section "Dynamic Scheduling Without Giving Up CUDA
+    Graphs": logical expert ids are rewritten to physical cache slots.  The
+    mapping is a plain gather of the stored operands (every array whose
+    first axis is the slot axis); nothing is decoded or recomputed.
+    """
+    out = dict(phys)
+    for key in ("w1", "w3", "w2", "s1", "s3", "s2"):
+        if phys.get(key) is not None:
+            out[key] = np.asarray(phys[key])[np.asarray(slot)]
+    return out

@@ -122,3 +122,21 @@ def test_router_stats_errors_before_launch():
     assert B.lib.moe_router_stats(sp, fake, fake, 1.0, fake, fake, fake, None, need, None) == -5
     assert B.lib.moe_router_stats(sp, fake, fake, 1.0, fake, fake, fake, fake, need - 1, None) == -5
     assert B.lib.moe_router_stats(sp, fake, fake, 1.0, fake, fake, fake, fake + 4, need, None) == -4
+
+
+def test_slots_and_active_experts_errors_before_launch():
+    import ctypes
+
+    from mixture_experts_layer_wave_amd import binding as B
+
+    shape = (16, 64, 8, 2, 64)
+    sp = ctypes.byref(B._shape(shape))
+    fake = 1 << 20  # never dereferenced: every check below fails before a launch
+    assert B.lib.moe_active_experts(None, fake, fake, fake, None) == -1
+    assert B.lib.moe_active_experts(sp, None, fake, fake, None) == -1
+    assert B.lib.moe_active_experts(sp, fake, fake, None, None) == -1
+    assert B.lib.moe_active_experts(ctypes.byref(B._shape((0, 64, 8, 2, 64))), fake, fake, fake, None) == -2
+    # a slot table needs at least one physical slot
+    w = B.ExpertWeights(1, fake, fake, fake, None, None, None, fake, 0)
+    y = fake
+    assert B.lib.moe_expert_down(sp, fake, fake, ctypes.byref(w), y, None) == -2

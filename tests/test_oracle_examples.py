@@ -122,3 +122,34 @@ def test_aux_loss_tables():
     assert abs(rr["loss"] - 1.0) < 1e-12
     assert abs(oracle.aux_loss(pb, oracle.topk_select(np.log(pb), 1), alpha=ex["alpha"])["loss"]
                - ex["terms_added"][1]) < 1e-15
+
+
+def test_active_experts_on_the_page_dispatch_example():
+    """[MoE] forward-pass example: argmax experts (2, 1, 4, 2, 1, 2) use
+    experts 1, 2 and 4; expert 3 gets no tokens."""
+    am = np.array(GOLD["dispatch_six_tokens"]["argmax_expert_1based"]) - 1
+    assert oracle.active_experts(am.reshape(-1, 1), 4).tolist() == [0, 1, 3]
+
+
+def test_active_experts_is_the_nonempty_piles():
+    """Brute force: the deduplicated choices are the experts whose pile (built
+    by the oracle's pile scan) is non-empty, for random and degenerate inputs."""
+    rng = np.random.default_rng(5)
+    for E, shape in ((8, (40, 2)), (1, (9, 1)), (130, (3, 4)), (6, (50, 6))):
+        idx = rng.integers(0, E, size=shape)
+        want = np.nonzero(oracle.dispatch(idx, E)["counts"] > 0)[0]
+        assert np.array_equal(oracle.active_experts(idx, E), want)
+
+
+def test_resolve_slots_is_a_gather():
+    """Slots given by a permutation bring each expert's stored rows back;
+    the identity table changes nothing."""
+    rng = np.random.default_rng(6)
+    E = 5
+    w = rng.standard_normal((E, 3, 4))
+    same = oracle.resolve_slots({"w1": w, "w3": None, "w2": None}, np.arange(E))
+    assert np.array_equal(same["w1"], w)
+    pos = rng.permutation(E + 2)[:E]
+    phys2 = np.zeros((E + 2, 3, 4))
+    phys2[pos] = w
+    assert np.array_equal(oracle.resolve_slots({"w1": phys2}, pos)["w1"], w)
