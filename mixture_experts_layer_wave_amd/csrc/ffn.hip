@@ -335,36 +335,66 @@ bool big_ok(const FfnArgs &a, size_t a_bytes, int N, int K) {
 }
 
 // Block-tile choice for the large-tile kernel.  Pile sizes live on the
-// device, so the host estimates them: R rows over min(E, R) piles, each pile
-// at most its mean plus two binomial standard deviations (uniform routing).
-// A candidate's cost is the number of rounds of blocks over the 256 CUs
-// times the bytes one block loads per K step times the K steps: the kernel
-// is bound by loading its tiles, and a round lasts as long as its slowest
-// block.
+// device, so the host estimates the row tiles: R rows over min(E, R) piles,
+// each pile ~ Normal(mean, binomial variance) for uniform routing, and the
+// expected ceil(m / bm) of a pile is sum_j P(m > j bm).  A candidate's cost
+// is the number of rounds of blocks over the 256 CUs times the K steps of a
+// block times the bytes one block loads per step (the kernel is bound by
+// loading its tiles; a round lasts as long as its slowest block), plus a
+// fixed cost per round (launch to first step, epilogue) and, when K is
+// split, the traffic of the partial sums.  Cost units: one step of a
+// 256 x 256 tile (64 KB) is 512 units, about 1.6 us.
 struct TileChoice {
-  int bm, bnb;
+  int bm, bnb, splits;
 };
+
+double expected_row_tiles(const FfnArgs &a, int bm) {
+  const int piles = a.E < a.R ? a.E : a.R;
+  const double avg = (double)a.R / piles;
+  const double sd = sqrt(avg * (1.0 - 1.0 / a.E));
+  double t = 0.0;
+  for (int j = 0; j * (double)bm < a.R; ++j) {
+    const double edge = j * (double)bm + 0.5;  // P(m > j bm) for integer m
+    t += sd > 0 ? 0.5 * erfc((edge - avg) / (sd * sqrt(2.0))) : (avg > j * (double)bm ? 1.0 : 0.0);
+  }
+  return piles * t;
+}
 
 TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_cand) {
   const int N = up ? a.d_ff : a.d, K = up ? a.d : a.d_ff;
-  const int piles = a.E < a.R ? a.E : a.R;
-  const double avg = (double)a.R / piles;
-  const double big = avg + 2.0 * sqrt(avg * (1.0 - 1.0 / a.E));
   const long long nk = (K + 63) / 64;
+  constexpr double kUnitsPerRound = 1500.0;   // ~5 us of per-block fixed cost
+  constexpr double kUnitsPerByte = 312.0 / 6.0e6;  // partial sums at ~6 TB/s
   TileChoice best = cand[0];
   double best_cost = 0;
   for (int i = 0; i < n_cand; ++i) {
+    const int S = cand[i].splits < 1 ? 1 : cand[i].splits;
+    if (S > 1 && (up || !a.split_ok || nk < 2 * S)) continue;
+    if (S > 1 && (double)S * a.R * N * 4 >= 2147483647.0) continue;
     const int cols = up ? cand[i].bnb / 2 : cand[i].bnb;
-    const long long mt = (long long)piles * (long long)ceil(fmin(big, (double)a.R) / cand[i].bm);
+    // (a fraction of a tile below 0.02 is the normal tail, not a tile)
+    const double mt = ceil(expected_row_tiles(a, cand[i].bm) - 0.02);
     const long long nt = (N + cols - 1) / cols;
-    const long long rounds = (mt * nt + 255) / 256;
-    const double cost = (double)rounds * nk * (cand[i].bm + cand[i].bnb);
+    const long long rounds = ((long long)mt * nt * S + 255) / 256;
+    double cost = (double)rounds * ((nk + S - 1) / S) * (cand[i].bm + cand[i].bnb) +
+                  rounds * kUnitsPerRound;
+    if (S > 1) cost += (2.0 * S - 1.0) * a.R * (double)N * 4.0 * kUnitsPerByte;
     if (i == 0 || cost < best_cost) {
       best = cand[i];
       best_cost = cost;
     }
   }
   return best;
+}
+
+// The down pass's block tile and K split (the same answer for the up pass,
+// which clears the split counters, and the down pass).
+TileChoice down_tile(const FfnArgs &a) {
+  static const TileChoice cand_bf16[] = {{256, 256, 1}, {320, 256, 1}, {256, 128, 1}, {128, 128, 1},
+                                         {256, 256, 2}, {256, 256, 3}, {256, 256, 4}};
+  static const TileChoice cand_mx[] = {{256, 256, 1}, {256, 128, 1}, {128, 128, 1},
+                                       {256, 256, 2}, {256, 256, 3}, {256, 256, 4}};
+  return a.w_dtype == 2 ? choose_tile(a, false, cand_mx, 6) : choose_tile(a, false, cand_bf16, 7);
 }
 
 BigGemmParams big_params(const FfnArgs &a, bool up) {
@@ -407,6 +437,13 @@ bool use_decode(const FfnArgs &a) {
   return a.w_dtype == 2 && a.R <= kDecodeMaxRows && decode_ffn_fits(a.d, a.d_ff, a.E);
 }
 
+int down_split_factor(const FfnArgs &a) {
+  if (!a.split_ok || a.R == 0 || use_decode(a) || a.d % 4 ||
+      !big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff))
+    return 1;
+  return down_tile(a).splits;
+}
+
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
   if (use_decode(a)) return launch_decode_up(a, st);
@@ -419,10 +456,11 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   }
   const size_t a_bytes = (size_t)(a.perm ? a.n : a.R) * a.d * 2;
   if (big_ok(a, a_bytes, a.d_ff, a.d)) {
-    static const TileChoice cand[2] = {{256, 256}, {320, 256}};
+    static const TileChoice cand[2] = {{256, 256, 1}, {320, 256, 1}};
     const TileChoice t = choose_tile(a, true, cand, a.w_dtype == 2 ? 1 : 2);
     BigGemmParams p = big_params(a, true);
     p.n_tiles = (a.d_ff + t.bnb / 2 - 1) / (t.bnb / 2);
+
     return launch_big_gemm(p, true, a.w_dtype == 2, a.perm != nullptr, false, t.bm, t.bnb, st);
   }
   GemmParams up{};
@@ -457,13 +495,23 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
     return hipGetLastError();
   }
   if (big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff)) {
-    static const TileChoice cand_bf16[4] = {{256, 256}, {320, 256}, {256, 128}, {128, 128}};
-    static const TileChoice cand_mx[3] = {{256, 256}, {256, 128}, {128, 128}};
-    const TileChoice t = a.w_dtype == 2 ? choose_tile(a, false, cand_mx, 3)
-                                        : choose_tile(a, false, cand_bf16, 4);
+    const TileChoice t = down_tile(a);
     const int bm = t.bm, bnb = t.bnb;
     BigGemmParams p = big_params(a, false);
     p.n_tiles = (a.d + bnb - 1) / bnb;
+    if (t.splits > 1 && a.split_part && down_split_factor(a) > 1) {
+      p.splits = t.splits;
+      p.ksplit = ((a.d_ff + 64 * t.splits - 1) / (64 * t.splits)) * 64;
+      p.part = a.split_part;
+      hipError_t err = launch_big_gemm(p, false, a.w_dtype == 2, false, false, bm, bnb, st);
+      if (err != hipSuccess) return err;
+      if (a.comb_y) {
+        if (fused) *fused = true;
+        return launch_splitk_combine(a.split_part, t.splits, a.R, a.comb_inv, a.comb_w, a.n, a.k,
+                                     a.d, a.comb_y, a.comb_bf16, st);
+      }
+      return launch_splitk_sum(a.split_part, t.splits, a.R, a.d, a.y_perm, st);
+    }
     const bool fuse = a.fuse_y != nullptr && a.k == 1;
     if (fuse) {
       p.out = a.fuse_y;

@@ -105,11 +105,12 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   constexpr int NST = MX ? 2 : MOE_BF16_NST;
   using T = Tile<BM, BNB, BK>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_e, s_row0, s_rows, s_nt;
+  __shared__ int s_e, s_row0, s_rows, s_nt, s_item;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases
   const int N = p.N, K = p.K;
+  const int S = UP ? 1 : (p.splits > 1 ? p.splits : 1);
 
   // ---- block -> tile ------------------------------------------------------
   if (wave == 0) {
@@ -119,15 +120,17 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
     for (int x = eb; x < ee; ++x) local += (p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM;
     const int incl = wave_incl_scan(local);
     const int excl = incl - local;
-    const int total = __builtin_amdgcn_readlane(incl, MOE_WAVE - 1) * p.n_tiles;  // tiles of work
+    // Work items: tiles x splits, the splits of a tile adjacent.
+    const int total = __builtin_amdgcn_readlane(incl, MOE_WAVE - 1) * p.n_tiles * S;
     const int b = blockIdx.x;
     if (lane == 0 && b >= total) s_e = -1;
     if (b < total) {
-      // XCD-contiguous remap of the ordered tile list.
+      // XCD-contiguous remap of the ordered work list.
       const int xcd = b & 7, slot = b >> 3;
       int base = 0;
       for (int x = 0; x < xcd; ++x) base += (total - x + 7) >> 3;
-      const int L = base + slot;
+      const int L = (base + slot) / S;
+      if (lane == 0) s_item = base + slot;
       const int lo = excl * p.n_tiles, hi = incl * p.n_tiles;
       if (L >= lo && L < hi) {
         int acc = lo;
@@ -153,6 +156,10 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   if (e < 0) return;
   const int row0 = s_row0, rows = s_rows;
   const int n0 = s_nt * (UP ? BNB / 2 : BNB);
+  const int split = s_item % S;
+  // K range of this block: [kbeg, kend), a whole multiple of BK but the end.
+  const int kbeg = S > 1 ? split * p.ksplit : 0;
+  const int kend = S > 1 ? min(K, kbeg + p.ksplit) : K;
 
   // ---- per-lane DMA offsets -----------------------------------------------
   // Run j of wave w fills LDS chunks q = (4 j + w) * 64 + lane, i.e. row
@@ -218,11 +225,11 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   u32x4 mq[2][MX ? T::MX_UNITS : 1];
   uint32_t ms[2][MX ? T::MX_UNITS : 1];
   auto load_b = [&](int kt, u32x4 *q, uint32_t *sv) {
-    const int k0 = kt * BK;
+    const int k0 = kbeg + kt * BK;
 #pragma unroll
     for (int i = 0; i < T::MX_UNITS; ++i) {
       const int half = (tid + kNT * i) % (BK / 32);
-      const uint32_t pen = (k0 + half * 32 < K) ? 0u : kOOB;
+      const uint32_t pen = (k0 + half * 32 < kend) ? 0u : kOOB;
       // Units u >= (BNB / 2) * (BK / 32) (a multiple of 64) are W3 rows, so
       // the choice follows the wave index (uniform: one buffer resource).
       static_assert((BNB / 2) * (BK / 32) % 64 == 0, "W1/W3 split at a wave boundary");
@@ -239,8 +246,8 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   // (a compile-time index: the K loop is unrolled by two).
   auto issue = [&](int kt, int stage, auto slc) {
     constexpr int SL = decltype(slc)::value;
-    const int k0 = kt * BK;
-    const uint32_t kpen = (k0 + c * 8 < K) ? 0u : kOOB;
+    const int k0 = kbeg + kt * BK;
+    const uint32_t kpen = (k0 + c * 8 < kend) ? 0u : kOOB;
     const uint32_t k0b = (uint32_t)k0 * 2u;
     uint8_t *sa = smem + stage * T::STAGE;
 #pragma unroll
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
     }
   };
 
-  const int nk = (K + BK - 1) / BK;
+  const int nk = (kend - kbeg + BK - 1) / BK;
   // Vector memory operations issued after a step's copies: NST - 2 later
   // steps of copies, or (MXFP4) the register loads of the following step.
   constexpr int NAFTER = MX ? 2 * T::MX_UNITS : (NST - 2) * NV;
@@ -413,6 +420,29 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   // element i of lane l is pile row l % 32 of the 32-row group and output
   // column (i/4)*8 + (l/32)*4 + i%4 of the 32-column group: every lane holds
   // runs of four consecutive columns of one row.
+  if constexpr (!UP) {
+    if (S > 1) {
+      // Split K: this block's partial sums go to plane `split` (16-B stores of
+      // four columns); a later kernel adds the planes in split order.
+      float *pl = p.part + (size_t)split * p.R * N;
+#pragma unroll
+      for (int tm = 0; tm < T::TM; ++tm) {
+        const int r = wm * T::WM + tm * 32 + lr;
+#pragma unroll
+        for (int tn = 0; tn < T::TN; ++tn)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = n0 + wn * T::WN + tn * 32 + g * 8 + lg * 4;
+            if (r < rows && col < N) {
+              const f32x4 v = {acc[tm][tn][g * 4], acc[tm][tn][g * 4 + 1], acc[tm][tn][g * 4 + 2],
+                               acc[tm][tn][g * 4 + 3]};
+              *(f32x4 *)(pl + (size_t)(row0 + r) * N + col) = v;
+            }
+          }
+      }
+      return;
+    }
+  }
   if constexpr (UP || FUSE) {
     // bf16 output staged through LDS (8-B writes of four columns) so that
     // global stores are 16-B pieces of rows.
@@ -512,7 +542,7 @@ hipError_t launch_one(const BigGemmParams &p, int blocks, hipStream_t st) {
 hipError_t launch_big_gemm(const BigGemmParams &p, bool up, bool mx, bool gather, bool fuse,
                            int bm, int bnb, hipStream_t st) {
   const int m_tiles = (p.R + bm - 1) / bm + (p.E < p.R ? p.E : p.R);
-  const int blocks = m_tiles * p.n_tiles;
+  const int blocks = m_tiles * p.n_tiles * (up ? 1 : (p.splits > 1 ? p.splits : 1));
 #define MOE_BIG(U, M, G, F, A, B)                                             \
   if (up == U && mx == M && gather == G && fuse == F && bm == A && bnb == B) \
     return launch_one<U, M, G, F, A, B>(p, blocks, st);

@@ -60,7 +60,21 @@ struct FfnArgs {
   void *fuse_y;
   const int32_t *fuse_perm;
   const float *fuse_w;
+  // Optional split-K workspace of the down pass: partial planes
+  // (down_split_factor(a) x R x d f32).  When K is split the down pass also
+  // adds the planes: into y_perm, or, given comb_y, straight into the layer
+  // output y[t] = sum_j comb_w[t][j] * (sum of planes)[comb_inv[t][j]].
+  bool split_ok;         // the caller provides split_part
+  float *split_part;
+  void *comb_y;
+  const int32_t *comb_inv;
+  const float *comb_w;
+  bool comb_bf16;
 };
+// K splits the down pass takes for these arguments (1 = none); with
+// split_ok set it tells the workspace layout how many partial planes
+// (splits x R x d f32) to reserve.
+int down_split_factor(const FfnArgs &a);
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st);    // A -> h
 // h -> y_perm, or straight into fuse_y; *fused (may be NULL) tells which.
 hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
@@ -74,6 +88,12 @@ hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st);
 hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st);
 
 // ---- combine --------------------------------------------------------------
+// Split-K: y = combine of (sum of the S planes part[s][R][d]); or y_perm =
+// that sum.  d % 4 == 0.
+hipError_t launch_splitk_combine(const float *part, int S, int R, const int32_t *inv,
+                                 const float *w, int n, int k, int d, void *y, bool out_bf16,
+                                 hipStream_t st);
+hipError_t launch_splitk_sum(const float *part, int S, int R, int d, float *yp, hipStream_t st);
 hipError_t launch_combine(const float *y_perm, const int32_t *inv, const float *w,
                           int n, int k, int d, void *y, bool out_bf16, hipStream_t st);
 

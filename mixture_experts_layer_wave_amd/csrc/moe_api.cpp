@@ -16,8 +16,23 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct WsLayout {
-  size_t logits, idx, w, counts, offsets, perm, inv, h, yp, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, h, yp, part, total;
+  int splits;
 };
+
+// The FFN arguments that decide kernel shapes (no pointers).
+moe::FfnArgs plan_args(const moe_shape *s, int wdt) {
+  moe::FfnArgs f{};
+  f.E = s->E;
+  f.R = s->n * s->k;
+  f.d = s->d;
+  f.d_ff = s->d_ff;
+  f.w_dtype = wdt;
+  f.n = s->n;
+  f.k = s->k;
+  f.split_ok = true;
+  return f;
+}
 
 int check_shape(const moe_shape *s) {
   if (!s) return MOE_ERR_NULL;
@@ -68,6 +83,8 @@ WsLayout layout(const moe_shape *s, int wdt) {
   L.inv = take(R * 4);
   L.h = take(R * (size_t)s->d_ff * (wdt == MOE_F32 ? 4 : 2));
   L.yp = take(R * (size_t)s->d * 4);
+  L.splits = moe::down_split_factor(plan_args(s, wdt));
+  L.part = take(L.splits > 1 ? (size_t)L.splits * R * (size_t)s->d * 4 : 0);
   L.total = o;
   return L;
 }
@@ -221,7 +238,9 @@ int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act, const int32
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
   char *base = (char *)ws;
-  const moe::FfnArgs f = ffn_args(s, x_perm, nullptr, offsets, w, base + L.h, (float *)y_perm);
+  moe::FfnArgs f = ffn_args(s, x_perm, nullptr, offsets, w, base + L.h, (float *)y_perm);
+  f.split_ok = true;
+  f.split_part = (float *)(base + L.part);
   return hip_status(moe::launch_grouped_ffn(f, (hipStream_t)stream));
 }
 
@@ -298,6 +317,12 @@ int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, cons
   bool fused = false;
   if (e == hipSuccess) {
     moe::FfnArgs f = ffn_args(s, x, perm, offsets, w, base + L.h, yp);
+    f.split_ok = true;
+    f.split_part = (float *)(base + L.part);
+    f.comb_y = y;
+    f.comb_inv = inv;
+    f.comb_w = wt;
+    f.comb_bf16 = out == MOE_BF16;
     if (s->k == 1 && out == MOE_BF16) {  // one expert per token: scale-and-scatter in the down pass
       f.fuse_y = y;
       f.fuse_perm = perm;
