@@ -116,8 +116,14 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   if (wave == 0) {
     const int per = (p.E + MOE_WAVE - 1) / MOE_WAVE;
     const int eb = lane * per, ee = min(p.E, eb + per);
+    // With one expert per lane (E <= 64) its offsets are loaded once.
+    const int o0 = per == 1 && eb < p.E ? p.offsets[eb] : 0;
+    const int o1 = per == 1 && eb < p.E ? p.offsets[eb + 1] : 0;
     int local = 0;
-    for (int x = eb; x < ee; ++x) local += (p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM;
+    if (per == 1)
+      local = (o1 - o0 + BM - 1) / BM;
+    else
+      for (int x = eb; x < ee; ++x) local += (p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM;
     const int incl = wave_incl_scan(local);
     const int excl = incl - local;
     // Work items: tiles x splits, the splits of a tile adjacent.
@@ -135,14 +141,15 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
       if (L >= lo && L < hi) {
         int acc = lo;
         for (int x = eb; x < ee; ++x) {
-          const int m = p.offsets[x + 1] - p.offsets[x];
+          const int ox = per == 1 ? o0 : p.offsets[x];
+          const int m = (per == 1 ? o1 : p.offsets[x + 1]) - ox;
           const int te = (m + BM - 1) / BM;
           if (L < acc + te * p.n_tiles) {
             const int loc = L - acc;
             const int mloc = loc % te;
             s_e = x;
             s_nt = loc / te;
-            s_row0 = p.offsets[x] + mloc * BM;
+            s_row0 = ox + mloc * BM;
             s_rows = min(BM, m - mloc * BM);
             break;
           }
@@ -171,16 +178,19 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, p.a_bytes);
   // Valid offsets are < 2^31 (checked on the host); an invalid row carries
   // bit 31 and the K tail ORs it in, so such lanes read zeros.
+  // The pile-row -> token loads are issued together (row index clamped into
+  // the tile, so every load is in bounds) and awaited once.
   uint32_t a_off[T::A_RUNS];
+  int a_src[T::A_RUNS];
 #pragma unroll
   for (int j = 0; j < T::A_RUNS; ++j) {
     const int r = (kNW * j + wave) * T::RPR + lane / T::CPR;
-    uint32_t off = kOOB;
-    if (r < rows) {
-      const int src = GATHER ? p.perm[row0 + r] : row0 + r;
-      off = ((uint32_t)src * (uint32_t)K + (uint32_t)c * 8u) * 2u;
-    }
-    a_off[j] = off;
+    a_src[j] = GATHER ? p.perm[row0 + min(r, rows - 1)] : row0 + r;
+  }
+#pragma unroll
+  for (int j = 0; j < T::A_RUNS; ++j) {
+    const int r = (kNW * j + wave) * T::RPR + lane / T::CPR;
+    a_off[j] = r < rows ? ((uint32_t)a_src[j] * (uint32_t)K + (uint32_t)c * 8u) * 2u : kOOB;
   }
   const int pe = phys_slot(p.slot, p.n_slots, e);  // physical weight slot
   const size_t mat_elems = (size_t)N * K;
