@@ -16,6 +16,12 @@ from .moe_oracle import (  # noqa: F401
     decode_e2m1,
     decode_e8m0,
     decode_mxfp4,
+    decode_e4m3,
+    round_e4m3,
+    encode_e4m3,
+    quantize_mxfp8,
+    decode_mxfp8,
+    mxfp8_round,
     decode_matrix,
     router_logits,
     softmax_rows,

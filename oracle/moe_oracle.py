@@ -31,6 +31,17 @@ Sources, cited by page title and section:
   32 that share one scale.  The bit layout (e2m1 element, e8m0 scale) is not
   on the pages; it is read from the OCP Microscaling Formats v1.0
   specification.
+* [VL] minseoc03.com feed, review of the vLLM paper, section "What's Next":
+  quantised weights are usually expanded back to a wider type before the
+  arithmetic, and that expansion eats the gain.  The W4A8 mode below is the
+  alternative: activations are quantised too (to MXFP8) so that the matrix
+  unit takes both operands in their narrow form.  The MXFP8 element (E4M3)
+  and the rule that picks a block's shared scale are not on the pages; they
+  are read from OCP Microscaling Formats v1.0 (the E4M3 element of the OCP
+  8-bit floating point format: bias 7, no infinities, S.1111.111 is NaN,
+  largest magnitude 448; shared exponent = floor(log2(block amax)) minus the
+  element's largest exponent, 8; elements rounded to nearest even and
+  clamped to +-448).
 
 Readings where the pages are silent (each listed in the design notes):
 
@@ -127,6 +138,96 @@ def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return blocks.reshape(vals.shape)
 
 
+def decode_e4m3(code: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 element codes (0..255) -> float64, from the format's definition.
+
+    Bit 7 is the sign, bits 6..3 the exponent (bias 7), bits 2..0 the
+    mantissa.  Exponent field 0 is subnormal: m/8 * 2^-6.  Otherwise
+    2^(e-7) * (1 + m/8).  Exponent 15 with mantissa 7 is NaN; there are no
+    infinities, so the largest magnitude is 1.75 * 2^8 = 448.  [VL] (OCP).
+    """
+    code = np.asarray(code).astype(np.int64)
+    sign = np.where((code >> 7) & 1, -1.0, 1.0)
+    e = (code >> 3) & 15
+    m = code & 7
+    mag = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where((code & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+E4M3_MAX = 448.0
+E4M3_EMAX = 8  # exponent of the largest power of two the element reaches
+
+
+def _floor_log2(a: np.ndarray) -> np.ndarray:
+    """floor(log2 a) for a > 0, exactly (frexp: a = f 2^e with f in [0.5, 1))."""
+    return np.frexp(a)[1].astype(np.int64) - 1
+
+
+def round_e4m3(a: np.ndarray) -> np.ndarray:
+    """Non-negative float64 -> the nearest E4M3 magnitude, ties to even.
+
+    In the binade [2^e, 2^(e+1)) (e >= -6) E4M3 has 8 steps of 2^(e-3);
+    below 2^-6 the subnormal step is 2^-9.  Rounding a / step to the
+    nearest integer with ties to even (numpy's round) and scaling back
+    gives the nearest value; a carry into the next binade lands on its
+    first value, which is exact.  Values above 448 saturate to 448.  [VL]
+    """
+    a = np.asarray(a, dtype=np.float64)
+    e = np.where(a > 0, _floor_log2(np.where(a > 0, a, 1.0)), -6)
+    step = np.ldexp(1.0, np.maximum(e, -6) - 3)
+    return np.minimum(np.round(a / step) * step, E4M3_MAX)
+
+
+def encode_e4m3(v: np.ndarray) -> np.ndarray:
+    """Code of values that are exactly E4M3 magnitudes with a sign (float64,
+    |v| <= 448); the sign bit is the sign bit of v, so -0.0 gives 0x80."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    sub = a < 2.0 ** -6
+    e = np.where(sub, 0, _floor_log2(np.where(sub, 1.0, a)) + 7)
+    m = np.where(sub, a / 2.0 ** -9, (a / np.ldexp(1.0, np.maximum(e, 1) - 7) - 1.0) * 8)
+    code = (e.astype(np.int64) << 3) | np.rint(m).astype(np.int64)
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_mxfp8(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP8 encoding of float64 rows: blocks of 32 consecutive values along
+    the last axis share one E8M0 scale 2^X, each element is an E4M3 code.
+
+    X = floor(log2 amax) - 8 with amax the block's largest magnitude (the
+    block's largest element lands in [256, 512) * 2^X, and values above
+    448 * 2^X are clamped); an all-zero block takes the smallest scale,
+    code 0.  X is clamped to the E8M0 range [-127, 127].  Each element is
+    v / 2^X (exact: a power of two) rounded to the nearest E4M3 value, ties
+    to even.  Returns (codes uint8 [..., K], scales uint8 [..., K/32]).  [VL]
+    """
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    if K % 32:
+        raise ValueError("the last axis must be a multiple of 32")
+    blocks = v.reshape(*v.shape[:-1], K // 32, 32)
+    amax = np.abs(blocks).max(axis=-1)
+    X = np.where(amax > 0, _floor_log2(np.where(amax > 0, amax, 1.0)) - E4M3_EMAX, -127)
+    X = np.clip(X, -127, 127)
+    scaled = blocks / np.ldexp(1.0, X)[..., None]
+    q = np.copysign(round_e4m3(np.abs(scaled)), scaled)
+    codes = encode_e4m3(q).reshape(v.shape)
+    return codes, (X + 127).astype(np.uint8)
+
+
+def decode_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP8 rows -> float64: e4m3(code) * 2^(scale - 127) per 32-block."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    K = codes.shape[-1]
+    vals = decode_e4m3(codes).reshape(*codes.shape[:-1], K // 32, 32)
+    return (vals * decode_e8m0(scales)[..., None]).reshape(codes.shape)
+
+
+def mxfp8_round(v: np.ndarray) -> np.ndarray:
+    """The value v takes after MXFP8 encoding and decoding."""
+    return decode_mxfp8(*quantize_mxfp8(v))
+
+
 def decode_matrix(raw: np.ndarray, dtype: str, scales: np.ndarray | None = None) -> np.ndarray:
     """Decode one stored operand ('bf16', 'f32' or 'mxfp4') to float64."""
     if dtype == "bf16":
@@ -210,16 +311,28 @@ def _silu(g: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g))
 
 
-def swiglu_expert(x: np.ndarray, w1_t: np.ndarray, w3_t: np.ndarray, w2_t: np.ndarray) -> np.ndarray:
+def swiglu_expert(x: np.ndarray, w1_t: np.ndarray, w3_t: np.ndarray, w2_t: np.ndarray,
+                  act_quant: str | None = None) -> np.ndarray:
     """One expert's FFN on the rows of ``x`` (n x d -> n x d).
 
     Up-projection to d_ff through W1 (gate) and W3 (value), the SiLU-gated
     product, and the down-projection W2 back to d.  Stored matrices are the
     transposes: ``w1_t``/``w3_t`` are d_ff x d, ``w2_t`` is d x d_ff.
+
+    ``act_quant='mxfp8'`` (the W4A8 mode, [VL]): each projection's input
+    rows -- x before the up-projection, the hidden h before the
+    down-projection -- are replaced by their MXFP8 values, blocks of 32
+    along the row (the contraction axis).
     """
+    if act_quant not in (None, "mxfp8"):
+        raise ValueError(f"unknown act_quant {act_quant!r}")
+    if act_quant:
+        x = mxfp8_round(x)
     g = x @ w1_t.T
     u = x @ w3_t.T
     h = _silu(g) * u
+    if act_quant:
+        h = mxfp8_round(h)
     return h @ w2_t.T
 
 
@@ -241,7 +354,8 @@ def _expert_mats(layer: dict, e: int):
     return w1, w3, w2
 
 
-def forward(layer: dict, k: int, renorm: bool | None = None, rows=None) -> dict:
+def forward(layer: dict, k: int, renorm: bool | None = None, rows=None,
+            act_quant: str | None = None) -> dict:
     """The MoE layer forward on (a subset of) the tokens, in float64.
 
     ``layer`` holds the raw stored arrays: 'x', 'x_dtype' ('bf16'|'f32'),
@@ -257,7 +371,8 @@ def forward(layer: dict, k: int, renorm: bool | None = None, rows=None) -> dict:
          was chosen for t, else 0.
     The FFN treats tokens independently ([MoE] dense-model section), so the
     result for a subset ``rows`` of tokens equals those rows of the full
-    result.
+    result.  ``act_quant='mxfp8'`` runs every expert in the W4A8 mode of
+    :func:`swiglu_expert`; the router still sees the unquantised x.
     """
     if renorm is None:
         renorm = k > 1
@@ -278,7 +393,7 @@ def forward(layer: dict, k: int, renorm: bool | None = None, rows=None) -> dict:
     y = np.zeros_like(x)
     for e in range(E):
         w1, w3, w2 = _expert_mats(layer, e)
-        y += mask[:, e:e + 1] * swiglu_expert(x, w1, w3, w2)
+        y += mask[:, e:e + 1] * swiglu_expert(x, w1, w3, w2, act_quant)
     return {"y": y, "idx": idx, "w": w, "p": p, "z": z}
 
 
