@@ -1,6 +1,6 @@
 """Benchmark of the sparse MoE layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--act-quant mxfp8]
 
 A step is one moe_forward (router + top-k, dispatch, grouped expert FFN up
 and down, combine) over one batch of synthetic tokens already resident in
@@ -17,6 +17,10 @@ Printed (one JSON line on stdout): tokens/s of the layer, plus
                   counter summary under profiles/,
   cpu_baseline -- the float64 CPU oracle on a bounded token sample of the
                   same workload, on this host's cores.
+With --act-quant mxfp8 (MXFP4 workloads) the layer runs in the W4A8 mode:
+the experts' input and hidden are MXFP8 and both projections run on the
+scaled MFMA; the prefill roofline is then against the dense FP8 peak (the
+FP8 x FP4 MFMA issues at the FP8 rate), and the oracle runs the same mode.
 """
 
 from __future__ import annotations
@@ -34,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + % HBM peak (decode) / % MFMA peak (prefill)"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -41,7 +46,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_work(L, counts):
+def algorithmic_work(L, counts, act_quant=None):
     """FLOPs of the routed layer and HBM bytes of what it must read/write."""
     n, d, E, k, f = L["n"], L["d"], L["E"], L["k"], L["d_ff"]
     R = n * k
@@ -54,12 +59,15 @@ def algorithmic_work(L, counts):
         per_expert = 3 * d * f * (2 if L["w_dtype"] == "bf16" else 4)
     active = int((counts > 0).sum())
     bytes_ = E * d * act_b + 2 * n * d * act_b + active * per_expert
-    up_bytes = active * (2 * d * f * (per_expert / (3 * d * f))) + n * d * act_b + R * f * 2
+    if act_quant:  # MXFP8 rows in and out: a byte per value plus a scale per 32
+        up_bytes = active * (2 * d * f * (per_expert / (3 * d * f))) + (n * d + R * f) * 33 / 32
+    else:
+        up_bytes = active * (2 * d * f * (per_expert / (3 * d * f))) + n * d * act_b + R * f * 2
     return {"flops": flops, "flops_up": flops_up, "bytes": bytes_, "up_bytes": up_bytes,
             "active_experts": active}
 
 
-def cpu_baseline(L, budget_s=15.0, threads=16):
+def cpu_baseline(L, budget_s=15.0, threads=16, act_quant=None):
     """Time the float64 oracle on a token sample: a probe on 64 tokens sizes
     the sample to about budget_s seconds; a sample that is the whole batch is
     repeated until about 10 s of work have been timed."""
@@ -69,20 +77,21 @@ def cpu_baseline(L, budget_s=15.0, threads=16):
     with threadpool_limits(limits=threads):
         m = min(L["n"], 64)
         t0 = time.perf_counter()
-        oracle.forward(L, L["k"], L["renorm"], rows=np.arange(m))
+        oracle.forward(L, L["k"], L["renorm"], rows=np.arange(m), act_quant=act_quant)
         dt = time.perf_counter() - t0
         if dt < budget_s / 3 and m < L["n"]:
             m = int(min(L["n"], max(m, m * budget_s / max(dt, 1e-3))))
         runs, total = 0, 0.0
         while runs == 0 or total < 10.0:
             t0 = time.perf_counter()
-            oracle.forward(L, L["k"], L["renorm"], rows=np.arange(m))
+            oracle.forward(L, L["k"], L["renorm"], rows=np.arange(m), act_quant=act_quant)
             total += time.perf_counter() - t0
             runs += 1
         used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": m * runs / total, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
             "sample": f"float64 dense-then-masked oracle on the first {m} of {L['n']} tokens "
-                      f"(all {L['E']} experts per token), {runs} run(s), {total:.2f} s"}
+                      f"(all {L['E']} experts per token{', W4A8 mode' if act_quant else ''}), "
+                      f"{runs} run(s), {total:.2f} s"}
 
 
 def main():
@@ -93,6 +102,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--act-quant", choices=["mxfp8"], default=None,
+                    help="W4A8 mode of an MXFP4 layer (MXFP8 expert inputs and hidden)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; "
                          "run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE")
@@ -124,7 +135,11 @@ def main():
     log(f"[bench] workload {name}: generating inputs")
     L = W.make_layer(name, cache=False)
     torch.cuda.set_device(0)
-    D = DeviceLayer(L)
+    aq = args.act_quant
+    if aq and wl.wdt != "mxfp4":
+        print("--act-quant needs an MXFP4 workload", file=sys.stderr)
+        sys.exit(2)
+    D = DeviceLayer(L, act_quant=aq)
     stream = torch.cuda.current_stream()
 
     # Identical weight copies in distinct HBM buffers, rotated per step.
@@ -133,7 +148,8 @@ def main():
     for _ in range(max(0, args.copies - 1)):
         ws = {key: (None if D.w[key] is None else D.w[key].clone()) for key in D.w}
         keep.append(ws)
-        copies.append(B.ExpertWeights(D.weights.dtype, *(B._ptr(ws[key]) for key in ("w1", "w3", "w2", "s1", "s3", "s2"))))
+        copies.append(B.ExpertWeights(D.weights.dtype, *(B._ptr(ws[key]) for key in ("w1", "w3", "w2", "s1", "s3", "s2")),
+                                      None, 0, D.weights.act_quant))
 
     def step(i):
         B.moe_forward(D.shape, D.x, D.act, D.wg, D.bias, copies[i % len(copies)], D.y, D.act,
@@ -169,17 +185,24 @@ def main():
     inv = torch.empty((n, k), dtype=torch.int32, device="cuda")
     B.moe_router_topk(D.shape, D.x, D.act, D.wg, D.bias, logits, idx, tw, stream)
     B.moe_dispatch(D.shape, idx, counts, offsets, perm, inv, None, D.act, None, None, 0, stream)
-    h = torch.empty((R, D.d_ff), dtype=torch.int16 if D.wdt != "f32" else torch.float32, device="cuda")
+    a_in, a_dt = D.x, D.act
+    if aq:  # the up projection of the mode takes the MXFP8 tokens, writes an MXFP8 hidden
+        a_in = torch.empty(B.moe_mxfp8_bytes(n, D.d), dtype=torch.uint8, device="cuda")
+        B.moe_quantize_mxfp8(n, D.d, D.x, D.act, a_in, stream)
+        a_dt = aq
+        h = torch.empty(B.moe_mxfp8_bytes(R, D.d_ff), dtype=torch.uint8, device="cuda")
+    else:
+        h = torch.empty((R, D.d_ff), dtype=torch.int16 if D.wdt != "f32" else torch.float32, device="cuda")
     torch.cuda.synchronize()
-    work = algorithmic_work(L, counts.cpu().numpy())
+    work = algorithmic_work(L, counts.cpu().numpy(), aq)
 
     # Dominant kernel: the grouped up-projection, one launch per call.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.warmup):
-        B.moe_expert_up(D.shape, D.x, D.act, perm, offsets, copies[i % len(copies)], h, stream)
+        B.moe_expert_up(D.shape, a_in, a_dt, perm, offsets, copies[i % len(copies)], h, stream)
     for i, (a, b) in enumerate(evs):
         a.record(stream)
-        B.moe_expert_up(D.shape, D.x, D.act, perm, offsets, copies[i % len(copies)], h, stream)
+        B.moe_expert_up(D.shape, a_in, a_dt, perm, offsets, copies[i % len(copies)], h, stream)
         b.record(stream)
     torch.cuda.synchronize()
     up_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -189,11 +212,12 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
         achieved = work["flops_up"] / (up_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        peak = PEAK_FP8_TFLOPS if aq else PEAK_BF16_TFLOPS
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     # HBM bytes per launch of this kernel from the committed rocprofv3
     # FETCH_SIZE / WRITE_SIZE summary (null once the kernel's sources change).
-    fam = "mx_decode_kernel" if decode else "big_gemm_kernel"
+    fam = "w4a8_gemm_kernel" if aq else ("mx_decode_kernel" if decode else "big_gemm_kernel")
     traffic, src = read_traffic(name, fam)
     roof["traffic"] = traffic
     roof["traffic_source"] = src
@@ -206,7 +230,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host")
-        cpu = cpu_baseline(L)
+        cpu = cpu_baseline(L, act_quant=aq)
         log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
     value = n / (ms_per_step * 1e-3)
@@ -214,10 +238,12 @@ def main():
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": D.act if D.wdt != "mxfp4" else "bf16 (mxfp4 weights)",
+        "dtype": (D.act if D.wdt != "mxfp4" else
+                  "mxfp8 x mxfp4 (w4a8)" if aq else "bf16 (mxfp4 weights)"),
         "data": "synthetic",
         "config": {"workload": name, "n": wl.n, "d": wl.d, "E": wl.E, "k": wl.k, "d_ff": wl.d_ff,
-                   "weights": wl.wdt, "activations": wl.act, "weight_copies": len(copies),
+                   "weights": wl.wdt, "activations": wl.act, "act_quant": aq,
+                   "weight_copies": len(copies),
                    "layer_tflops": layer_tflops},
         "step_ms": pct,
         "roofline": roof,

@@ -34,10 +34,19 @@
  *   - Row-major layouts.  bf16 is stored as its 16-bit pattern.  MXFP4
  *     matrices are [rows][K/2] bytes with the even-K element in the low
  *     nibble, plus [rows][K/32] E8M0 scale bytes.
+ *   - MXFP8 matrices (rows x cols, cols % 32 == 0; the W4A8 mode below)
+ *     are one buffer: E4M3 codes [rows][cols] at offset 0, then, from
+ *     offset rows*cols rounded up to a multiple of 256, E8M0 scales
+ *     [rows][sp] with sp = cols/32 rounded up to a multiple of 4 (padding
+ *     bytes 0).  moe_mxfp8_bytes gives the size.  Encoding (OCP MX v1.0):
+ *     per 32-block, X = floor(log2 amax) - 8 (the scale code X + 127,
+ *     clamped at 0; an all-zero block has code 0); each element is v / 2^X
+ *     rounded to the nearest E4M3 value, ties to even, clamped to +-448.
  *   - Rounding: products are accumulated in float32; the expert hidden
  *     activation is rounded to bf16 (round to nearest even) before the
- *     down-projection when the weights are bf16 or MXFP4; pile outputs are
- *     kept in float32 and rounded once in the combine.
+ *     down-projection when the weights are bf16 or MXFP4 (to MXFP8 in the
+ *     W4A8 mode); pile outputs are kept in float32 and rounded once in the
+ *     combine.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -49,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -61,7 +70,7 @@ typedef enum {
   MOE_ERR_HIP = -6          /* a HIP launch failed                           */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_MXFP8 = 3 } moe_dtype;
 
 /* Layer shape.  n tokens of width d, E experts of hidden width d_ff, k
  * experts per token.  renorm: 1 = divide the k probabilities by their sum,
@@ -96,6 +105,16 @@ typedef struct {
    * n_slots >= 1 is required when slot is given. */
   const int32_t *slot;
   int32_t n_slots;
+  /* 0, or MOE_MXFP8 for the W4A8 mode (MXFP4 weights only): the input of
+   * each projection -- the token rows, then the hidden -- is encoded as
+   * MXFP8 and the products run on the scaled MFMA with both operands in
+   * their stored form.  The minseoc03.com feed's review of the vLLM paper
+   * (section "What's Next") observes that quantised weights are usually
+   * widened back before the arithmetic, which costs the speed-up; this
+   * mode widens neither operand.  The router still sees the unencoded x.
+   * Needs d and d_ff <= 7168, and d_ff*(d/32) and d*(d_ff/32) multiples of
+   * 4 (MOE_ERR_SHAPE otherwise); scale arrays 16-byte aligned. */
+  int32_t act_quant;
 } moe_expert_weights;
 
 /* ABI version of the loaded library (MOE_ABI_VERSION). */
@@ -105,8 +124,20 @@ int moe_abi_version(void);
 const char *moe_status_string(int status);
 
 /* Workspace bytes that moe_forward needs for this shape and weight dtype
- * (also enough for moe_grouped_ffn).  Returns 0 for an invalid shape. */
+ * (also enough for moe_grouped_ffn, and for MXFP4 in either mode).  Returns
+ * 0 for an invalid shape. */
 size_t moe_workspace_bytes(const moe_shape *s, int w_dtype);
+
+/* Bytes of an MXFP8 matrix of rows x cols (layout above); 0 when rows < 0
+ * or cols is not a positive multiple of 32. */
+size_t moe_mxfp8_bytes(int64_t rows, int32_t cols);
+
+/* MXFP8 encoding of x [rows][cols] (act = MOE_F32 or MOE_BF16) into the
+ * MXFP8 matrix q (moe_mxfp8_bytes(rows, cols) bytes), as described above;
+ * the encoding of a W4A8 projection's input.  x and q 16-byte aligned;
+ * cols % 32 == 0.  rows = 0 does nothing. */
+int moe_quantize_mxfp8(int64_t rows, int32_t cols, const void *x, int act, void *q,
+                       void *stream);
 
 /* Router and top-k (routing and Top-K sections of the MoE page).
  *   x      [n][d]   activations (act = MOE_F32 or MOE_BF16)
@@ -185,7 +216,9 @@ int moe_active_experts(const moe_shape *s, const int32_t *counts, int32_t *activ
  *   y_perm  [n*k][d] float32 output (out must be MOE_F32)
  *   ws      device workspace of at least moe_workspace_bytes(s, w->dtype).
  * offsets is read on the device only; empty experts cost nothing.
- * With BF16/MXFP4 weights, x_perm and y_perm must be 16-byte aligned. */
+ * With BF16/MXFP4 weights, x_perm and y_perm must be 16-byte aligned.
+ * W4A8 mode: x_perm is bf16 (encoded here) or already MXFP8
+ * (act = MOE_MXFP8, an MXFP8 matrix of n*k rows). */
 int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act,
                     const int32_t *offsets, const moe_expert_weights *w,
                     void *y_perm, int out, void *ws, size_t ws_bytes,
@@ -202,7 +235,9 @@ int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act,
  * moe_expert_down: y_perm[r] = h[r] W2_e^T ("Dense models" section:
  *   down-projection), y_perm [n*k][d] f32.
  * offsets [E+1] as produced by moe_dispatch; read on the device only.
- * With BF16/MXFP4 weights, a, h and y_perm must be 16-byte aligned. */
+ * With BF16/MXFP4 weights, a, h and y_perm must be 16-byte aligned.
+ * W4A8 mode: a is an MXFP8 matrix (act = MOE_MXFP8) of n rows (with perm)
+ * or n*k rows, and h is an MXFP8 matrix of n*k rows x d_ff. */
 int moe_expert_up(const moe_shape *s, const void *a, int act, const int32_t *perm,
                   const int32_t *offsets, const moe_expert_weights *w, void *h,
                   void *stream);
@@ -223,7 +258,8 @@ int moe_combine(const moe_shape *s, const void *y_perm, int in,
  *   y [n][d] output (out = act, or F32),
  *   topk_idx / topk_w: optional [n][k] outputs (NULL = keep internal),
  *   ws: workspace of at least moe_workspace_bytes(s, w->dtype) bytes,
- *       16-byte aligned; its contents on entry do not matter. */
+ *       16-byte aligned; its contents on entry do not matter.
+ * W4A8 mode: x must be bf16; it is encoded to MXFP8 for the experts. */
 int moe_forward(const moe_shape *s, const void *x, int act, const void *wg,
                 const float *bias, const moe_expert_weights *w, void *y,
                 int out, int32_t *topk_idx, float *topk_w, void *ws,

@@ -16,8 +16,8 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
-MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
+MOE_F32, MOE_BF16, MOE_MXFP4, MOE_MXFP8 = 0, 1, 2, 3
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4, "mxfp8": MOE_MXFP8}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -34,11 +34,13 @@ class Shape(ctypes.Structure):
 
 class ExpertWeights(ctypes.Structure):
     # slot (device int32 [E]) / n_slots: logical -> physical expert slots;
-    # left at NULL / 0, expert e is slot e.
+    # left at NULL / 0, expert e is slot e.  act_quant: 0, or MOE_MXFP8 for
+    # the W4A8 mode.
     _fields_ = [("dtype", ctypes.c_int32),
                 ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("s1", ctypes.c_void_p), ("s3", ctypes.c_void_p), ("s2", ctypes.c_void_p),
-                ("slot", ctypes.c_void_p), ("n_slots", ctypes.c_int32)]
+                ("slot", ctypes.c_void_p), ("n_slots", ctypes.c_int32),
+                ("act_quant", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -59,6 +61,10 @@ lib.moe_status_string.restype = ctypes.c_char_p
 lib.moe_status_string.argtypes = [_I]
 lib.moe_workspace_bytes.restype = _SZ
 lib.moe_workspace_bytes.argtypes = [_SP, _I]
+lib.moe_mxfp8_bytes.restype = _SZ
+lib.moe_mxfp8_bytes.argtypes = [ctypes.c_int64, ctypes.c_int32]
+lib.moe_quantize_mxfp8.restype = _I
+lib.moe_quantize_mxfp8.argtypes = [ctypes.c_int64, ctypes.c_int32, _P, _I, _P, _P]
 lib.moe_router_topk.restype = _I
 lib.moe_router_topk.argtypes = [_SP, _P, _I, _P, _P, _P, _P, _P, _P]
 lib.moe_router_stats_workspace_bytes.restype = _SZ
@@ -80,7 +86,8 @@ lib.moe_combine.argtypes = [_SP, _P, _I, _P, _P, _P, _I, _P]
 lib.moe_forward.restype = _I
 lib.moe_forward.argtypes = [_SP, _P, _I, _P, _P, _WP, _P, _I, _P, _P, _P, _SZ, _P]
 
-EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_bytes", "moe_router_topk",
+EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_bytes", "moe_mxfp8_bytes",
+           "moe_quantize_mxfp8", "moe_router_topk",
            "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_active_experts",
            "moe_dispatch", "moe_grouped_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
            "moe_forward")
@@ -122,9 +129,10 @@ def _shape(s) -> Shape:
 def _weights(w) -> ExpertWeights:
     if isinstance(w, ExpertWeights):
         return w
+    aq = w.get("act_quant", 0)
     return ExpertWeights(_dt(w["dtype"]), _ptr(w["w1"]), _ptr(w["w3"]), _ptr(w["w2"]),
                          _ptr(w.get("s1")), _ptr(w.get("s3")), _ptr(w.get("s2")),
-                         _ptr(w.get("slot")), int(w.get("n_slots", 0)))
+                         _ptr(w.get("slot")), int(w.get("n_slots", 0)), _dt(aq) if aq else 0)
 
 
 def moe_abi_version() -> int:
@@ -137,6 +145,15 @@ def moe_status_string(status: int) -> str:
 
 def moe_workspace_bytes(shape, w_dtype) -> int:
     return lib.moe_workspace_bytes(ctypes.byref(_shape(shape)), _dt(w_dtype))
+
+
+def moe_mxfp8_bytes(rows, cols) -> int:
+    return int(lib.moe_mxfp8_bytes(int(rows), int(cols)))
+
+
+def moe_quantize_mxfp8(rows, cols, x, act, q, stream=None):
+    _check("moe_quantize_mxfp8", lib.moe_quantize_mxfp8(
+        int(rows), int(cols), _ptr(x), _dt(act), _ptr(q), _stream(stream)))
 
 
 def moe_router_topk(shape, x, act, wg, bias, logits, topk_idx, topk_w, stream=None):

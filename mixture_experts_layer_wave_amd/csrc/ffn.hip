@@ -15,10 +15,18 @@
 // accumulate).  MXFP4 tiles are dequantised to bf16 as they are written to
 // LDS (v_cvt_scalef32_pk_bf16_fp4: E2M1 x 2^(s-127) is exact in bf16), so
 // the MFMA loop is shared.  float32 weights take a plain FMA path.
+//
+// W4A8 mode (MXFP4 weights with act_quant): the expert input and the hidden
+// are MXFP8 and both projections run on the scaled MFMA with the weights in
+// their stored form (gemm_w4a8.hip).  The minseoc03.com feed's review of the
+// vLLM paper (section "What's Next") notes that quantised weights are
+// usually widened before the arithmetic and that the widening eats the
+// gain; here neither operand is widened.
 #include <cmath>
 
 #include "common.h"
 #include "gemm_big.h"
+#include "gemm_w4a8.h"
 #include "kernels.h"
 
 namespace moe {
@@ -360,9 +368,13 @@ double expected_row_tiles(const FfnArgs &a, int bm) {
   return piles * t;
 }
 
-TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_cand) {
+TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_cand,
+                       bool w4a8 = false) {
   const int N = up ? a.d_ff : a.d, K = up ? a.d : a.d_ff;
-  const long long nk = (K + 63) / 64;
+  // W4A8 steps are 128 deep and load bm x 128 B of codes, 256 x 64 B of
+  // weight codes and 2 KB of scales: bm + 144 units.
+  const int kstep = w4a8 ? 128 : 64;
+  const long long nk = (K + kstep - 1) / kstep;
   constexpr double kUnitsPerRound = 1500.0;   // ~5 us of per-block fixed cost
   constexpr double kUnitsPerByte = 312.0 / 6.0e6;  // partial sums at ~6 TB/s
   TileChoice best = cand[0];
@@ -376,8 +388,8 @@ TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_
     const double mt = ceil(expected_row_tiles(a, cand[i].bm) - 0.02);
     const long long nt = (N + cols - 1) / cols;
     const long long rounds = ((long long)mt * nt * S + 255) / 256;
-    double cost = (double)rounds * ((nk + S - 1) / S) * (cand[i].bm + cand[i].bnb) +
-                  rounds * kUnitsPerRound;
+    const double step_units = w4a8 ? cand[i].bm + 144.0 : (double)(cand[i].bm + cand[i].bnb);
+    double cost = (double)rounds * ((nk + S - 1) / S) * step_units + rounds * kUnitsPerRound;
     if (S > 1) cost += (2.0 * S - 1.0) * a.R * (double)N * 4.0 * kUnitsPerByte;
     if (i == 0 || cost < best_cost) {
       best = cand[i];
@@ -394,7 +406,72 @@ TileChoice down_tile(const FfnArgs &a) {
                                          {256, 256, 2}, {256, 256, 3}, {256, 256, 4}};
   static const TileChoice cand_mx[] = {{256, 256, 1}, {256, 128, 1}, {128, 128, 1},
                                        {256, 256, 2}, {256, 256, 3}, {256, 256, 4}};
+  static const TileChoice cand_w4a8[] = {{256, 256, 1}, {128, 256, 1}, {256, 256, 2},
+                                         {256, 256, 3}, {256, 256, 4}};
+  if (a.act_quant) return choose_tile(a, false, cand_w4a8, 5, true);
   return a.w_dtype == 2 ? choose_tile(a, false, cand_mx, 6) : choose_tile(a, false, cand_bf16, 7);
+}
+
+// W4A8 operands: MXFP8 matrix of `rows` rows x `cols` at m.
+W4A8Params w4a8_params(const FfnArgs &a, bool up) {
+  W4A8Params p{};
+  p.offsets = a.offsets;
+  p.slot = a.slot;
+  p.n_slots = a.n_slots;
+  p.E = a.E;
+  p.R = a.R;
+  const size_t rows = up ? (size_t)(a.perm ? a.n : a.R) : (size_t)a.R;
+  const int K = up ? a.d : a.d_ff;
+  const uint8_t *m = (const uint8_t *)(up ? a.a : a.h);
+  p.a = m;
+  p.as = m + mx8_scale_offset(rows, K);
+  p.a_bytes = (uint32_t)(rows * K);
+  p.as_bytes = (uint32_t)(rows * mx8_scale_pitch(K));
+  p.K = K;
+  if (up) {
+    p.perm = a.perm;
+    p.N = a.d_ff;
+    p.b0 = (const uint8_t *)a.w1;
+    p.b1 = (const uint8_t *)a.w3;
+    p.s0 = a.s1;
+    p.s1 = a.s3;
+    p.out = a.h;
+    p.out_s = (uint8_t *)a.h + mx8_scale_offset(a.R, a.d_ff);
+  } else {
+    p.N = a.d;
+    p.b0 = (const uint8_t *)a.w2;
+    p.s0 = a.s2;
+    p.out = a.y_perm;
+  }
+  return p;
+}
+
+hipError_t launch_w4a8_up(const FfnArgs &a, hipStream_t st) {
+  static const TileChoice cand[2] = {{256, 256, 1}, {128, 256, 1}};
+  const TileChoice t = choose_tile(a, true, cand, 2, true);
+  W4A8Params p = w4a8_params(a, true);
+  p.n_tiles = (a.d_ff + 127) / 128;
+  return launch_w4a8_gemm(p, true, a.perm != nullptr, t.bm, st);
+}
+
+hipError_t launch_w4a8_down(const FfnArgs &a, hipStream_t st, bool *fused) {
+  const TileChoice t = down_tile(a);
+  W4A8Params p = w4a8_params(a, false);
+  p.n_tiles = (a.d + 255) / 256;
+  if (t.splits > 1 && a.split_part && down_split_factor(a) > 1) {
+    p.splits = t.splits;
+    p.ksplit = ((a.d_ff + 128 * t.splits - 1) / (128 * t.splits)) * 128;
+    p.part = a.split_part;
+    hipError_t err = launch_w4a8_gemm(p, false, false, t.bm, st);
+    if (err != hipSuccess) return err;
+    if (a.comb_y) {
+      if (fused) *fused = true;
+      return launch_splitk_combine(a.split_part, t.splits, a.R, a.comb_inv, a.comb_w, a.n, a.k,
+                                   a.d, a.comb_y, a.comb_bf16, st);
+    }
+    return launch_splitk_sum(a.split_part, t.splits, a.R, a.d, a.y_perm, st);
+  }
+  return launch_w4a8_gemm(p, false, false, t.bm, st);
 }
 
 BigGemmParams big_params(const FfnArgs &a, bool up) {
@@ -434,10 +511,12 @@ BigGemmParams big_params(const FfnArgs &a, bool up) {
 constexpr int kDecodeMaxRows = 1024;
 
 bool use_decode(const FfnArgs &a) {
-  return a.w_dtype == 2 && a.R <= kDecodeMaxRows && decode_ffn_fits(a.d, a.d_ff, a.E);
+  return a.w_dtype == 2 && !a.act_quant && a.R <= kDecodeMaxRows &&
+         decode_ffn_fits(a.d, a.d_ff, a.E);
 }
 
 int down_split_factor(const FfnArgs &a) {
+  if (a.act_quant) return a.split_ok && a.R > 0 ? down_tile(a).splits : 1;
   if (!a.split_ok || a.R == 0 || use_decode(a) || a.d % 4 ||
       !big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff))
     return 1;
@@ -446,6 +525,7 @@ int down_split_factor(const FfnArgs &a) {
 
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
+  if (a.act_quant) return launch_w4a8_up(a, st);
   if (use_decode(a)) return launch_decode_up(a, st);
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d_ff;
@@ -486,6 +566,7 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
 hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
   if (fused) *fused = false;
   if (a.R == 0) return hipSuccess;
+  if (a.act_quant) return launch_w4a8_down(a, st, fused);
   if (use_decode(a)) return launch_decode_down(a, st);
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d;

@@ -32,11 +32,13 @@
 #include <atomic>
 #include <type_traits>
 
-#include "common.h"
 #include "gemm_big.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
+
+using namespace gemm;
 
 // K step and LDS stage count of the bf16 path (MXFP4 uses 64 and 2).
 #ifndef MOE_BF16_BK
@@ -45,45 +47,6 @@ namespace {
 #ifndef MOE_BF16_NST
 #define MOE_BF16_NST 2
 #endif
-// Waves per block (4 = one per SIMD, 8 = two per SIMD), arranged 2 x NW/2.
-#ifndef MOE_BIG_WAVES
-#define MOE_BIG_WAVES 8
-#endif
-constexpr int kNW = MOE_BIG_WAVES;
-constexpr int kNT = kNW * 64;
-
-constexpr uint32_t kOOB = 0x80000000u;  // offset bit past every record count
-constexpr uint32_t kRsrcFlags = 0x00020000u;
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                           kRsrcFlags);
-}
-
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_run, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_run, 16, voff, 0, 0, 0);
-}
-
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// LDS tile layout: rows of BK bf16 (BK * 2 bytes), 16-B chunks swizzled so
-// that the 16 consecutive rows read by one 16-lane pass of ds_read_b128 fall
-// in 16 distinct groups of 4 banks:
-//   BK = 64 (128-B rows): chunk c of row r at c ^ ((r / 2) % 8)
-//   BK = 32 ( 64-B rows): chunk c of row r at c ^ ((r / 4) % 4)
-template <int BK>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  if constexpr (BK == 64) return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
-  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
 
 template <int BM, int BNB, int BK>
 struct Tile {
@@ -105,7 +68,7 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   constexpr int NST = MX ? 2 : MOE_BF16_NST;
   using T = Tile<BM, BNB, BK>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ int s_e, s_row0, s_rows, s_nt, s_item;
+  __shared__ TileSlot s_t;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS DMA bases
@@ -113,57 +76,13 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   const int S = UP ? 1 : (p.splits > 1 ? p.splits : 1);
 
   // ---- block -> tile ------------------------------------------------------
-  if (wave == 0) {
-    const int per = (p.E + MOE_WAVE - 1) / MOE_WAVE;
-    const int eb = lane * per, ee = min(p.E, eb + per);
-    // With one expert per lane (E <= 64) its offsets are loaded once.
-    const int o0 = per == 1 && eb < p.E ? p.offsets[eb] : 0;
-    const int o1 = per == 1 && eb < p.E ? p.offsets[eb + 1] : 0;
-    int local = 0;
-    if (per == 1)
-      local = (o1 - o0 + BM - 1) / BM;
-    else
-      for (int x = eb; x < ee; ++x) local += (p.offsets[x + 1] - p.offsets[x] + BM - 1) / BM;
-    const int incl = wave_incl_scan(local);
-    const int excl = incl - local;
-    // Work items: tiles x splits, the splits of a tile adjacent.
-    const int total = __builtin_amdgcn_readlane(incl, MOE_WAVE - 1) * p.n_tiles * S;
-    const int b = blockIdx.x;
-    if (lane == 0 && b >= total) s_e = -1;
-    if (b < total) {
-      // XCD-contiguous remap of the ordered work list.
-      const int xcd = b & 7, slot = b >> 3;
-      int base = 0;
-      for (int x = 0; x < xcd; ++x) base += (total - x + 7) >> 3;
-      const int L = (base + slot) / S;
-      if (lane == 0) s_item = base + slot;
-      const int lo = excl * p.n_tiles, hi = incl * p.n_tiles;
-      if (L >= lo && L < hi) {
-        int acc = lo;
-        for (int x = eb; x < ee; ++x) {
-          const int ox = per == 1 ? o0 : p.offsets[x];
-          const int m = (per == 1 ? o1 : p.offsets[x + 1]) - ox;
-          const int te = (m + BM - 1) / BM;
-          if (L < acc + te * p.n_tiles) {
-            const int loc = L - acc;
-            const int mloc = loc % te;
-            s_e = x;
-            s_nt = loc / te;
-            s_row0 = ox + mloc * BM;
-            s_rows = min(BM, m - mloc * BM);
-            break;
-          }
-          acc += te * p.n_tiles;
-        }
-      }
-    }
-  }
+  if (wave == 0) map_block<BM>(p.offsets, p.E, p.n_tiles, S, lane, &s_t);
   __syncthreads();
-  const int e = s_e;
+  const int e = s_t.e;
   if (e < 0) return;
-  const int row0 = s_row0, rows = s_rows;
-  const int n0 = s_nt * (UP ? BNB / 2 : BNB);
-  const int split = s_item % S;
+  const int row0 = s_t.row0, rows = s_t.rows;
+  const int n0 = s_t.nt * (UP ? BNB / 2 : BNB);
+  const int split = s_t.item % S;
   // K range of this block: [kbeg, kend), a whole multiple of BK but the end.
   const int kbeg = S > 1 ? split * p.ksplit : 0;
   const int kend = S > 1 ? min(K, kbeg + p.ksplit) : K;
@@ -173,8 +92,7 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   // (4 j + w) * RPR + lane / CPR, stored chunk lane % CPR, which must hold
   // global chunk c = stored ^ key(row).  key(row) is the same for every run
   // of a wave: BK = 64: (4 (w % 2) + lane / 16) % 8;  BK = 32: lane / 16.
-  const int c = BK == 64 ? ((lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7))
-                         : ((lane & 3) ^ (lane >> 4));
+  const int c = dma_chunk<BK * 2>(wave, lane);
   const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, p.a_bytes);
   // Valid offsets are < 2^31 (checked on the host); an invalid row carries
   // bit 31 and the K tail ORs it in, so such lanes read zeros.
@@ -293,7 +211,7 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
           const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 3);
           const u32x4 o = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                            __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-          *(u32x4 *)(sb + swz<BK>(br, half * 4 + q)) = o;
+          *(u32x4 *)(sb + swz<BK * 2>(br, half * 4 + q)) = o;
         }
       }
     }
@@ -334,10 +252,10 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
     const int ch = kk * 2 + lg;
 #pragma unroll
     for (int tm = 0; tm < ACT; ++tm)
-      af[tm] = *(const bf16x8 *)(sa + swz<BK>(wm * T::WM + tm * 32 + lr, ch));
+      af[tm] = *(const bf16x8 *)(sa + swz<BK * 2>(wm * T::WM + tm * 32 + lr, ch));
     if constexpr (ACT > 0) {
 #pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn) bfr[tn] = *(const bf16x8 *)(sb + swz<BK>(brow(tn), ch));
+      for (int tn = 0; tn < T::TN; ++tn) bfr[tn] = *(const bf16x8 *)(sb + swz<BK * 2>(brow(tn), ch));
     }
   };
   auto mfmas = [&](auto actc, const bf16x8 *af, const bf16x8 *bfr) {
@@ -434,22 +352,8 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
     if (S > 1) {
       // Split K: this block's partial sums go to plane `split` (16-B stores of
       // four columns); a later kernel adds the planes in split order.
-      float *pl = p.part + (size_t)split * p.R * N;
-#pragma unroll
-      for (int tm = 0; tm < T::TM; ++tm) {
-        const int r = wm * T::WM + tm * 32 + lr;
-#pragma unroll
-        for (int tn = 0; tn < T::TN; ++tn)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int col = n0 + wn * T::WN + tn * 32 + g * 8 + lg * 4;
-            if (r < rows && col < N) {
-              const f32x4 v = {acc[tm][tn][g * 4], acc[tm][tn][g * 4 + 1], acc[tm][tn][g * 4 + 2],
-                               acc[tm][tn][g * 4 + 3]};
-              *(f32x4 *)(pl + (size_t)(row0 + r) * N + col) = v;
-            }
-          }
-      }
+      store_f32_tile<T::TM, T::TN, T::WM, T::WN>(acc, p.part + (size_t)split * p.R * N, N, row0,
+                                                 rows, n0, wm, wn, lane);
       return;
     }
   }
@@ -504,23 +408,9 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
       }
     }
   } else {
-    // f32 pile outputs: 16-B stores of four columns (N is a multiple of 8).
-    float *y = (float *)p.out;
-#pragma unroll
-    for (int tm = 0; tm < T::TM; ++tm) {
-      const int r = wm * T::WM + tm * 32 + lr;
-#pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int col = n0 + wn * T::WN + tn * 32 + g * 8 + lg * 4;
-          if (r < rows && col < N) {
-            const f32x4 v = {acc[tm][tn][g * 4], acc[tm][tn][g * 4 + 1], acc[tm][tn][g * 4 + 2],
-                             acc[tm][tn][g * 4 + 3]};
-            *(f32x4 *)(y + (size_t)(row0 + r) * N + col) = v;
-          }
-        }
-    }
+    // f32 pile outputs.
+    store_f32_tile<T::TM, T::TN, T::WM, T::WN>(acc, (float *)p.out, N, row0, rows, n0, wm, wn,
+                                               lane);
   }
 }
 

@@ -1,0 +1,151 @@
+// Device helpers shared by the grouped expert GEMMs (gemm_big.hip, bf16 and
+// MXFP4-dequantising; gemm_w4a8.hip, MXFP8 x MXFP4 on the scaled MFMA):
+// buffer resources and direct-to-LDS copies, the swizzled LDS row layouts,
+// the block -> (expert, row tile, column tile, K split) map and the f32
+// epilogue of the down projection.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace gemm {
+
+// Waves per block (4 = one per SIMD, 8 = two per SIMD), arranged 2 x NW/2.
+#ifndef MOE_BIG_WAVES
+#define MOE_BIG_WAVES 8
+#endif
+constexpr int kNW = MOE_BIG_WAVES;
+constexpr int kNT = kNW * 64;
+
+constexpr uint32_t kOOB = 0x80000000u;  // offset bit past every record count
+constexpr uint32_t kRsrcFlags = 0x00020000u;
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           kRsrcFlags);
+}
+
+// Direct-to-LDS copies: lane i of the instruction writes bytes
+// [16 i, 16 i + 16) (dma16) or [4 i, 4 i + 4) (dma4) of the run at lds_run.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t *lds_run, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_run, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t *lds_run, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_run, 4, voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS tile rows, 16-B chunks swizzled so that the 16 consecutive rows read
+// by one 16-lane pass of ds_read_b128 fall in 16 distinct groups of 4 banks:
+//   128-B rows: chunk c of row r at c ^ ((r / 2) % 8)
+//    64-B rows: chunk c of row r at c ^ ((r / 4) % 4)
+template <int ROWB>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  static_assert(ROWB == 128 || ROWB == 64, "row bytes");
+  if constexpr (ROWB == 128) return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// Global chunk a lane must fetch so that a 1 KB direct-to-LDS run of wave
+// `wave` lands in the swizzled layout (run j of wave w is rows
+// (kNW j + w) * 1024 / ROWB onwards; kNW is even, so the key depends on the
+// wave's parity only).
+template <int ROWB>
+__device__ __forceinline__ int dma_chunk(int wave, int lane) {
+  if constexpr (ROWB == 128) return (lane & 7) ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+  return (lane & 3) ^ (lane >> 4);
+}
+
+// Where a block works: pile e, rows [row0, row0 + rows), column tile nt,
+// work item (tile index * S + split).  Run by wave 0; e = -1 when the block
+// has no work.  Tiles are ordered expert-major, then column tile, then row
+// tile, the S splits of a tile adjacent; the ordered list is cut into 8
+// contiguous chunks, one per XCD (block b runs on XCD b mod 8), so the
+// tiles that share an expert's weights share one L2.
+struct TileSlot {
+  int e, row0, rows, nt, item;
+};
+
+template <int BM>
+__device__ __forceinline__ void map_block(const int32_t *offsets, int E, int n_tiles, int S,
+                                          int lane, TileSlot *out) {
+  const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
+  const int eb = lane * per, ee = min(E, eb + per);
+  // With one expert per lane (E <= 64) its offsets are loaded once.
+  const int o0 = per == 1 && eb < E ? offsets[eb] : 0;
+  const int o1 = per == 1 && eb < E ? offsets[eb + 1] : 0;
+  int local = 0;
+  if (per == 1)
+    local = (o1 - o0 + BM - 1) / BM;
+  else
+    for (int x = eb; x < ee; ++x) local += (offsets[x + 1] - offsets[x] + BM - 1) / BM;
+  const int incl = wave_incl_scan(local);
+  const int excl = incl - local;
+  const int total = __builtin_amdgcn_readlane(incl, MOE_WAVE - 1) * n_tiles * S;
+  const int b = blockIdx.x;
+  if (lane == 0 && b >= total) out->e = -1;
+  if (b >= total) return;
+  const int xcd = b & 7, slot = b >> 3;
+  int base = 0;
+  for (int x = 0; x < xcd; ++x) base += (total - x + 7) >> 3;
+  const int L = (base + slot) / S;
+  if (lane == 0) out->item = base + slot;
+  const int lo = excl * n_tiles, hi = incl * n_tiles;
+  if (L >= lo && L < hi) {
+    int acc = lo;
+    for (int x = eb; x < ee; ++x) {
+      const int ox = per == 1 ? o0 : offsets[x];
+      const int m = (per == 1 ? o1 : offsets[x + 1]) - ox;
+      const int te = (m + BM - 1) / BM;
+      if (L < acc + te * n_tiles) {
+        const int loc = L - acc;
+        const int mloc = loc % te;
+        out->e = x;
+        out->nt = loc / te;
+        out->row0 = ox + mloc * BM;
+        out->rows = min(BM, m - mloc * BM);
+        break;
+      }
+      acc += te * n_tiles;
+    }
+  }
+}
+
+// f32 stores of a block's accumulators: acc[tm][tn] of wave (wm, wn) holds
+// pile row wm*WM + tm*32 + lane%32 and columns wn*WN + tn*32 + (i/4)*8 +
+// (lane/32)*4 + i%4 (the MFMA takes the weight rows as its first operand),
+// so each lane stores 16-B runs of four columns.  dst is [R][N] f32 (N a
+// multiple of 8); rows past `rows` and columns past N are skipped.
+template <int TM, int TN, int WM, int WN>
+__device__ __forceinline__ void store_f32_tile(const f32x16 (&acc)[TM][TN], float *dst, int N,
+                                               int row0, int rows, int n0, int wm, int wn,
+                                               int lane) {
+  const int lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int r = wm * WM + tm * 32 + lr;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = n0 + wn * WN + tn * 32 + g * 8 + lg * 4;
+        if (r < rows && col < N) {
+          const f32x4 v = {acc[tm][tn][g * 4], acc[tm][tn][g * 4 + 1], acc[tm][tn][g * 4 + 2],
+                           acc[tm][tn][g * 4 + 3]};
+          *(f32x4 *)(dst + (size_t)(row0 + r) * N + col) = v;
+        }
+      }
+  }
+}
+
+}  // namespace gemm
+}  // namespace moe

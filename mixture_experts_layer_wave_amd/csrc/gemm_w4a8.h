@@ -1,0 +1,57 @@
+// Grouped expert GEMM on MXFP8 activations and MXFP4 weights
+// (gemm_w4a8.hip): host launch interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// MXFP8 matrix in memory (rows x cols, cols % 32 == 0): E4M3 codes
+// [rows][cols], then, from a 256-B aligned offset, E8M0 scales [rows][sp]
+// with sp = cols / 32 rounded up to a multiple of 4 (the padding bytes are
+// 0, the smallest scale).
+inline int mx8_scale_pitch(int cols) { return (cols / 32 + 3) / 4 * 4; }
+inline size_t mx8_scale_offset(size_t rows, int cols) {
+  return (rows * (size_t)cols + 255) / 256 * 256;
+}
+inline size_t mx8_bytes(size_t rows, int cols) {
+  return mx8_scale_offset(rows, cols) + rows * (size_t)mx8_scale_pitch(cols);
+}
+
+struct W4A8Params {
+  const uint8_t *a;         // E4M3 codes: token rows (gathered through perm) or pile rows
+  const uint8_t *as;        // their E8M0 scales, pitch mx8_scale_pitch(K)
+  uint32_t a_bytes, as_bytes;  // bytes of the code and scale parts (< 2^31)
+  const int32_t *perm;      // up: pile row -> row of a (NULL = contiguous)
+  const int32_t *offsets;   // [E+1] pile boundaries (device)
+  int E, R, N, K, n_tiles;  // R = rows of the pile matrix; N, K of one expert matrix
+  const uint8_t *b0, *b1;   // MXFP4 codes [E][N][K/2]; b1 (W3) for up only
+  const uint8_t *s0, *s1;   // their E8M0 scales [E][N][K/32]
+  const int32_t *slot;      // [E] logical -> physical weight slot, or NULL
+  int n_slots;
+  // up: the hidden as MXFP8, codes [R][N] at out and scales [R][pitch(N)]
+  // at out_s; down: f32 [R][N] at out.
+  void *out;
+  uint8_t *out_s;
+  // Split K (down only), as in the bf16 GEMM: block s of a tile covers K
+  // range [s ksplit, (s+1) ksplit) and writes part[s][R][N].
+  int splits, ksplit;
+  float *part;
+};
+
+// Largest K the kernel takes (the whole K range of a tile's weight scales
+// is kept in LDS).
+constexpr int kW4A8MaxK = 7168;
+
+// up: H = mx8(silu(A W1^T) * (A W3^T)); down: Yp = H W2^T.  Block tile
+// bm x 256 (bm = 256 or 128).  Returns hipErrorInvalidValue for a
+// combination not built.
+hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, hipStream_t st);
+
+// MXFP8 encoding of rows x cols bf16 (is_bf16) or f32 values into an
+// MXFP8 matrix (codes at q, scales at q_s).
+hipError_t launch_quantize_mx8(const void *x, bool is_bf16, int rows, int cols, uint8_t *q,
+                               uint8_t *q_s, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,466 @@
+// Grouped expert GEMM on the gfx950 scaled MFMA: MXFP8 activations times
+// MXFP4 weights, both kept in their stored form (the W4A8 mode of the
+// expert FFN; ffn.hip states the operation and its sources).
+//
+//   up:   H[r]  = mx8(silu(A[r] . W1_e^T) * (A[r] . W3_e^T))   (MXFP8 out)
+//   down: Yp[r] = H[r] . W2_e^T                                (f32 out)
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4 multiplies E2M1 weight codes (first
+// operand, format 4) by E4M3 activation codes (second operand, format 0),
+// each with one E8M0 scale per 32 K.  Its operand layout on gfx950:
+//   - FP4 operand: lane l holds row l % 32 and the 32 consecutive K
+//     [32 h, 32 h + 32) of the 64-K step (h = l / 32), two per byte with the
+//     even K in the low nibble: a 16-B piece of a stored MXFP4 row.
+//   - FP8 operand: lane l holds row l % 32; bytes 0-15 are K [16 h, 16 h + 16)
+//     and bytes 16-31 are K [32 + 16 h, 48 + 16 h).
+//   - Scales: lane l gives the scale of block h (K [32 h, 32 h + 32)) of its
+//     row, from the byte of its scale register that op_sel names.
+// The output layout is that of the bf16 MFMA: with the weight rows as the
+// first operand, accumulator element i of lane l is pile row l % 32 and
+// output column (i/4)*8 + (l/32)*4 + i%4 of the 32 x 32 tile.
+//
+// Block = 8 waves (2 x 4); tile BM pile rows x 256 weight rows; K step 128
+// (two MFMA k-steps) through two LDS stages.  A stage holds BM x 128 B of
+// activation codes (128-B rows), 256 x 64 B of weight codes (64-B rows),
+// both swizzled, and the BM rows' activation scales (one 4-B word per row
+// per step), all copied by direct-to-LDS buffer loads.  The weight scales of
+// the tile's 256 rows over the whole K range are one contiguous run per
+// matrix and are copied once per tile.  At BM = 256 a step moves 50 KB for
+// 16.8 MFLOP (the bf16 GEMM: 64 KB for 8.4 MFLOP), and the MFMA runs at
+// twice the bf16 rate.
+//
+// The up epilogue encodes the hidden as MXFP8 (OCP MX v1.0 rule): per row
+// and 32 columns, shared exponent X = floor(log2 amax) - 8 read from the
+// exponent bits of the float32 amax, elements v * 2^-X (exact) converted by
+// v_cvt_pk_fp8_f32 (round to nearest even) after a clamp to +-448.
+#include <atomic>
+#include <type_traits>
+
+#include "gemm_common.h"
+#include "gemm_w4a8.h"
+
+namespace moe {
+namespace {
+
+using namespace gemm;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+template <int BM_>
+struct T8 {
+  static constexpr int BM = BM_, BNB = 256, BK = 128;
+  static constexpr int WM = BM / 2, WN = BNB / (kNW / 2);
+  static constexpr int TM = WM / 32, TN = WN / 32;
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BNB * 64, AS_BYTES = kNW * 256;
+  static constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES;
+  static constexpr int A_RUNS = A_BYTES / 1024 / kNW;  // 1 KB runs per wave per stage
+  static constexpr int B_RUNS = B_BYTES / 1024 / kNW;
+  static constexpr int RW = BM / kNW;  // activation-scale rows copied by each wave
+  static_assert(A_RUNS >= 1 && B_RUNS >= 1 && RW <= 64, "tile shape");
+};
+
+// Weight-scale bytes of a tile kept in LDS: per matrix, rows x K/32 padded
+// to a whole 256-B run.
+__host__ __device__ constexpr int ws_region(int rows, int K) {
+  return (rows * (K / 32) + 255) / 256 * 256;
+}
+
+// One scaled MFMA: weights (E2M1, scale byte 0 of sw) times activations
+// (E4M3, scale byte OPA of sa).
+template <int OPA>
+__device__ __forceinline__ f32x16 mma(const v8i &w, const v8i &a, const f32x16 &c, int sw, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, 4, 0, 0, sw, OPA, sa);
+}
+
+// E8M0 code of the shared exponent for a block whose largest magnitude is
+// amax: floor(log2 amax) - 8 + 127 from the float32 exponent field (0 for
+// zero and float32 subnormals, the clamp at the bottom of the range).
+__device__ __forceinline__ uint32_t mx8_scale_code(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 255u);
+  return (uint32_t)max(ef - 8, 0);
+}
+// 2^-X for scale code c = X + 127 (c <= 247, so 254 - c is a normal exponent).
+__device__ __forceinline__ float mx8_inv_scale(uint32_t code) {
+  return __uint_as_float((254u - code) << 23);
+}
+
+// Four E4M3 codes of v[0..3] * inv (exact: a power of two), packed low to
+// high.  v_cvt_pk_fp8_f32 rounds to nearest even but turns magnitudes of
+// 464 and above into NaN, so the values are clamped to +-448 first; a value
+// in (448, 464) rounds to 448 either way, so this is the saturating
+// conversion.
+__device__ __forceinline__ uint32_t mx8_pack4(const float *v, float inv) {
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(v[i] * inv, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  return (uint32_t)w;
+}
+
+template <bool UP, bool GATHER, int BM>
+__global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
+  using T = T8<BM>;
+  constexpr int BNB = T::BNB, BK = T::BK;
+  constexpr int NR = UP ? BNB / 2 : BNB;  // weight rows per matrix in the tile
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ TileSlot s_t;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int N = p.N, K = p.K, KB = K / 32;
+  const int S = UP ? 1 : (p.splits > 1 ? p.splits : 1);
+
+  if (wave == 0) map_block<BM>(p.offsets, p.E, p.n_tiles, S, lane, &s_t);
+  __syncthreads();
+  const int e = s_t.e;
+  if (e < 0) return;
+  const int row0 = s_t.row0, rows = s_t.rows;
+  const int n0 = s_t.nt * NR;
+  const int split = s_t.item % S;
+  const int kbeg = S > 1 ? split * p.ksplit : 0;
+  const int kend = S > 1 ? min(K, kbeg + p.ksplit) : K;
+  const int sp = (KB + 3) / 4 * 4;  // activation scale pitch
+
+  // ---- copy offsets ---------------------------------------------------------
+  // Activation codes: run j of wave w fills rows (kNW j + w) * 8 + lane / 8.
+  // The pile-row -> token loads are issued together (index clamped into the
+  // tile, so every load is in bounds) and awaited once.  Valid offsets are
+  // < 2^31 (checked on the host); an invalid row carries bit 31, and so does
+  // a chunk past the K range, so such lanes read zeros.
+  const int ca = dma_chunk<128>(wave, lane);
+  const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, p.a_bytes), ras = rsrc(p.as, p.as_bytes);
+  uint32_t a_off[T::A_RUNS];
+  int a_src[T::A_RUNS];
+#pragma unroll
+  for (int j = 0; j < T::A_RUNS; ++j) {
+    const int r = (kNW * j + wave) * 8 + lane / 8;
+    a_src[j] = GATHER ? p.perm[row0 + min(r, rows - 1)] : row0 + r;
+  }
+  const int srow = T::RW * wave + lane;  // activation-scale row of this lane
+  const int s_src = GATHER ? p.perm[row0 + min(srow, rows - 1)] : row0 + srow;
+#pragma unroll
+  for (int j = 0; j < T::A_RUNS; ++j) {
+    const int r = (kNW * j + wave) * 8 + lane / 8;
+    a_off[j] = r < rows ? (uint32_t)a_src[j] * (uint32_t)K + (uint32_t)ca * 16u : kOOB;
+  }
+  const uint32_t as_off = (lane < T::RW && srow < rows) ? (uint32_t)s_src * (uint32_t)sp : kOOB;
+
+  // Weight codes: run j of wave w fills rows (kNW j + w) * 16 + lane / 4;
+  // up rows [0, 128) are W1 rows n0.., rows [128, 256) the same rows of W3.
+  const int pe = phys_slot(p.slot, p.n_slots, e);
+  const size_t qn = (size_t)N * (K / 2), sn = (size_t)N * KB;
+  const __amdgpu_buffer_rsrc_t rq0 = rsrc(p.b0 + (size_t)pe * qn, (uint32_t)qn);
+  const __amdgpu_buffer_rsrc_t rq1 = UP ? rsrc(p.b1 + (size_t)pe * qn, (uint32_t)qn) : rq0;
+  const __amdgpu_buffer_rsrc_t rs0 = rsrc(p.s0 + (size_t)pe * sn, (uint32_t)sn);
+  const __amdgpu_buffer_rsrc_t rs1 = UP ? rsrc(p.s1 + (size_t)pe * sn, (uint32_t)sn) : rs0;
+  const int cb = dma_chunk<64>(wave, lane);
+  uint32_t b_off[T::B_RUNS];
+#pragma unroll
+  for (int j = 0; j < T::B_RUNS; ++j) {
+    const int br = (kNW * j + wave) * 16 + lane / 4;
+    const int n = n0 + (UP ? br % NR : br);
+    b_off[j] = n < N ? (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)cb * 16u : kOOB;
+  }
+
+  // Weight scales of rows [n0, n0 + NR) over all K: one contiguous run of
+  // NR * K/32 bytes per matrix (4-B aligned: checked on the host), copied
+  // in 256-B pieces; bytes past the matrix read as zero.
+  uint8_t *wsc = smem + 2 * T::STAGE;
+  const int RB = NR * KB, RBP = ws_region(NR, K);
+  {
+    const uint32_t base = (uint32_t)n0 * (uint32_t)KB;
+#pragma unroll
+    for (int g = 0; g < (UP ? 2 : 1); ++g)
+      for (int q = wave; q < RBP / 256; q += kNW) {
+        const uint32_t o = (uint32_t)q * 256u + (uint32_t)lane * 4u;
+        dma4(g ? rs1 : rs0, wsc + g * RBP + q * 256, o < (uint32_t)RB ? base + o : kOOB);
+      }
+  }
+
+  // Copies of K step kt into LDS stage `stage`.  A step at or past the end
+  // issues only zero loads, which keeps the count per step fixed.
+  auto issue = [&](int kt, int stage) {
+    const int k0 = kbeg + kt * BK;
+    uint8_t *sa = smem + stage * T::STAGE;
+    uint8_t *sb = sa + T::A_BYTES;
+    uint8_t *ss = sb + T::B_BYTES;
+    const uint32_t pa = (k0 + ca * 16 < kend) ? 0u : kOOB;
+#pragma unroll
+    for (int j = 0; j < T::A_RUNS; ++j)
+      dma16(ra, sa + (kNW * j + wave) * 1024, (a_off[j] + (uint32_t)k0) | pa);
+    const uint32_t pb = (k0 + cb * 32 < kend) ? 0u : kOOB;
+#pragma unroll
+    for (int j = 0; j < T::B_RUNS; ++j) {
+      const bool second = UP && (kNW * j + wave) * 16 >= NR;
+      dma16(second ? rq1 : rq0, sb + (kNW * j + wave) * 1024,
+            (b_off[j] + (uint32_t)k0 / 2u) | pb);
+    }
+    dma4(ras, ss + wave * 256, (as_off + (uint32_t)k0 / 32u) | (k0 < kend ? 0u : kOOB));
+  };
+
+  const int wm = wave / (kNW / 2), wn = wave % (kNW / 2);
+  const int lr = lane & 31, lg = lane >> 5;
+  f32x16 acc[T::TM][T::TN];
+#pragma unroll
+  for (int a = 0; a < T::TM; ++a)
+#pragma unroll
+    for (int b = 0; b < T::TN; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  // B-row of wave-subtile j: up = gate rows then the matching value rows.
+  auto brow = [&](int j) {
+    if (UP)
+      return j < T::TN / 2 ? wn * (T::WN / 2) + j * 32 + lr
+                           : NR + wn * (T::WN / 2) + (j - T::TN / 2) * 32 + lr;
+    return wn * T::WN + j * 32 + lr;
+  };
+  // LDS address of this lane's weight-scale row for subtile j.
+  int ws_row[T::TN];
+#pragma unroll
+  for (int j = 0; j < T::TN; ++j) {
+    const int b = brow(j);
+    ws_row[j] = (b >= NR ? RBP : 0) + (b % NR) * KB;
+  }
+
+  // One K step: scales, then the fragments of both 64-K halves (the copies
+  // of a later step are issued between them), then the MFMAs.  ACT (a
+  // compile-time count) is the number of this wave's 32-row groups that hold
+  // pile rows; the empty groups of a ragged last row tile are neither read
+  // nor multiplied.  A wave with ACT = 0 still copies and meets every barrier.
+  auto step = [&](auto actc, int kt, int stage, int kt_issue, int stage_issue) {
+    constexpr int ACT = decltype(actc)::value;
+    const uint8_t *sa = smem + stage * T::STAGE;
+    const uint8_t *sb = sa + T::A_BYTES;
+    const uint8_t *ss = sb + T::B_BYTES;
+    const int blk0 = kbeg / 32 + kt * 4 + lg;  // K block of this lane's half, first 64-K half
+    const int kbend = (kend + 31) / 32;
+    uint32_t asc[T::TM], wsc0[T::TN], wsc1[T::TN];
+    v8i af0[T::TM], af1[T::TM], bf0[T::TN], bf1[T::TN];
+#pragma unroll
+    for (int tm = 0; tm < ACT; ++tm) {
+      const int r = wm * T::WM + tm * 32 + lr;
+      asc[tm] = *(const uint32_t *)(ss + (r / T::RW) * 256 + (r % T::RW) * 4) >> (8 * lg);
+    }
+    if constexpr (ACT > 0) {
+#pragma unroll
+      for (int tn = 0; tn < T::TN; ++tn) {
+        // a block past the K range multiplies zero codes; its byte (another
+        // row's) is replaced by 1.0 so that a NaN scale cannot leak in
+        wsc0[tn] = blk0 < kbend ? wsc[ws_row[tn] + blk0] : 127u;
+        wsc1[tn] = blk0 + 2 < kbend ? wsc[ws_row[tn] + blk0 + 2] : 127u;
+      }
+    }
+    auto frags = [&](int kk, v8i *af, v8i *bf) {
+#pragma unroll
+      for (int tm = 0; tm < ACT; ++tm) {
+        const int r = wm * T::WM + tm * 32 + lr;
+        const u32x4 lo = *(const u32x4 *)(sa + swz<128>(r, 4 * kk + lg));
+        const u32x4 hi = *(const u32x4 *)(sa + swz<128>(r, 4 * kk + 2 + lg));
+        af[tm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      if constexpr (ACT > 0) {
+#pragma unroll
+        for (int tn = 0; tn < T::TN; ++tn) {
+          const u32x4 w = *(const u32x4 *)(sb + swz<64>(brow(tn), 2 * kk + lg));
+          bf[tn] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+        }
+      }
+    };
+    frags(0, af0, bf0);
+    issue(kt_issue, stage_issue);
+    frags(1, af1, bf1);
+#pragma unroll
+    for (int tm = 0; tm < ACT; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < T::TN; ++tn)
+        acc[tm][tn] = mma<0>(bf0[tn], af0[tm], acc[tm][tn], (int)wsc0[tn], (int)asc[tm]);
+#pragma unroll
+    for (int tm = 0; tm < ACT; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < T::TN; ++tn)
+        acc[tm][tn] = mma<2>(bf1[tn], af1[tm], acc[tm][tn], (int)wsc1[tn], (int)asc[tm]);
+  };
+
+  const int nk = (kend - kbeg + BK - 1) / BK;
+  auto kloop = [&](auto actc) {
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      step(actc, kt, kt & 1, kt + 1, (kt + 1) & 1);
+    }
+  };
+  issue(0, 0);
+  const int act = __builtin_amdgcn_readfirstlane(min(T::TM, max(0, (rows - wm * T::WM + 31) / 32)));
+  static_assert(T::TM == 2 || T::TM == 4, "row groups per wave");
+  if (act == T::TM) {
+    kloop(std::integral_constant<int, T::TM>{});
+  } else if (act == 0) {
+    kloop(std::integral_constant<int, 0>{});
+  } else if (act == 1) {
+    kloop(std::integral_constant<int, 1>{});
+  } else if constexpr (T::TM == 4) {
+    if (act == 2)
+      kloop(std::integral_constant<int, 2>{});
+    else
+      kloop(std::integral_constant<int, 3>{});
+  }
+  wait_vmcnt<0>();
+
+  // ---- epilogue ---------------------------------------------------------------
+  if constexpr (!UP) {
+    float *dst = S > 1 ? p.part + (size_t)split * p.R * N : (float *)p.out;
+    store_f32_tile<T::TM, T::TN, T::WM, T::WN>(acc, dst, N, row0, rows, n0, wm, wn, lane);
+  } else {
+    // MXFP8 hidden staged through LDS: codes [BM][128 + 16 pad], then one
+    // 4-B word of scales per row (the tile's 128 columns are 4 blocks).
+    constexpr int OC = NR, PITCH = OC + 16;
+    static_assert(OC == 128, "four scale blocks per row and tile");
+    __syncthreads();  // every wave is done reading the stages
+    uint8_t *so = smem;
+    uint8_t *sso = smem + BM * PITCH;
+#pragma unroll
+    for (int tm = 0; tm < T::TM; ++tm) {
+      const int r = wm * T::WM + tm * 32 + lr;
+#pragma unroll
+      for (int j = 0; j < T::TN / 2; ++j) {
+        float v[16];
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          v[i] = silu(acc[tm][j][i]) * acc[tm][j + T::TN / 2][i];
+          amax = fmaxf(amax, fabsf(v[i]));
+        }
+        // the other 16 columns of the block are in lane l ^ 32
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const uint32_t code = mx8_scale_code(amax);
+        const float inv = mx8_inv_scale(code);
+        const int c0 = wn * (T::WN / 2) + j * 32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *(uint32_t *)(so + r * PITCH + c0 + g * 8 + lg * 4) = mx8_pack4(v + 4 * g, inv);
+        if (lg == 0) sso[r * 4 + c0 / 32] = (uint8_t)code;
+      }
+    }
+    __syncthreads();
+    uint8_t *oq = (uint8_t *)p.out;
+    const int spo = (N / 32 + 3) / 4 * 4;
+    constexpr int CH = OC / 16;
+    for (int idx = tid; idx < BM * CH; idx += kNT) {
+      const int r = idx / CH, ch = idx % CH;
+      const int col = n0 + ch * 16;
+      if (r < rows && col < N)
+        *(u32x4 *)(oq + (size_t)(row0 + r) * N + col) = *(const u32x4 *)(so + r * PITCH + ch * 16);
+    }
+    // n0 / 32 is a multiple of 4 and at most spo - 4: the word is in the row
+    for (int r = tid; r < rows; r += kNT)
+      *(uint32_t *)(p.out_s + (size_t)(row0 + r) * spo + n0 / 32) = *(const uint32_t *)(sso + r * 4);
+  }
+}
+
+template <bool UP, bool GATHER, int BM>
+hipError_t launch_one(const W4A8Params &p, int blocks, hipStream_t st) {
+  using T = T8<BM>;
+  constexpr int NR = UP ? T::BNB / 2 : T::BNB;
+  const int lds = 2 * T::STAGE + (UP ? 2 : 1) * ws_region(NR, p.K);
+  constexpr int lds_max = 2 * T::STAGE + (UP ? 2 : 1) * ws_region(NR, kW4A8MaxK);
+  static_assert(lds_max <= 160 * 1024, "LDS budget");
+  static_assert(BM * (NR + 16) + BM * 4 <= 2 * T::STAGE, "epilogue staging fits the stages");
+  auto kern = w4a8_gemm_kernel<UP, GATHER, BM>;
+  // Dynamic LDS above 64 KB must be allowed once per device (at the largest
+  // size any call asks for).
+  static std::atomic<uint64_t> attr_done{0};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_done.load(std::memory_order_acquire) & bit)) {
+    err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              lds_max);
+    if (err != hipSuccess) return err;
+    attr_done.fetch_or(bit, std::memory_order_release);
+  }
+  kern<<<blocks, kNT, lds, st>>>(p);
+  return hipGetLastError();
+}
+
+// MXFP8 encoding, one lane per 32-block (lanes past a row's last block
+// write its zero padding scales).
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_mx8_kernel(const void *x, int rows, int cols,
+                                                           uint8_t *q, uint8_t *qs) {
+  const int nb = cols / 32, sp = (nb + 3) / 4 * 4;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (long long)rows * sp) return;
+  const int row = (int)(gid / sp), blk = (int)(gid % sp);
+  if (blk >= nb) {
+    qs[(size_t)row * sp + blk] = 0;
+    return;
+  }
+  float v[32];
+  const size_t at = (size_t)row * cols + (size_t)blk * 32;
+  if constexpr (BF16) {
+    const u32x4 *src = (const u32x4 *)((const uint16_t *)x + at);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = src[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[c * 8 + 2 * i] = __uint_as_float(w[i] << 16);
+        v[c * 8 + 2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
+    }
+  } else {
+    const f32x4 *src = (const f32x4 *)((const float *)x + at);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const f32x4 w = src[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[c * 4 + i] = w[i];
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const uint32_t code = mx8_scale_code(amax);
+  const float inv = mx8_inv_scale(code);
+  uint32_t o[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) o[g] = mx8_pack4(v + 4 * g, inv);
+  u32x4 *dst = (u32x4 *)(q + at);
+  dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+  dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+  qs[(size_t)row * sp + blk] = (uint8_t)code;
+}
+
+}  // namespace
+
+hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, hipStream_t st) {
+  const int m_tiles = (p.R + bm - 1) / bm + (p.E < p.R ? p.E : p.R);
+  const int blocks = m_tiles * p.n_tiles * (up ? 1 : (p.splits > 1 ? p.splits : 1));
+  if (p.K > kW4A8MaxK || p.K % 32) return hipErrorInvalidValue;
+  if (up && gather && bm == 256) return launch_one<true, true, 256>(p, blocks, st);
+  if (up && !gather && bm == 256) return launch_one<true, false, 256>(p, blocks, st);
+  if (up && gather && bm == 128) return launch_one<true, true, 128>(p, blocks, st);
+  if (up && !gather && bm == 128) return launch_one<true, false, 128>(p, blocks, st);
+  if (!up && bm == 256) return launch_one<false, false, 256>(p, blocks, st);
+  if (!up && bm == 128) return launch_one<false, false, 128>(p, blocks, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_mx8(const void *x, bool is_bf16, int rows, int cols, uint8_t *q,
+                               uint8_t *q_s, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const long long lanes = (long long)rows * mx8_scale_pitch(cols);
+  if ((lanes + 255) / 256 > 0x7fffffffll) return hipErrorInvalidValue;
+  const int blocks = (int)((lanes + 255) / 256);
+  if (is_bf16)
+    quantize_mx8_kernel<true><<<blocks, 256, 0, st>>>(x, rows, cols, q, q_s);
+  else
+    quantize_mx8_kernel<false><<<blocks, 256, 0, st>>>(x, rows, cols, q, q_s);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -70,6 +70,10 @@ struct FfnArgs {
   const int32_t *comb_inv;
   const float *comb_w;
   bool comb_bf16;
+  // W4A8 mode (MXFP4 weights only): a and h are MXFP8 matrices (E4M3 codes,
+  // then E8M0 scales; layout in gemm_w4a8.h) of (perm ? n : R) and R rows,
+  // and both projections run on the scaled MFMA.
+  bool act_quant;
 };
 // K splits the down pass takes for these arguments (1 = none); with
 // split_ok set it tells the workspace layout how many partial planes

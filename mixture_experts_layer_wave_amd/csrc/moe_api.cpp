@@ -5,6 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
+#include "gemm_w4a8.h"
 #include "kernels.h"
 
 namespace {
@@ -81,18 +84,50 @@ WsLayout layout(const moe_shape *s, int wdt) {
   L.offsets = take((E + 1) * 4);
   L.perm = take(R * 4);
   L.inv = take(R * 4);
-  L.h = take(R * (size_t)s->d_ff * (wdt == MOE_F32 ? 4 : 2));
-  L.yp = take(R * (size_t)s->d * 4);
+  // h holds the bf16 hidden, or (W4A8) the MXFP8 hidden; yp holds the pile
+  // outputs and, before them, the MXFP8 expert input of the W4A8 mode.
+  size_t hb = R * (size_t)s->d_ff * (wdt == MOE_F32 ? 4 : 2);
+  size_t yb = R * (size_t)s->d * 4;
+  if (wdt == MOE_MXFP4 && s->d % 32 == 0 && s->d_ff % 32 == 0) {
+    hb = std::max(hb, moe::mx8_bytes(R, s->d_ff));
+    yb = std::max(yb, moe::mx8_bytes(R, s->d));
+  }
+  L.h = take(hb);
+  L.yp = take(yb);
   L.splits = moe::down_split_factor(plan_args(s, wdt));
+  if (wdt == MOE_MXFP4 && s->d % 32 == 0 && s->d_ff % 32 == 0 && s->d <= moe::kW4A8MaxK &&
+      s->d_ff <= moe::kW4A8MaxK) {
+    moe::FfnArgs q = plan_args(s, wdt);  // the W4A8 mode may split K differently
+    q.act_quant = true;
+    L.splits = std::max(L.splits, moe::down_split_factor(q));
+  }
   L.part = take(L.splits > 1 ? (size_t)L.splits * R * (size_t)s->d * 4 : 0);
   L.total = o;
   return L;
 }
 
-int check_weights(const moe_shape *s, int act, const moe_expert_weights *w) {
+// The W4A8 mode: MXFP4 weights, shapes the scaled-MFMA GEMM takes, and
+// 32-bit offsets into the MXFP8 operands (the larger of n*k and n rows).
+int check_w4a8(const moe_shape *s, const moe_expert_weights *w) {
+  if (w->act_quant == 0) return MOE_OK;
+  if (w->act_quant != MOE_MXFP8 || w->dtype != MOE_MXFP4) return MOE_ERR_DTYPE;
+  if (s->d > moe::kW4A8MaxK || s->d_ff > moe::kW4A8MaxK) return MOE_ERR_SHAPE;
+  if (((long long)s->d_ff * (s->d / 32)) % 4 || ((long long)s->d * (s->d_ff / 32)) % 4)
+    return MOE_ERR_SHAPE;
+  const long long R = (long long)s->n * s->k;
+  if (R * std::max(s->d, s->d_ff) >= (1ll << 31)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+// act_mx8: the activations handed in are already an MXFP8 matrix.
+int check_weights(const moe_shape *s, int act, const moe_expert_weights *w,
+                  bool act_mx8 = false) {
   if (!w) return MOE_ERR_NULL;
-  const int st = check_dtypes(s, act, w->dtype);
+  if (act_mx8 && !w->act_quant) return MOE_ERR_DTYPE;
+  const int st = check_dtypes(s, act_mx8 ? MOE_BF16 : act, w->dtype);
   if (st != MOE_OK) return st;
+  const int sq = check_w4a8(s, w);
+  if (sq != MOE_OK) return sq;
   if (!w->w1 || !w->w3 || !w->w2) return MOE_ERR_NULL;
   if (w->slot && w->n_slots < 1) return MOE_ERR_SHAPE;
   if (w->dtype == MOE_MXFP4 && (!w->s1 || !w->s3 || !w->s2)) return MOE_ERR_NULL;
@@ -128,6 +163,7 @@ moe::FfnArgs ffn_args(const moe_shape *s, const void *a, const int32_t *perm,
   f.y_perm = yp;
   f.n = s->n;
   f.k = s->k;
+  f.act_quant = w->act_quant == MOE_MXFP8;
   return f;
 }
 
@@ -154,6 +190,24 @@ size_t moe_workspace_bytes(const moe_shape *s, int w_dtype) {
   if (check_shape(s) != MOE_OK) return 0;
   if (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_MXFP4) return 0;
   return layout(s, w_dtype).total;
+}
+
+size_t moe_mxfp8_bytes(int64_t rows, int32_t cols) {
+  if (rows < 0 || cols <= 0 || cols % 32) return 0;
+  return moe::mx8_bytes((size_t)rows, cols);
+}
+
+int moe_quantize_mxfp8(int64_t rows, int32_t cols, const void *x, int act, void *q,
+                       void *stream) {
+  if (rows < 0 || rows > (1ll << 31) - 1 || cols <= 0 || cols % 32) return MOE_ERR_SHAPE;
+  if (act != MOE_F32 && act != MOE_BF16) return MOE_ERR_DTYPE;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q)) return MOE_ERR_ALIGN;
+  uint8_t *qc = (uint8_t *)q;
+  return hip_status(moe::launch_quantize_mx8(x, act == MOE_BF16, (int)rows, cols, qc,
+                                             qc + moe::mx8_scale_offset((size_t)rows, cols),
+                                             (hipStream_t)stream));
 }
 
 int moe_router_topk(const moe_shape *s, const void *x, int act, const void *wg,
@@ -229,29 +283,42 @@ int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act, const int32
                     size_t ws_bytes, void *stream) {
   int st = check_shape(s);
   if (st != MOE_OK) return st;
-  st = check_weights(s, act, w);
+  const bool mx8_in = act == MOE_MXFP8;
+  st = check_weights(s, act, w, mx8_in);
   if (st != MOE_OK) return st;
   if (!x_perm || !offsets || !y_perm) return MOE_ERR_NULL;
   if (out != MOE_F32) return MOE_ERR_DTYPE;
-  if (act == MOE_BF16 && (!aligned16(x_perm) || !aligned16(y_perm))) return MOE_ERR_ALIGN;
+  if (act != MOE_F32 && (!aligned16(x_perm) || !aligned16(y_perm))) return MOE_ERR_ALIGN;
   const WsLayout L = layout(s, w->dtype);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
   char *base = (char *)ws;
-  moe::FfnArgs f = ffn_args(s, x_perm, nullptr, offsets, w, base + L.h, (float *)y_perm);
+  hipStream_t hs = (hipStream_t)stream;
+  const void *a = x_perm;
+  if (w->act_quant && !mx8_in) {
+    // encode the pile rows into the (not yet used) pile-output region
+    uint8_t *xq = (uint8_t *)(base + L.yp);
+    const size_t R = (size_t)s->n * s->k;
+    hipError_t e = moe::launch_quantize_mx8(x_perm, true, (int)R, s->d, xq,
+                                            xq + moe::mx8_scale_offset(R, s->d), hs);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    a = xq;
+  }
+  moe::FfnArgs f = ffn_args(s, a, nullptr, offsets, w, base + L.h, (float *)y_perm);
   f.split_ok = true;
   f.split_part = (float *)(base + L.part);
-  return hip_status(moe::launch_grouped_ffn(f, (hipStream_t)stream));
+  return hip_status(moe::launch_grouped_ffn(f, hs));
 }
 
 int moe_expert_up(const moe_shape *s, const void *a, int act, const int32_t *perm,
                   const int32_t *offsets, const moe_expert_weights *w, void *h, void *stream) {
   int st = check_shape(s);
   if (st != MOE_OK) return st;
-  st = check_weights(s, act, w);
+  if (w && w->act_quant && act != MOE_MXFP8) return MOE_ERR_DTYPE;
+  st = check_weights(s, act, w, act == MOE_MXFP8);
   if (st != MOE_OK) return st;
   if (!a || !offsets || !h) return MOE_ERR_NULL;
-  if (act == MOE_BF16 && !aligned16(a)) return MOE_ERR_ALIGN;
+  if (act != MOE_F32 && (!aligned16(a) || !aligned16(h))) return MOE_ERR_ALIGN;
   const moe::FfnArgs f = ffn_args(s, a, perm, offsets, w, h, nullptr);
   return hip_status(moe::launch_expert_up(f, (hipStream_t)stream));
 }
@@ -314,9 +381,17 @@ int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, cons
     if (e == hipSuccess)
       e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
   }
+  const void *a = x;
+  if (e == hipSuccess && w->act_quant) {
+    // the experts' input: x as MXFP8, in the (not yet used) pile-output region
+    uint8_t *xq = (uint8_t *)yp;
+    e = moe::launch_quantize_mx8(x, true, s->n, s->d, xq,
+                                 xq + moe::mx8_scale_offset((size_t)s->n, s->d), hs);
+    a = xq;
+  }
   bool fused = false;
   if (e == hipSuccess) {
-    moe::FfnArgs f = ffn_args(s, x, perm, offsets, w, base + L.h, yp);
+    moe::FfnArgs f = ffn_args(s, a, perm, offsets, w, base + L.h, yp);
     f.split_ok = true;
     f.split_part = (float *)(base + L.part);
     f.comb_y = y;

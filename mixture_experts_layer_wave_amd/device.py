@@ -32,7 +32,8 @@ def bf16_tensor_to_f64(t: torch.Tensor) -> np.ndarray:
 class DeviceLayer:
     """One layer's inputs in HBM plus the output and workspace buffers."""
 
-    def __init__(self, layer: dict, device: str = "cuda", renorm: int | None = None):
+    def __init__(self, layer: dict, device: str = "cuda", renorm: int | None = None,
+                 act_quant: str | None = None):
         self.layer = layer
         self.device = device
         self.n, self.d, self.E, self.k, self.d_ff = (layer[key] for key in ("n", "d", "E", "k", "d_ff"))
@@ -44,7 +45,9 @@ class DeviceLayer:
         self.wg = to_device(layer["wg"], device)
         self.bias = to_device(layer.get("bias"), device)
         self.w = {key: to_device(layer.get(key), device) for key in ("w1", "w3", "w2", "s1", "s3", "s2")}
-        self.weights = B.ExpertWeights(B.DTYPES[self.wdt], *(B._ptr(self.w[key]) for key in ("w1", "w3", "w2", "s1", "s3", "s2")))
+        self.act_quant = act_quant
+        self.weights = B.ExpertWeights(B.DTYPES[self.wdt], *(B._ptr(self.w[key]) for key in ("w1", "w3", "w2", "s1", "s3", "s2")),
+                                       None, 0, B.DTYPES[act_quant] if act_quant else 0)
         self.ws_bytes = B.moe_workspace_bytes(self.shape, self.wdt)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         ydt = torch.int16 if self.act == "bf16" else torch.float32

@@ -29,7 +29,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 # Sources that define each profiled kernel family (relative to the package).
 KERNEL_SOURCES = {
-    "big_gemm_kernel": ["csrc/gemm_big.hip", "csrc/gemm_big.h", "csrc/common.h"],
+    "big_gemm_kernel": ["csrc/gemm_big.hip", "csrc/gemm_big.h", "csrc/gemm_common.h",
+                        "csrc/common.h"],
+    "w4a8_gemm_kernel": ["csrc/gemm_w4a8.hip", "csrc/gemm_w4a8.h", "csrc/gemm_common.h",
+                         "csrc/common.h"],
     "mx_decode_kernel": ["csrc/decode.hip", "csrc/common.h"],
 }
 

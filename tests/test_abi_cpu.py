@@ -140,3 +140,47 @@ def test_slots_and_active_experts_errors_before_launch():
     w = B.ExpertWeights(1, fake, fake, fake, None, None, None, fake, 0)
     y = fake
     assert B.lib.moe_expert_down(sp, fake, fake, ctypes.byref(w), y, None) == -2
+
+
+def test_w4a8_sizes_and_errors_before_launch():
+    import ctypes
+
+    from mixture_experts_layer_wave_amd import binding as B
+
+    # MXFP8 matrix: codes, then scales from a 256-B boundary, pitch rounded to 4
+    assert B.moe_mxfp8_bytes(3, 96) == 512 + 3 * 4
+    assert B.moe_mxfp8_bytes(4096, 2880) == 4096 * 2880 + 4096 * 92
+    assert B.moe_mxfp8_bytes(0, 64) == 0
+    assert B.moe_mxfp8_bytes(4, 40) == 0 and B.moe_mxfp8_bytes(-1, 64) == 0
+    fake = 1 << 20  # never dereferenced: every check below fails before a launch
+    assert B.lib.moe_quantize_mxfp8(4, 40, fake, 1, fake, None) == -2
+    assert B.lib.moe_quantize_mxfp8(4, 64, fake, 2, fake, None) == -3
+    assert B.lib.moe_quantize_mxfp8(4, 64, None, 1, fake, None) == -1
+    assert B.lib.moe_quantize_mxfp8(4, 64, fake + 8, 1, fake, None) == -4
+    assert B.lib.moe_quantize_mxfp8(0, 64, None, 1, None, None) == 0
+
+    mx8 = B.MOE_MXFP8
+    big_ws = 1 << 30
+    sp = ctypes.byref(B._shape((16, 64, 8, 2, 64)))
+    fwd = lambda shape, w: B.lib.moe_forward(shape, fake, 1, fake, None, ctypes.byref(w), fake, 1,
+                                             None, None, fake, big_ws, None)
+    # the W4A8 mode needs MXFP4 weights, and a known mode
+    assert fwd(sp, B.ExpertWeights(1, fake, fake, fake, None, None, None, None, 0, mx8)) == -3
+    assert fwd(sp, B.ExpertWeights(2, fake, fake, fake, fake, fake, fake, None, 0, 7)) == -3
+    w4 = B.ExpertWeights(2, fake, fake, fake, fake, fake, fake, None, 0, mx8)
+    # K past what the GEMM keeps of a tile's weight scales
+    assert fwd(ctypes.byref(B._shape((16, 7200, 8, 2, 64))), w4) == -2
+    assert fwd(ctypes.byref(B._shape((16, 64, 8, 2, 7200))), w4) == -2
+    # moe_expert_up in the mode takes MXFP8 rows (act = MOE_MXFP8), aligned
+    assert B.lib.moe_expert_up(sp, fake, 1, None, fake, ctypes.byref(w4), fake, None) == -3
+    assert B.lib.moe_expert_up(sp, None, mx8, None, fake, ctypes.byref(w4), fake, None) == -1
+    assert B.lib.moe_expert_up(sp, fake + 8, mx8, None, fake, ctypes.byref(w4), fake, None) == -4
+    # MXFP8 rows without the mode
+    w0 = B.ExpertWeights(2, fake, fake, fake, fake, fake, fake, None, 0, 0)
+    assert B.lib.moe_expert_up(sp, fake, mx8, None, fake, ctypes.byref(w0), fake, None) == -3
+    assert B.lib.moe_grouped_ffn(sp, fake, mx8, fake, ctypes.byref(w0), fake, 0, fake, big_ws, None) == -3
+    # the workspace of MXFP4 covers the mode's encoded input and hidden
+    n, d, E, k, f = 4096, 2880, 128, 4, 2880
+    R = n * k
+    ws = B.moe_workspace_bytes((n, d, E, k, f), "mxfp4")
+    assert ws >= B.moe_mxfp8_bytes(R, d) + B.moe_mxfp8_bytes(R, f)
