@@ -104,4 +104,35 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(s << 23);
 }
 
+// ---- MXFP8 encoding (OCP MX v1.0: E4M3 elements, one E8M0 scale per 32) --
+// E8M0 code of the shared exponent for a block whose largest magnitude is
+// amax: floor(log2 amax) - 8 + 127 from the float32 exponent field (0 for
+// zero and float32 subnormals, the clamp at the bottom of the range).
+__device__ __forceinline__ uint32_t mx8_scale_code(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 255u);
+  return (uint32_t)max(ef - 8, 0);
+}
+// Scale bytes per row of an MXFP8 matrix: cols / 32 rounded up to 4.
+__host__ __device__ __forceinline__ int mx8_scale_pitch_dev(int cols) {
+  return (cols / 32 + 3) / 4 * 4;
+}
+// 2^-X for scale code c = X + 127 (c <= 247, so 254 - c is a normal exponent).
+__device__ __forceinline__ float mx8_inv_scale(uint32_t code) {
+  return __uint_as_float((254u - code) << 23);
+}
+
+// Four E4M3 codes of v[0..3] * inv (exact: a power of two), packed low to
+// high.  v_cvt_pk_fp8_f32 rounds to nearest even but turns magnitudes of
+// 464 and above into NaN, so the values are clamped to +-448 first; a value
+// in (448, 464) rounds to 448 either way, so this is the saturating
+// conversion.
+__device__ __forceinline__ uint32_t mx8_pack4(const float *v, float inv) {
+  float c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(v[i] * inv, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  return (uint32_t)w;
+}
+
 }  // namespace moe

@@ -28,9 +28,22 @@
 // activations are read in the same order (any fixed K order is valid when
 // both operands agree).  The four waves split K; partial sums meet in LDS
 // in a fixed order (deterministic).
+//
+// W4A8 mode (A8): the pile rows are MXFP8 and the multiply runs on
+// v_mfma_scale_f32_16x16x128_f8f6f4 with the weight codes as they sit in
+// LDS (no conversion).  Operand layout on gfx950: the FP4 operand's lane
+// group g holds K [32 g, 32 g + 32) of the 128-deep step (the 16 code bytes
+// of block 4 s + g, as above) and gives that block's scale; the FP8
+// operand's lane group g holds K [16 g, 16 g + 16) in bytes 0-15 and
+// K [64 + 16 g, 80 + 16 g) in bytes 16-31 and gives the scale of block g.
+// The up epilogue encodes the hidden as MXFP8: a workgroup's work range is
+// cut at multiples of four tiles (the 32 columns of one scale block), wave 0
+// keeps the SwiGLU values of the four tiles, then takes each row's block
+// maximum across its lanes and writes codes and scale.
 #include <atomic>
 
 #include "common.h"
+#include "gemm_w4a8.h"
 #include "kernels.h"
 
 namespace moe {
@@ -93,7 +106,10 @@ struct DecodeParams {
   const uint8_t *s0, *s1;  // scales [E][N][K/32]
   const int32_t *slot;     // [E] logical -> physical weight slot, or NULL
   int n_slots;
-  void *out;               // up: bf16 h [R][N]; down: f32 y_perm [R][N]
+  void *out;               // up: bf16 h [R][N] (A8: MXFP8 codes); down: f32 y_perm [R][N]
+  const uint8_t *as;       // A8: E8M0 scales of a's rows, pitch sp
+  int sp;
+  uint8_t *out_s;          // A8 up: scales of the hidden, pitch mx8_scale_pitch(N)
   StagePlan plan;
 };
 
@@ -131,8 +147,10 @@ __device__ __forceinline__ void vm_wait_dyn(int n) {
   }
 }
 
-// KS = 128-deep K steps per wave (decode_steps(K)).
-template <bool UP, int KS>
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// KS = 128-deep K steps per wave (decode_steps(K)); A8: MXFP8 pile rows.
+template <bool UP, int KS, bool A8>
 __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   constexpr int NMAT = UP ? 2 : 1;
   constexpr int ROWS = tile_rows(UP);  // rows of each matrix per tile
@@ -175,8 +193,11 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   }
   const int W = s_gpre[E] * T;  // work items
   const int G = gridDim.x;
-  const int w_lo = (int)(((long long)blockIdx.x * W) / G);
-  const int w_hi = (int)(((long long)(blockIdx.x + 1) * W) / G);
+  // A8 up: ranges in whole quads of tiles (T % 4 == 0, so quads never
+  // straddle a group).
+  constexpr int QT = (UP && A8) ? 4 : 1;
+  const int w_lo = QT * (int)(((long long)blockIdx.x * (W / QT)) / G);
+  const int w_hi = QT * (int)(((long long)(blockIdx.x + 1) * (W / QT)) / G);
   const int n_my = w_hi - w_lo;
   if (n_my <= 0) return;
 
@@ -248,7 +269,10 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   const int bmat = UP ? (r >> 3) : 0, brow = UP ? (r & 7) : r;
   const int kb_lo = (KB * wave) / kWaves, kb_hi = (KB * (wave + 1)) / kWaves;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
-  u32x4 act[KS][4];
+  u32x4 act[A8 ? 1 : KS][4];
+  u32x4 act8[A8 ? KS : 1][2];    // A8: the two 16-B halves of each step
+  uint32_t asc[A8 ? KS : 1];     // A8: the row's scale of block 4 s + g
+  float hq[(UP && A8) ? 4 : 1][4];  // A8 up (wave 0): SwiGLU values of a quad
   int cur_group = -1, e_cur = e_first, row0 = 0, m = 0, t0 = 0;
 
   for (int i = 0; i < n_my; ++i) {
@@ -269,13 +293,26 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
       const int t = t0 + r;
       const bool tv = t < m;
       const int arow = tv ? (p.perm ? p.perm[row0 + t] : row0 + t) : 0;
-      const uint16_t *ap = p.a + (size_t)arow * K;
+      if constexpr (A8) {
+        const uint8_t *ap = (const uint8_t *)p.a + (size_t)arow * K;
+        const uint8_t *sp = p.as + (size_t)arow * p.sp;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int b = kb_lo + 4 * s + g;
-        const bool ok = tv && b < kb_hi;
+        for (int s = 0; s < KS; ++s) {
+          const int wb = kb_lo + 4 * s;  // first block of the step
+          const int blo = wb + (g >> 1), bhi = wb + 2 + (g >> 1);
+          act8[s][0] = (tv && blo < kb_hi) ? *(const u32x4 *)(ap + wb * 32 + 16 * g) : z4;
+          act8[s][1] = (tv && bhi < kb_hi) ? *(const u32x4 *)(ap + wb * 32 + 64 + 16 * g) : z4;
+          asc[s] = (tv && wb + g < kb_hi) ? (uint32_t)sp[wb + g] : 127u;
+        }
+      } else {
+        const uint16_t *ap = p.a + (size_t)arow * K;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) act[s][q] = ok ? *(const u32x4 *)(ap + b * 32 + q * 8) : z4;
+        for (int s = 0; s < KS; ++s) {
+          const int b = kb_lo + 4 * s + g;
+          const bool ok = tv && b < kb_hi;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) act[s][q] = ok ? *(const u32x4 *)(ap + b * 32 + q * 8) : z4;
+        }
       }
       vm_wait<0>();
     }
@@ -290,6 +327,17 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
       const int b = kb_lo + 4 * s + g;
       const bool bv = b < kb_hi;
       const u32x4 codes = bv ? *(const u32x4 *)(lw + brow * rowb + b * 16) : z4;
+      if constexpr (A8) {
+        // a block past this wave's range has zero codes; its scale byte is
+        // replaced by 1.0 so that no NaN can enter
+        const int wsb = bv ? (int)ls[brow * KB + b] : 127;
+        const v8i av = {(int)act8[s][0].x, (int)act8[s][0].y, (int)act8[s][0].z, (int)act8[s][0].w,
+                        (int)act8[s][1].x, (int)act8[s][1].y, (int)act8[s][1].z, (int)act8[s][1].w};
+        const v8i bw = {(int)codes.x, (int)codes.y, (int)codes.z, (int)codes.w, 0, 0, 0, 0};
+        acc2[s & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw, acc2[s & 1], 0, 4, 0,
+                                                                       (int)asc[s], 0, wsb);
+        continue;
+      }
       const float sc = bv ? e8m0_to_f32(ls[brow * KB + b]) : 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -321,6 +369,40 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
       // partner column c + 8 is summed from the LDS partials of lane l + 8.
       const f32x4 u = UP ? column_sum(lane ^ 8) : v;
       // 16x16 output: lane l holds pile rows t0 + (l / 16) * 4 + i, column l % 16.
+      if constexpr (UP && A8) {
+        // MXFP8 hidden: columns quad * 32 + sub * 8 + r (r < 8) of each row;
+        // the block maximum is taken over the four tiles here and over the
+        // eight lanes r = 0..7 of the row's lane group.
+        const int sub = tile & 3;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) hq[sub][ii] = silu(v[ii]) * u[ii];
+        if (sub == 3) {
+          const int quad = tile >> 2, spo = mx8_scale_pitch_dev(N);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            float am = fmaxf(fmaxf(fabsf(hq[0][ii]), fabsf(hq[1][ii])),
+                             fmaxf(fabsf(hq[2][ii]), fabsf(hq[3][ii])));
+            am = fmaxf(am, __shfl_xor(am, 1, 64));
+            am = fmaxf(am, __shfl_xor(am, 2, 64));
+            am = fmaxf(am, __shfl_xor(am, 4, 64));
+            const uint32_t code = mx8_scale_code(am);
+            const float vv[4] = {hq[0][ii], hq[1][ii], hq[2][ii], hq[3][ii]};
+            const uint32_t pk = mx8_pack4(vv, mx8_inv_scale(code));
+            const int tt = t0 + (lane >> 4) * 4 + ii;
+            if (tt < m && r < 8) {
+              uint8_t *o = (uint8_t *)p.out + (size_t)(row0 + tt) * N + quad * 32 + r;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) o[8 * q] = (uint8_t)(pk >> (8 * q));
+              if (r == 0) {
+                uint8_t *os = p.out_s + (size_t)(row0 + tt) * spo;
+                os[quad] = (uint8_t)code;
+                if (quad == N / 32 - 1)  // the row's padding scale bytes are 0
+                  for (int b = N / 32; b < spo; ++b) os[b] = 0;
+              }
+            }
+          }
+        }
+      } else {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int tt = t0 + (lane >> 4) * 4 + ii;
@@ -331,6 +413,7 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
         } else {
           if (tt < m) ((float *)p.out)[(size_t)(row0 + tt) * N + tile * ROWS + r] = v[ii];
         }
+      }
       }
     }
     if (i + S < n_my) {
@@ -352,9 +435,9 @@ int cu_count() {
   return c;
 }
 
-template <bool UP, int KS>
+template <bool UP, int KS, bool A8>
 hipError_t launch_decode_ks(const DecodeParams &p, hipStream_t st) {
-  auto kern = mx_decode_kernel<UP, KS>;
+  auto kern = mx_decode_kernel<UP, KS, A8>;
   const int lds = p.plan.lds_bytes;
   if (lds > 64 * 1024) {
     // The LDS limit is raised once per device (a per-device kernel attribute).
@@ -374,19 +457,19 @@ hipError_t launch_decode_ks(const DecodeParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool UP>
+template <bool UP, bool A8>
 hipError_t launch_decode(DecodeParams p, hipStream_t st) {
   p.plan = stage_plan(p.K, UP, p.E);
   if (p.plan.stages < 1) return hipErrorInvalidValue;
   switch (decode_steps(p.K)) {
-    case 1: return launch_decode_ks<UP, 1>(p, st);
-    case 2: return launch_decode_ks<UP, 2>(p, st);
-    case 3: return launch_decode_ks<UP, 3>(p, st);
-    case 4: return launch_decode_ks<UP, 4>(p, st);
-    case 5: return launch_decode_ks<UP, 5>(p, st);
-    case 6: return launch_decode_ks<UP, 6>(p, st);
-    case 7: return launch_decode_ks<UP, 7>(p, st);
-    case 8: return launch_decode_ks<UP, 8>(p, st);
+    case 1: return launch_decode_ks<UP, 1, A8>(p, st);
+    case 2: return launch_decode_ks<UP, 2, A8>(p, st);
+    case 3: return launch_decode_ks<UP, 3, A8>(p, st);
+    case 4: return launch_decode_ks<UP, 4, A8>(p, st);
+    case 5: return launch_decode_ks<UP, 5, A8>(p, st);
+    case 6: return launch_decode_ks<UP, 6, A8>(p, st);
+    case 7: return launch_decode_ks<UP, 7, A8>(p, st);
+    case 8: return launch_decode_ks<UP, 8, A8>(p, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -416,7 +499,14 @@ hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st) {
   p.slot = a.slot;
   p.n_slots = a.n_slots;
   p.out = a.h;
-  return launch_decode<true>(p, st);
+  if (a.act_quant) {
+    const size_t rows = (size_t)(a.perm ? a.n : a.R);
+    p.as = (const uint8_t *)a.a + mx8_scale_offset(rows, a.d);
+    p.sp = mx8_scale_pitch(a.d);
+    p.out_s = (uint8_t *)a.h + mx8_scale_offset(a.R, a.d_ff);
+    return launch_decode<true, true>(p, st);
+  }
+  return launch_decode<true, false>(p, st);
 }
 
 hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st) {
@@ -432,7 +522,12 @@ hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st) {
   p.slot = a.slot;
   p.n_slots = a.n_slots;
   p.out = a.y_perm;
-  return launch_decode<false>(p, st);
+  if (a.act_quant) {
+    p.as = (const uint8_t *)a.h + mx8_scale_offset(a.R, a.d_ff);
+    p.sp = mx8_scale_pitch(a.d_ff);
+    return launch_decode<false, true>(p, st);
+  }
+  return launch_decode<false, false>(p, st);
 }
 
 }  // namespace moe

@@ -451,7 +451,7 @@ hipError_t launch_w4a8_up(const FfnArgs &a, hipStream_t st) {
   const TileChoice t = choose_tile(a, true, cand, 2, true);
   W4A8Params p = w4a8_params(a, true);
   p.n_tiles = (a.d_ff + 127) / 128;
-  return launch_w4a8_gemm(p, true, a.perm != nullptr, t.bm, st);
+  return launch_w4a8_gemm(p, true, a.perm != nullptr, t.bm, w4a8_stages(true, t.bm, a.d), st);
 }
 
 hipError_t launch_w4a8_down(const FfnArgs &a, hipStream_t st, bool *fused) {
@@ -462,7 +462,7 @@ hipError_t launch_w4a8_down(const FfnArgs &a, hipStream_t st, bool *fused) {
     p.splits = t.splits;
     p.ksplit = ((a.d_ff + 128 * t.splits - 1) / (128 * t.splits)) * 128;
     p.part = a.split_part;
-    hipError_t err = launch_w4a8_gemm(p, false, false, t.bm, st);
+    hipError_t err = launch_w4a8_gemm(p, false, false, t.bm, w4a8_stages(false, t.bm, a.d_ff), st);
     if (err != hipSuccess) return err;
     if (a.comb_y) {
       if (fused) *fused = true;
@@ -471,7 +471,7 @@ hipError_t launch_w4a8_down(const FfnArgs &a, hipStream_t st, bool *fused) {
     }
     return launch_splitk_sum(a.split_part, t.splits, a.R, a.d, a.y_perm, st);
   }
-  return launch_w4a8_gemm(p, false, false, t.bm, st);
+  return launch_w4a8_gemm(p, false, false, t.bm, w4a8_stages(false, t.bm, a.d_ff), st);
 }
 
 BigGemmParams big_params(const FfnArgs &a, bool up) {
@@ -511,12 +511,11 @@ BigGemmParams big_params(const FfnArgs &a, bool up) {
 constexpr int kDecodeMaxRows = 1024;
 
 bool use_decode(const FfnArgs &a) {
-  return a.w_dtype == 2 && !a.act_quant && a.R <= kDecodeMaxRows &&
-         decode_ffn_fits(a.d, a.d_ff, a.E);
+  return a.w_dtype == 2 && a.R <= kDecodeMaxRows && decode_ffn_fits(a.d, a.d_ff, a.E);
 }
 
 int down_split_factor(const FfnArgs &a) {
-  if (a.act_quant) return a.split_ok && a.R > 0 ? down_tile(a).splits : 1;
+  if (a.act_quant) return a.split_ok && a.R > 0 && !use_decode(a) ? down_tile(a).splits : 1;
   if (!a.split_ok || a.R == 0 || use_decode(a) || a.d % 4 ||
       !big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff))
     return 1;
@@ -525,8 +524,8 @@ int down_split_factor(const FfnArgs &a) {
 
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
-  if (a.act_quant) return launch_w4a8_up(a, st);
   if (use_decode(a)) return launch_decode_up(a, st);
+  if (a.act_quant) return launch_w4a8_up(a, st);
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d_ff;
     ffn_up_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
@@ -566,8 +565,8 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
 hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
   if (fused) *fused = false;
   if (a.R == 0) return hipSuccess;
-  if (a.act_quant) return launch_w4a8_down(a, st, fused);
   if (use_decode(a)) return launch_decode_down(a, st);
+  if (a.act_quant) return launch_w4a8_down(a, st, fused);
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d;
     ffn_down_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(

@@ -46,9 +46,9 @@ using namespace gemm;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-template <int BM_>
+template <int BM_, int NST_>
 struct T8 {
-  static constexpr int BM = BM_, BNB = 256, BK = 128;
+  static constexpr int BM = BM_, BNB = 256, BK = 128, NST = NST_;
   static constexpr int WM = BM / 2, WN = BNB / (kNW / 2);
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_BYTES = BM * 128, B_BYTES = BNB * 64, AS_BYTES = kNW * 256;
@@ -56,7 +56,9 @@ struct T8 {
   static constexpr int A_RUNS = A_BYTES / 1024 / kNW;  // 1 KB runs per wave per stage
   static constexpr int B_RUNS = B_BYTES / 1024 / kNW;
   static constexpr int RW = BM / kNW;  // activation-scale rows copied by each wave
+  static constexpr int NV = A_RUNS + B_RUNS + 1;  // copies per wave per step
   static_assert(A_RUNS >= 1 && B_RUNS >= 1 && RW <= 64, "tile shape");
+  static_assert(NST >= 2 && (NST - 2) * NV < 64, "stages");
 };
 
 // Weight-scale bytes of a tile kept in LDS: per matrix, rows x K/32 padded
@@ -72,35 +74,9 @@ __device__ __forceinline__ f32x16 mma(const v8i &w, const v8i &a, const f32x16 &
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, 4, 0, 0, sw, OPA, sa);
 }
 
-// E8M0 code of the shared exponent for a block whose largest magnitude is
-// amax: floor(log2 amax) - 8 + 127 from the float32 exponent field (0 for
-// zero and float32 subnormals, the clamp at the bottom of the range).
-__device__ __forceinline__ uint32_t mx8_scale_code(float amax) {
-  const int ef = (int)((__float_as_uint(amax) >> 23) & 255u);
-  return (uint32_t)max(ef - 8, 0);
-}
-// 2^-X for scale code c = X + 127 (c <= 247, so 254 - c is a normal exponent).
-__device__ __forceinline__ float mx8_inv_scale(uint32_t code) {
-  return __uint_as_float((254u - code) << 23);
-}
-
-// Four E4M3 codes of v[0..3] * inv (exact: a power of two), packed low to
-// high.  v_cvt_pk_fp8_f32 rounds to nearest even but turns magnitudes of
-// 464 and above into NaN, so the values are clamped to +-448 first; a value
-// in (448, 464) rounds to 448 either way, so this is the saturating
-// conversion.
-__device__ __forceinline__ uint32_t mx8_pack4(const float *v, float inv) {
-  float c[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c[i] = fminf(fmaxf(v[i] * inv, -448.f), 448.f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
-  return (uint32_t)w;
-}
-
-template <bool UP, bool GATHER, int BM>
+template <bool UP, bool GATHER, int BM, int NST>
 __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
-  using T = T8<BM>;
+  using T = T8<BM, NST>;
   constexpr int BNB = T::BNB, BK = T::BK;
   constexpr int NR = UP ? BNB / 2 : BNB;  // weight rows per matrix in the tile
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -123,27 +99,33 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
   const int sp = (KB + 3) / 4 * 4;  // activation scale pitch
 
   // ---- copy offsets ---------------------------------------------------------
-  // Activation codes: run j of wave w fills rows (kNW j + w) * 8 + lane / 8.
-  // The pile-row -> token loads are issued together (index clamped into the
-  // tile, so every load is in bounds) and awaited once.  Valid offsets are
-  // < 2^31 (checked on the host); an invalid row carries bit 31, and so does
-  // a chunk past the K range, so such lanes read zeros.
-  const int ca = dma_chunk<128>(wave, lane);
+  // Activation codes: wave w copies the 1 KB runs w * A_RUNS + j (rows
+  // 8 (w A_RUNS + j) + lane / 8).  The pile-row -> token loads are issued
+  // together (index clamped into the tile, so every load is in bounds) and
+  // awaited once.  Valid offsets are < 2^31 (checked on the host); an invalid
+  // row carries bit 31, and so does a chunk past the K range, so such lanes
+  // read zeros.  With two stages (every step waits for all copies) a run
+  // wholly past the pile's rows is not issued at all: the rows it would
+  // fill feed only outputs that are never stored.
   const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, p.a_bytes), ras = rsrc(p.as, p.as_bytes);
   uint32_t a_off[T::A_RUNS];
-  int a_src[T::A_RUNS];
+  int a_src[T::A_RUNS], a_chk[T::A_RUNS];
 #pragma unroll
   for (int j = 0; j < T::A_RUNS; ++j) {
-    const int r = (kNW * j + wave) * 8 + lane / 8;
+    const int run = wave * T::A_RUNS + j, r = run * 8 + lane / 8;
+    a_chk[j] = (lane & 7) ^ ((4 * (run & 1) + (lane >> 4)) & 7);
     a_src[j] = GATHER ? p.perm[row0 + min(r, rows - 1)] : row0 + r;
   }
   const int srow = T::RW * wave + lane;  // activation-scale row of this lane
   const int s_src = GATHER ? p.perm[row0 + min(srow, rows - 1)] : row0 + srow;
 #pragma unroll
   for (int j = 0; j < T::A_RUNS; ++j) {
-    const int r = (kNW * j + wave) * 8 + lane / 8;
-    a_off[j] = r < rows ? (uint32_t)a_src[j] * (uint32_t)K + (uint32_t)ca * 16u : kOOB;
+    const int r = (wave * T::A_RUNS + j) * 8 + lane / 8;
+    a_off[j] = r < rows ? (uint32_t)a_src[j] * (uint32_t)K + (uint32_t)a_chk[j] * 16u : kOOB;
   }
+  const int a_live = NST > 2 ? T::A_RUNS
+                             : __builtin_amdgcn_readfirstlane(
+                                   min(T::A_RUNS, max(0, (rows - wave * T::A_RUNS * 8 + 7) / 8)));
   const uint32_t as_off = (lane < T::RW && srow < rows) ? (uint32_t)s_src * (uint32_t)sp : kOOB;
 
   // Weight codes: run j of wave w fills rows (kNW j + w) * 16 + lane / 4;
@@ -166,7 +148,7 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
   // Weight scales of rows [n0, n0 + NR) over all K: one contiguous run of
   // NR * K/32 bytes per matrix (4-B aligned: checked on the host), copied
   // in 256-B pieces; bytes past the matrix read as zero.
-  uint8_t *wsc = smem + 2 * T::STAGE;
+  uint8_t *wsc = smem + NST * T::STAGE;
   const int RB = NR * KB, RBP = ws_region(NR, K);
   {
     const uint32_t base = (uint32_t)n0 * (uint32_t)KB;
@@ -185,10 +167,11 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
     uint8_t *sa = smem + stage * T::STAGE;
     uint8_t *sb = sa + T::A_BYTES;
     uint8_t *ss = sb + T::B_BYTES;
-    const uint32_t pa = (k0 + ca * 16 < kend) ? 0u : kOOB;
 #pragma unroll
     for (int j = 0; j < T::A_RUNS; ++j)
-      dma16(ra, sa + (kNW * j + wave) * 1024, (a_off[j] + (uint32_t)k0) | pa);
+      if (j < a_live)
+        dma16(ra, sa + (wave * T::A_RUNS + j) * 1024,
+              (a_off[j] + (uint32_t)k0) | ((k0 + a_chk[j] * 16 < kend) ? 0u : kOOB));
     const uint32_t pb = (k0 + cb * 32 < kend) ? 0u : kOOB;
 #pragma unroll
     for (int j = 0; j < T::B_RUNS; ++j) {
@@ -284,28 +267,34 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
         acc[tm][tn] = mma<2>(bf1[tn], af1[tm], acc[tm][tn], (int)wsc1[tn], (int)asc[tm]);
   };
 
+  // Step kt's copies are done once only the NST - 2 later steps' copies
+  // are pending (loads complete in order); it then issues step kt + NST - 1
+  // into the stage that step kt - 1 used.
   const int nk = (kend - kbeg + BK - 1) / BK;
   auto kloop = [&](auto actc) {
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt<0>();
+      wait_vmcnt<(NST - 2) * T::NV>();
       __syncthreads();
-      step(actc, kt, kt & 1, kt + 1, (kt + 1) & 1);
+      step(actc, kt, kt % NST, kt + NST - 1, (kt + NST - 1) % NST);
     }
   };
-  issue(0, 0);
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s, s);
   const int act = __builtin_amdgcn_readfirstlane(min(T::TM, max(0, (rows - wm * T::WM + 31) / 32)));
-  static_assert(T::TM == 2 || T::TM == 4, "row groups per wave");
+  static_assert(T::TM == 1 || T::TM == 2 || T::TM == 4, "row groups per wave");
   if (act == T::TM) {
     kloop(std::integral_constant<int, T::TM>{});
   } else if (act == 0) {
     kloop(std::integral_constant<int, 0>{});
-  } else if (act == 1) {
-    kloop(std::integral_constant<int, 1>{});
-  } else if constexpr (T::TM == 4) {
-    if (act == 2)
-      kloop(std::integral_constant<int, 2>{});
-    else
-      kloop(std::integral_constant<int, 3>{});
+  } else if constexpr (T::TM >= 2) {
+    if (act == 1) {
+      kloop(std::integral_constant<int, 1>{});
+    } else if constexpr (T::TM == 4) {
+      if (act == 2)
+        kloop(std::integral_constant<int, 2>{});
+      else
+        kloop(std::integral_constant<int, 3>{});
+    }
   }
   wait_vmcnt<0>();
 
@@ -360,15 +349,22 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
   }
 }
 
-template <bool UP, bool GATHER, int BM>
+// LDS of a launch: the stages and the tile's weight scales.
+template <bool UP, int BM, int NST>
+constexpr int lds_bytes(int K) {
+  using T = T8<BM, NST>;
+  return NST * T::STAGE + (UP ? 2 : 1) * ws_region(UP ? T::BNB / 2 : T::BNB, K);
+}
+constexpr int kLdsMax = 160 * 1024 - 256;  // minus the static tile slot
+
+template <bool UP, bool GATHER, int BM, int NST>
 hipError_t launch_one(const W4A8Params &p, int blocks, hipStream_t st) {
-  using T = T8<BM>;
+  using T = T8<BM, NST>;
   constexpr int NR = UP ? T::BNB / 2 : T::BNB;
-  const int lds = 2 * T::STAGE + (UP ? 2 : 1) * ws_region(NR, p.K);
-  constexpr int lds_max = 2 * T::STAGE + (UP ? 2 : 1) * ws_region(NR, kW4A8MaxK);
-  static_assert(lds_max <= 160 * 1024, "LDS budget");
-  static_assert(BM * (NR + 16) + BM * 4 <= 2 * T::STAGE, "epilogue staging fits the stages");
-  auto kern = w4a8_gemm_kernel<UP, GATHER, BM>;
+  const int lds = lds_bytes<UP, BM, NST>(p.K);
+  if (lds > kLdsMax) return hipErrorInvalidValue;
+  static_assert(BM * (NR + 16) + BM * 4 <= NST * T::STAGE, "epilogue staging fits the stages");
+  auto kern = w4a8_gemm_kernel<UP, GATHER, BM, NST>;
   // Dynamic LDS above 64 KB must be allowed once per device (at the largest
   // size any call asks for).
   static std::atomic<uint64_t> attr_done{0};
@@ -378,7 +374,7 @@ hipError_t launch_one(const W4A8Params &p, int blocks, hipStream_t st) {
   const uint64_t bit = 1ull << (dev & 63);
   if (!(attr_done.load(std::memory_order_acquire) & bit)) {
     err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              lds_max);
+                              kLdsMax);
     if (err != hipSuccess) return err;
     attr_done.fetch_or(bit, std::memory_order_release);
   }
@@ -437,16 +433,38 @@ __global__ __launch_bounds__(256) void quantize_mx8_kernel(const void *x, int ro
 
 }  // namespace
 
-hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, hipStream_t st) {
+int w4a8_stages(bool up, int bm, int K) {
+  auto fits = [](int lds) { return lds <= kLdsMax; };
+  if (bm == 256) return fits(up ? lds_bytes<true, 256, 2>(K) : lds_bytes<false, 256, 2>(K)) ? 2 : 0;
+  if (bm == 128) {
+    if (fits(up ? lds_bytes<true, 128, 4>(K) : lds_bytes<false, 128, 4>(K))) return 4;
+    if (fits(up ? lds_bytes<true, 128, 3>(K) : lds_bytes<false, 128, 3>(K))) return 3;
+    return 0;
+  }
+  if (bm == 64) return fits(up ? lds_bytes<true, 64, 4>(K) : lds_bytes<false, 64, 4>(K)) ? 4 : 0;
+  return 0;
+}
+
+hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, int nst,
+                            hipStream_t st) {
   const int m_tiles = (p.R + bm - 1) / bm + (p.E < p.R ? p.E : p.R);
   const int blocks = m_tiles * p.n_tiles * (up ? 1 : (p.splits > 1 ? p.splits : 1));
   if (p.K > kW4A8MaxK || p.K % 32) return hipErrorInvalidValue;
-  if (up && gather && bm == 256) return launch_one<true, true, 256>(p, blocks, st);
-  if (up && !gather && bm == 256) return launch_one<true, false, 256>(p, blocks, st);
-  if (up && gather && bm == 128) return launch_one<true, true, 128>(p, blocks, st);
-  if (up && !gather && bm == 128) return launch_one<true, false, 128>(p, blocks, st);
-  if (!up && bm == 256) return launch_one<false, false, 256>(p, blocks, st);
-  if (!up && bm == 128) return launch_one<false, false, 128>(p, blocks, st);
+#define MOE_W4A8(U, G, M, S) \
+  if (up == U && gather == G && bm == M && nst == S) return launch_one<U, G, M, S>(p, blocks, st);
+  MOE_W4A8(true, true, 256, 2)
+  MOE_W4A8(true, false, 256, 2)
+  MOE_W4A8(false, false, 256, 2)
+  MOE_W4A8(true, true, 128, 3)
+  MOE_W4A8(true, false, 128, 3)
+  MOE_W4A8(false, false, 128, 3)
+  MOE_W4A8(true, true, 128, 4)
+  MOE_W4A8(true, false, 128, 4)
+  MOE_W4A8(false, false, 128, 4)
+  MOE_W4A8(true, true, 64, 4)
+  MOE_W4A8(true, false, 64, 4)
+  MOE_W4A8(false, false, 64, 4)
+#undef MOE_W4A8
   return hipErrorInvalidValue;
 }
 

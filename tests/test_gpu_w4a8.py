@@ -62,12 +62,15 @@ def test_mxfp8_encoder_is_bit_exact(rows, cols, act):
 
 # Layers for the mode: K tails of 64 in both projections (d, d_ff = 64 mod
 # 128), one expert per token, a single token, several row tiles per pile.
+# Up to 1024 routed rows take the weight-streaming kernel, more the GEMM.
 W4A8_SMALL = {
     "w4a8-ragged": small("w4a8-ragged", 300, 320, 8, 2, 448, "mxfp4", 21),
     "w4a8-k1": small("w4a8-k1", 200, 256, 4, 1, 384, "mxfp4", 22),
     "w4a8-n1": small("w4a8-n1", 1, 128, 16, 4, 96, "mxfp4", 23),
     "w4a8-deep": small("w4a8-deep", 700, 192, 3, 2, 2880, "mxfp4", 24),
+    "w4a8-gemm-ragged": small("w4a8-gemm-ragged", 700, 320, 8, 2, 448, "mxfp4", 25),
 }
+STREAM_CASE, GEMM_CASE = "w4a8-ragged", "w4a8-gemm-ragged"
 
 
 def _layer(name):
@@ -106,16 +109,18 @@ def test_w4a8_forward_matches_oracle(name):
     assert np.isfinite(D.y_f64()).all()
 
 
-def test_w4a8_hidden_against_oracle():
+@pytest.mark.parametrize("name", [STREAM_CASE, GEMM_CASE])
+def test_w4a8_hidden_against_oracle(name):
     """The up projection alone: its MXFP8 hidden decodes to the oracle's
     encoded hidden up to a code flip where float32 and float64 round
-    differently (rare, one E4M3 step)."""
+    differently (rare, one E4M3 step); padding scale bytes are 0."""
     import torch
 
     from mixture_experts_layer_wave_amd import binding as B
     from mixture_experts_layer_wave_amd.device import to_device
 
-    L = _layer("w4a8-ragged")
+    say(f"[w4a8 hidden] {name}")
+    L = _layer(name)
     ref = oracle_routing(L)
     n, d, E, k, f = (L[key] for key in ("n", "d", "E", "k", "d_ff"))
     R = n * k
@@ -128,6 +133,7 @@ def test_w4a8_hidden_against_oracle():
     B.moe_expert_up(D.shape, xq, "mxfp8", perm, off, D.weights, h)
     torch.cuda.synchronize()
     hc, hs = _split_mx8(h.cpu().numpy(), R, f)
+    assert np.all(hs[:, f // 32:] == 0)
     got = oracle.decode_mxfp8(hc, hs[:, : f // 32])
     x = oracle.mxfp8_round(oracle.decode_bf16(L["x"]))
     want = np.zeros((R, f))
@@ -144,7 +150,8 @@ def test_w4a8_hidden_against_oracle():
     assert row_rel_err(got, want) <= 2 ** -3
 
 
-def test_w4a8_grouped_ffn_bf16_and_mxfp8_inputs_agree():
+@pytest.mark.parametrize("name", [STREAM_CASE, GEMM_CASE])
+def test_w4a8_grouped_ffn_bf16_and_mxfp8_inputs_agree(name):
     """moe_grouped_ffn encodes bf16 pile rows itself; handing it the same
     rows already encoded gives the same bits."""
     import torch
@@ -152,7 +159,8 @@ def test_w4a8_grouped_ffn_bf16_and_mxfp8_inputs_agree():
     from mixture_experts_layer_wave_amd import binding as B
     from mixture_experts_layer_wave_amd.device import to_device
 
-    L = _layer("w4a8-ragged")
+    say(f"[w4a8 grouped] {name}")
+    L = _layer(name)
     ref = oracle_routing(L)
     n, d, k = L["n"], L["d"], L["k"]
     R = n * k
@@ -179,7 +187,8 @@ def test_w4a8_grouped_ffn_bf16_and_mxfp8_inputs_agree():
     assert row_rel_err(y1.double().cpu().numpy(), want) <= TOL["mxfp4"]
 
 
-def test_w4a8_slots_are_bit_exact():
+@pytest.mark.parametrize("name", [STREAM_CASE, GEMM_CASE])
+def test_w4a8_slots_are_bit_exact(name):
     """Weights stored in shuffled physical slots, with the slot table,
     give the same bits as the weights in expert order."""
     import torch
@@ -187,7 +196,8 @@ def test_w4a8_slots_are_bit_exact():
     from mixture_experts_layer_wave_amd import binding as B
     from mixture_experts_layer_wave_amd.device import DeviceLayer, to_device
 
-    L = _layer("w4a8-ragged")
+    say(f"[w4a8 slots] {name}")
+    L = _layer(name)
     E = L["E"]
     A = _device(L)
     slot = np.random.default_rng(3).permutation(E).astype(np.int32)
