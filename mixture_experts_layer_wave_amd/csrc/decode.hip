@@ -50,6 +50,7 @@ namespace moe {
 namespace {
 
 constexpr int kWaves = 4;      // waves per workgroup, splitting K
+constexpr int kCopyWaves = kWaves - 1;  // waves 1.. issue the copies; wave 0 stores
 constexpr int kMaxSteps = 8;   // 128-deep K steps per wave: K <= 32 * 4 * 4 * 8 = 4096
 constexpr int kBlocksPerCu = 2;  // persistent workgroups per CU
 constexpr int kMaxStages = 8;    // LDS ring depth per workgroup
@@ -91,7 +92,7 @@ StagePlan stage_plan(int K, bool up, int E) {
   s.stages = avail > 0 ? avail / s.stage_bytes : 0;
   if (s.stages > kMaxStages) s.stages = kMaxStages;
   // Copies a wave may leave in flight: (stages - 1) tiles, < 64.
-  const int per_wave = (s.copies + kWaves - 1) / kWaves;
+  const int per_wave = (s.copies + kCopyWaves - 1) / kCopyWaves;
   while (s.stages > 1 && (s.stages - 1) * per_wave > 63) --s.stages;
   s.lds_bytes = s.stages * s.stage_bytes + kRedBytes + s.table_bytes;
   return s;
@@ -226,12 +227,17 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   // Stage layout: codes of matrix 0 [ROWS][K/2], (up) codes of matrix 1,
   // scales of matrix 0 [ROWS][K/32], (up) scales of matrix 1; each region is
   // contiguous in memory.  Copy q of a tile (regions in that order, 1 KB
-  // pieces) belongs to wave q % 4; lane l moves bytes 16 l of the piece.
+  // pieces) belongs to wave 1 + q % 3; lane l moves bytes 16 l of the piece.
+  // Wave 0 issues no copies: it writes the outputs, and its stores would
+  // otherwise sit in the same in-order counter as its copies and make its
+  // wait for a tile's copies also wait for later copies.
   const uint32_t lds_base = (uint32_t)(size_t)(lds_void *)smem;
   const uint32_t voff = lane * 16;
   const int code_pieces = (code_bytes + 1023) >> 10, scale_pieces = (scale_bytes + 1023) >> 10;
   auto issue_region = [&](const uint8_t *src, int bytes, int pieces, uint32_t lds, int q0) {
-    for (int j = (wave - q0) & (kWaves - 1); j < pieces; j += kWaves) {
+    if (wave == 0) return;
+    for (int j = ((wave - 1 - q0) % kCopyWaves + kCopyWaves) % kCopyWaves; j < pieces;
+         j += kCopyWaves) {
       const uint32_t at = (uint32_t)j << 10;
       if (at + voff < (uint32_t)bytes)
         copy16_to_lds(src + at, voff, __builtin_amdgcn_readfirstlane(lds + at));
@@ -251,7 +257,8 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   };
   // Copies this wave issues per tile.
   int my_copies = 0;
-  for (int q = wave; q < P.copies; q += kWaves) ++my_copies;
+  if (wave > 0)
+    for (int q = wave - 1; q < P.copies; q += kCopyWaves) ++my_copies;
 
   // Prologue: the first S tiles in flight.
   {
@@ -277,10 +284,9 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
 
   for (int i = 0; i < n_my; ++i) {
     const int w = w_lo + i, gidx = w / T, tile = w % T, st = i % S;
-    // This wave's copies of tile i have landed once at most the copies of
-    // the tiles issued after it are outstanding (loads and stores complete
-    // in order).
-    vm_wait_dyn(min(S - 1, n_my - 1 - i) * my_copies);
+    // A copying wave's copies of tile i have landed once at most the copies
+    // of the tiles issued after it are outstanding (they complete in order).
+    if (wave > 0) vm_wait_dyn(min(S - 1, n_my - 1 - i) * my_copies);
     if (gidx != cur_group) {
       // ---- activations of the new group (rows t0..t0+15 of the pile) ----
       // Pile rows are gathered from the token matrix when perm is given
@@ -357,8 +363,7 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
     lds_barrier();  // stage st is free; all partial sums are in LDS
 
     // ---- wave 0: fixed-order sum (w0 + w1) + (w2 + w3), epilogue ---------
-    // Its stores are issued before its next copies, so the in-order wait
-    // above covers them.
+    // Nothing in the loop waits for its stores.
     if (wave == 0) {
       auto column_sum = [&](int l) {
         return (*(const f32x4 *)(red + (0 * 64 + l) * 4) + *(const f32x4 *)(red + (1 * 64 + l) * 4)) +
