@@ -218,7 +218,7 @@ def main():
     # HBM bytes per launch of this kernel from the committed rocprofv3
     # FETCH_SIZE / WRITE_SIZE summary (null once the kernel's sources change).
     fam = "w4a8_gemm_kernel" if aq else ("mx_decode_kernel" if decode else "big_gemm_kernel")
-    traffic, src = read_traffic(name, fam)
+    traffic, src = read_traffic(name, fam, aq)
     roof["traffic"] = traffic
     roof["traffic_source"] = src
     roof["kernel"] = f"{fam}<up> (moe_expert_up)"

@@ -33,7 +33,7 @@ KERNEL_SOURCES = {
                         "csrc/common.h"],
     "w4a8_gemm_kernel": ["csrc/gemm_w4a8.hip", "csrc/gemm_w4a8.h", "csrc/gemm_common.h",
                          "csrc/common.h"],
-    "mx_decode_kernel": ["csrc/decode.hip", "csrc/common.h"],
+    "mx_decode_kernel": ["csrc/decode.hip", "csrc/gemm_w4a8.h", "csrc/common.h"],
 }
 
 
@@ -136,6 +136,7 @@ def cmd_traffic(a):
         f"| HBM bytes written per launch (scaled) | {write_b:.0f} |",
         "",
         f"workload: {a.workload}",
+        f"act_quant: {a.act_quant or 'none'}",
         f"kernel: {short_name(kname)}",
         f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
         f"sources_sha256: {sources_digest(fam)}",
@@ -144,7 +145,7 @@ def cmd_traffic(a):
     print(f"wrote {a.out}: {fetch_b + write_b:.0f} bytes per launch")
 
 
-def read_traffic(workload: str, kernel_family: str):
+def read_traffic(workload: str, kernel_family: str, act_quant: str | None = None):
     """(bytes per launch, path) from profiles/ if its sources digest still
     matches the current sources of the kernel, else (None, reason)."""
     for path in sorted(glob.glob(os.path.join(PROFILES, "*traffic*.md"))):
@@ -154,6 +155,8 @@ def read_traffic(workload: str, kernel_family: str):
                 k, _, v = line.partition(":")
                 kv[k.strip()] = v.strip()
         if kv.get("workload") != workload or kernel_family not in kv.get("kernel", ""):
+            continue
+        if kv.get("act_quant", "none") != (act_quant or "none"):
             continue
         if kv.get("sources_sha256") != sources_digest(kernel_family):
             return None, f"{os.path.relpath(path, ROOT)}: kernel sources changed since measured"
@@ -175,6 +178,7 @@ def main():
     for k in ("workload", "kernel", "fetch", "write", "copy_fetch", "copy_write", "command", "out"):
         t.add_argument("--" + k.replace("_", "-"), required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--act-quant", default=None)
     a = ap.parse_args()
     {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
 

@@ -28,3 +28,14 @@ def test_committed_traffic_profiles_parse():
         kv = dict(l.split(":", 1) for l in open(path) if l.startswith(("workload:", "kernel:", "traffic_bytes_per_launch:", "sources_sha256:")))
         assert float(kv["traffic_bytes_per_launch"]) > 0
         assert len(kv["sources_sha256"].strip()) == 64
+
+
+def test_read_traffic_keeps_the_modes_apart(tmp_path, monkeypatch):
+    monkeypatch.setattr(P, "PROFILES", str(tmp_path))
+    fam = "mx_decode_kernel"
+    good = P.sources_digest(fam)
+    tail = f"kernel: mx_decode_kernel<true, 6, true>\nsources_sha256: {good}\n"
+    (tmp_path / "a_traffic.md").write_text("workload: w1\nact_quant: mxfp8\ntraffic_bytes_per_launch: 7\n" + tail)
+    (tmp_path / "b_traffic.md").write_text("workload: w1\ntraffic_bytes_per_launch: 5\n" + tail)
+    assert P.read_traffic("w1", fam, "mxfp8")[0] == 7.0
+    assert P.read_traffic("w1", fam)[0] == 5.0
