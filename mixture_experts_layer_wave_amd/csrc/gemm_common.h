@@ -46,13 +46,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // LDS tile rows, 16-B chunks swizzled so that the 16 consecutive rows read
 // by one 16-lane pass of ds_read_b128 fall in 16 distinct groups of 4 banks:
+//   256-B rows: chunk c of row r at c ^ (r % 16)
 //   128-B rows: chunk c of row r at c ^ ((r / 2) % 8)
 //    64-B rows: chunk c of row r at c ^ ((r / 4) % 4)
 template <int ROWB>
+__device__ __forceinline__ int swz_key(int row) {
+  static_assert(ROWB == 256 || ROWB == 128 || ROWB == 64, "row bytes");
+  if constexpr (ROWB == 256) return row & 15;
+  if constexpr (ROWB == 128) return (row >> 1) & 7;
+  return (row >> 2) & 3;
+}
+template <int ROWB>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  static_assert(ROWB == 128 || ROWB == 64, "row bytes");
-  if constexpr (ROWB == 128) return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
-  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+  return row * ROWB + ((chunk ^ swz_key<ROWB>(row)) << 4);
+}
+// Global chunk that lane `lane` of the 1 KB direct-to-LDS run `run` (rows
+// run * 1024 / ROWB onwards) must fetch so that the run lands swizzled.
+template <int ROWB>
+__device__ __forceinline__ int run_chunk(int run, int lane) {
+  constexpr int CPR = ROWB / 16, RPR = 1024 / ROWB;
+  return (lane % CPR) ^ swz_key<ROWB>(run * RPR + lane / CPR);
 }
 
 // Global chunk a lane must fetch so that a 1 KB direct-to-LDS run of wave

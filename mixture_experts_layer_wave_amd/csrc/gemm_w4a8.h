@@ -45,11 +45,12 @@ struct W4A8Params {
 constexpr int kW4A8MaxK = 7168;
 
 // up: H = mx8(silu(A W1^T) * (A W3^T)); down: Yp = H W2^T.  Block tile
-// bm x 256 through an nst-stage LDS ring: (256, 2), (128, 3 or 4), (64, 4).
-// w4a8_stages gives the nst a bm takes at this K (0: none fits).  Returns
-// hipErrorInvalidValue for a combination not built or too large.
-int w4a8_stages(bool up, int bm, int K);
-hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, int nst,
+// bm x 256 with a K step of bk, two LDS stages: (bm, bk) = (256, 128) or
+// (128, 256).  w4a8_fits tells whether the tile's LDS fits at
+// this K.  Returns hipErrorInvalidValue for a combination not built or too
+// large.
+bool w4a8_fits(bool up, int bm, int bk, int K);
+hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, int bk,
                             hipStream_t st);
 
 // MXFP8 encoding of rows x cols bf16 (is_bf16) or f32 values into an

@@ -19,11 +19,13 @@
 // first operand, accumulator element i of lane l is pile row l % 32 and
 // output column (i/4)*8 + (l/32)*4 + i%4 of the 32 x 32 tile.
 //
-// Block = 8 waves (2 x 4); tile BM pile rows x 256 weight rows; K step 128
-// (two MFMA k-steps) through two LDS stages.  A stage holds BM x 128 B of
-// activation codes (128-B rows), 256 x 64 B of weight codes (64-B rows),
-// both swizzled, and the BM rows' activation scales (one 4-B word per row
-// per step), all copied by direct-to-LDS buffer loads.  The weight scales of
+// Block = 8 waves (2 x 4); tile BM pile rows x 256 weight rows; K step BK =
+// 128 or 256 (two or four MFMA k-steps) through two LDS stages.  A stage
+// holds BM x BK B of activation codes, 256 x BK/2 B of weight codes (both
+// in swizzled rows) and the BM rows' activation scales (BK/32 bytes per row
+// and step), all copied by direct-to-LDS buffer loads.  A 256-deep step
+// reads 128 contiguous bytes of each weight row, which streams from HBM
+// about a quarter faster than 64-byte pieces of as many rows.  The weight scales of
 // the tile's 256 rows over the whole K range are one contiguous run per
 // matrix and are copied once per tile.  At BM = 256 a step moves 50 KB for
 // 16.8 MFLOP (the bf16 GEMM: 64 KB for 8.4 MFLOP), and the MFMA runs at
@@ -46,18 +48,24 @@ using namespace gemm;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-template <int BM_, int NST_>
+// Tile of BM pile rows x 256 weight rows, K step BK (128 or 256: 64 or 128
+// bytes of each weight row per step), NST LDS stages.
+template <int BM_, int NST_, int BK_>
 struct T8 {
-  static constexpr int BM = BM_, BNB = 256, BK = 128, NST = NST_;
+  static constexpr int BM = BM_, BNB = 256, BK = BK_, NST = NST_;
   static constexpr int WM = BM / 2, WN = BNB / (kNW / 2);
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int A_BYTES = BM * 128, B_BYTES = BNB * 64, AS_BYTES = kNW * 256;
+  static constexpr int ROWA = BK, ROWB = BK / 2;  // LDS bytes per row and step
+  static constexpr int RPA = 1024 / ROWA, RPB = 1024 / ROWB;  // rows per 1 KB run
+  static constexpr int A_BYTES = BM * ROWA, B_BYTES = BNB * ROWB, AS_BYTES = kNW * 256;
   static constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES;
   static constexpr int A_RUNS = A_BYTES / 1024 / kNW;  // 1 KB runs per wave per stage
   static constexpr int B_RUNS = B_BYTES / 1024 / kNW;
+  static constexpr int NKK = BK / 64;                  // MFMA k-steps per K step
+  static constexpr int SB = BK / 32;                   // scale bytes per row and step
   static constexpr int RW = BM / kNW;  // activation-scale rows copied by each wave
   static constexpr int NV = A_RUNS + B_RUNS + 1;  // copies per wave per step
-  static_assert(A_RUNS >= 1 && B_RUNS >= 1 && RW <= 64, "tile shape");
+  static_assert(A_RUNS >= 1 && B_RUNS >= 1 && RW * SB <= 256, "tile shape");
   static_assert(NST >= 2 && (NST - 2) * NV < 64, "stages");
 };
 
@@ -74,10 +82,11 @@ __device__ __forceinline__ f32x16 mma(const v8i &w, const v8i &a, const f32x16 &
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, 4, 0, 0, sw, OPA, sa);
 }
 
-template <bool UP, bool GATHER, int BM, int NST>
+template <bool UP, bool GATHER, int BM, int NST, int BK_>
 __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
-  using T = T8<BM, NST>;
+  using T = T8<BM, NST, BK_>;
   constexpr int BNB = T::BNB, BK = T::BK;
+  static_assert(BK == 128 || BK == 256, "K step");
   constexpr int NR = UP ? BNB / 2 : BNB;  // weight rows per matrix in the tile
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ TileSlot s_t;
@@ -99,36 +108,43 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
   const int sp = (KB + 3) / 4 * 4;  // activation scale pitch
 
   // ---- copy offsets ---------------------------------------------------------
-  // Activation codes: wave w copies the 1 KB runs w * A_RUNS + j (rows
-  // 8 (w A_RUNS + j) + lane / 8).  The pile-row -> token loads are issued
-  // together (index clamped into the tile, so every load is in bounds) and
-  // awaited once.  Valid offsets are < 2^31 (checked on the host); an invalid
-  // row carries bit 31, and so does a chunk past the K range, so such lanes
-  // read zeros.  With two stages (every step waits for all copies) a run
-  // wholly past the pile's rows is not issued at all: the rows it would
-  // fill feed only outputs that are never stored.
+  // Activation codes: wave w copies the 1 KB runs w * A_RUNS + j (RPA rows
+  // each).  The pile-row -> token loads are issued together (index clamped
+  // into the tile, so every load is in bounds) and awaited once.  Valid
+  // offsets are < 2^31 (checked on the host); an invalid row carries bit 31,
+  // and so does a chunk past the K range, so such lanes read zeros.  With two
+  // stages (every step waits for all copies) a run wholly past the pile's
+  // rows is not issued at all: the rows it would fill feed only outputs that
+  // are never stored.
+  constexpr int CPA = T::ROWA / 16, CPB = T::ROWB / 16;  // 16-B chunks per row and step
+  constexpr int SD = T::SB / 4;                            // scale words per row and step
   const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, p.a_bytes), ras = rsrc(p.as, p.as_bytes);
   uint32_t a_off[T::A_RUNS];
   int a_src[T::A_RUNS], a_chk[T::A_RUNS];
 #pragma unroll
   for (int j = 0; j < T::A_RUNS; ++j) {
-    const int run = wave * T::A_RUNS + j, r = run * 8 + lane / 8;
-    a_chk[j] = (lane & 7) ^ ((4 * (run & 1) + (lane >> 4)) & 7);
+    const int run = wave * T::A_RUNS + j, r = run * T::RPA + lane / CPA;
+    a_chk[j] = run_chunk<T::ROWA>(run, lane);
     a_src[j] = GATHER ? p.perm[row0 + min(r, rows - 1)] : row0 + r;
   }
-  const int srow = T::RW * wave + lane;  // activation-scale row of this lane
+  // Activation scales: lane l of wave w copies word l % SD of row
+  // RW w + l / SD (lanes past the wave's RW rows read zeros).
+  const int srow = T::RW * wave + lane / SD;
   const int s_src = GATHER ? p.perm[row0 + min(srow, rows - 1)] : row0 + srow;
 #pragma unroll
   for (int j = 0; j < T::A_RUNS; ++j) {
-    const int r = (wave * T::A_RUNS + j) * 8 + lane / 8;
+    const int r = (wave * T::A_RUNS + j) * T::RPA + lane / CPA;
     a_off[j] = r < rows ? (uint32_t)a_src[j] * (uint32_t)K + (uint32_t)a_chk[j] * 16u : kOOB;
   }
-  const int a_live = NST > 2 ? T::A_RUNS
-                             : __builtin_amdgcn_readfirstlane(
-                                   min(T::A_RUNS, max(0, (rows - wave * T::A_RUNS * 8 + 7) / 8)));
-  const uint32_t as_off = (lane < T::RW && srow < rows) ? (uint32_t)s_src * (uint32_t)sp : kOOB;
+  const int a_live =
+      NST > 2 ? T::A_RUNS
+              : __builtin_amdgcn_readfirstlane(
+                    min(T::A_RUNS, max(0, (rows - wave * T::A_RUNS * T::RPA + T::RPA - 1) / T::RPA)));
+  const uint32_t as_off = (lane < T::RW * SD && srow < rows)
+                              ? (uint32_t)s_src * (uint32_t)sp + 4u * (uint32_t)(lane % SD)
+                              : kOOB;
 
-  // Weight codes: run j of wave w fills rows (kNW j + w) * 16 + lane / 4;
+  // Weight codes: run j of wave w fills rows (kNW j + w) * RPB + lane / CPB;
   // up rows [0, 128) are W1 rows n0.., rows [128, 256) the same rows of W3.
   const int pe = phys_slot(p.slot, p.n_slots, e);
   const size_t qn = (size_t)N * (K / 2), sn = (size_t)N * KB;
@@ -136,19 +152,20 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
   const __amdgpu_buffer_rsrc_t rq1 = UP ? rsrc(p.b1 + (size_t)pe * qn, (uint32_t)qn) : rq0;
   const __amdgpu_buffer_rsrc_t rs0 = rsrc(p.s0 + (size_t)pe * sn, (uint32_t)sn);
   const __amdgpu_buffer_rsrc_t rs1 = UP ? rsrc(p.s1 + (size_t)pe * sn, (uint32_t)sn) : rs0;
-  const int cb = dma_chunk<64>(wave, lane);
   uint32_t b_off[T::B_RUNS];
+  int b_chk[T::B_RUNS];
 #pragma unroll
   for (int j = 0; j < T::B_RUNS; ++j) {
-    const int br = (kNW * j + wave) * 16 + lane / 4;
+    const int run = kNW * j + wave, br = run * T::RPB + lane / CPB;
     const int n = n0 + (UP ? br % NR : br);
-    b_off[j] = n < N ? (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)cb * 16u : kOOB;
+    b_chk[j] = run_chunk<T::ROWB>(run, lane);
+    b_off[j] = n < N ? (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)b_chk[j] * 16u : kOOB;
   }
 
   // Weight scales of rows [n0, n0 + NR) over all K: one contiguous run of
   // NR * K/32 bytes per matrix (4-B aligned: checked on the host), copied
   // in 256-B pieces; bytes past the matrix read as zero.
-  uint8_t *wsc = smem + NST * T::STAGE;
+  uint8_t *wscl = smem + NST * T::STAGE;
   const int RB = NR * KB, RBP = ws_region(NR, K);
   {
     const uint32_t base = (uint32_t)n0 * (uint32_t)KB;
@@ -156,7 +173,7 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
     for (int g = 0; g < (UP ? 2 : 1); ++g)
       for (int q = wave; q < RBP / 256; q += kNW) {
         const uint32_t o = (uint32_t)q * 256u + (uint32_t)lane * 4u;
-        dma4(g ? rs1 : rs0, wsc + g * RBP + q * 256, o < (uint32_t)RB ? base + o : kOOB);
+        dma4(g ? rs1 : rs0, wscl + g * RBP + q * 256, o < (uint32_t)RB ? base + o : kOOB);
       }
   }
 
@@ -172,12 +189,11 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
       if (j < a_live)
         dma16(ra, sa + (wave * T::A_RUNS + j) * 1024,
               (a_off[j] + (uint32_t)k0) | ((k0 + a_chk[j] * 16 < kend) ? 0u : kOOB));
-    const uint32_t pb = (k0 + cb * 32 < kend) ? 0u : kOOB;
 #pragma unroll
     for (int j = 0; j < T::B_RUNS; ++j) {
-      const bool second = UP && (kNW * j + wave) * 16 >= NR;
+      const bool second = UP && (kNW * j + wave) * T::RPB >= NR;
       dma16(second ? rq1 : rq0, sb + (kNW * j + wave) * 1024,
-            (b_off[j] + (uint32_t)k0 / 2u) | pb);
+            (b_off[j] + (uint32_t)k0 / 2u) | ((k0 + b_chk[j] * 32 < kend) ? 0u : kOOB));
     }
     dma4(ras, ss + wave * 256, (as_off + (uint32_t)k0 / 32u) | (k0 < kend ? 0u : kOOB));
   };
@@ -207,64 +223,76 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
     ws_row[j] = (b >= NR ? RBP : 0) + (b % NR) * KB;
   }
 
-  // One K step: scales, then the fragments of both 64-K halves (the copies
-  // of a later step are issued between them), then the MFMAs.  ACT (a
-  // compile-time count) is the number of this wave's 32-row groups that hold
-  // pile rows; the empty groups of a ragged last row tile are neither read
-  // nor multiplied.  A wave with ACT = 0 still copies and meets every barrier.
+  // One K step: scales, then the fragments of each 64-K MFMA step (those of
+  // step kk + 1 read while step kk multiplies; the copies of a later K step
+  // are issued after the first reads).  ACT (a compile-time count) is the
+  // number of this wave's 32-row groups that hold pile rows; the empty groups
+  // of a ragged last row tile are neither read nor multiplied.  A wave with
+  // ACT = 0 still copies and meets every barrier.
   auto step = [&](auto actc, int kt, int stage, int kt_issue, int stage_issue) {
     constexpr int ACT = decltype(actc)::value;
+    constexpr int NKK = T::NKK;
     const uint8_t *sa = smem + stage * T::STAGE;
     const uint8_t *sb = sa + T::A_BYTES;
     const uint8_t *ss = sb + T::B_BYTES;
-    const int blk0 = kbeg / 32 + kt * 4 + lg;  // K block of this lane's half, first 64-K half
+    const int blk0 = kbeg / 32 + kt * T::SB + lg;  // K block of this lane's half, k-step 0
     const int kbend = (kend + 31) / 32;
-    uint32_t asc[T::TM], wsc0[T::TN], wsc1[T::TN];
-    v8i af0[T::TM], af1[T::TM], bf0[T::TN], bf1[T::TN];
+    // activation scales: word kk / 2 of the row, this half's byte moved to
+    // byte 0 (k-step kk even) or 2 (odd)
+    uint32_t asc[T::TM][SD], wsc[T::TN][NKK];
 #pragma unroll
     for (int tm = 0; tm < ACT; ++tm) {
       const int r = wm * T::WM + tm * 32 + lr;
-      asc[tm] = *(const uint32_t *)(ss + (r / T::RW) * 256 + (r % T::RW) * 4) >> (8 * lg);
+      const uint8_t *q = ss + (r / T::RW) * 256 + (r % T::RW) * T::SB;
+#pragma unroll
+      for (int w = 0; w < SD; ++w) asc[tm][w] = ((const uint32_t *)q)[w] >> (8 * lg);
     }
     if constexpr (ACT > 0) {
 #pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn) {
-        // a block past the K range multiplies zero codes; its byte (another
-        // row's) is replaced by 1.0 so that a NaN scale cannot leak in
-        wsc0[tn] = blk0 < kbend ? wsc[ws_row[tn] + blk0] : 127u;
-        wsc1[tn] = blk0 + 2 < kbend ? wsc[ws_row[tn] + blk0 + 2] : 127u;
-      }
+      for (int tn = 0; tn < T::TN; ++tn)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          // a block past the K range multiplies zero codes; its byte (another
+          // row's) is replaced by 1.0 so that a NaN scale cannot leak in
+          wsc[tn][kk] = blk0 + 2 * kk < kbend ? wscl[ws_row[tn] + blk0 + 2 * kk] : 127u;
     }
     auto frags = [&](int kk, v8i *af, v8i *bf) {
 #pragma unroll
       for (int tm = 0; tm < ACT; ++tm) {
         const int r = wm * T::WM + tm * 32 + lr;
-        const u32x4 lo = *(const u32x4 *)(sa + swz<128>(r, 4 * kk + lg));
-        const u32x4 hi = *(const u32x4 *)(sa + swz<128>(r, 4 * kk + 2 + lg));
+        const u32x4 lo = *(const u32x4 *)(sa + swz<T::ROWA>(r, 4 * kk + lg));
+        const u32x4 hi = *(const u32x4 *)(sa + swz<T::ROWA>(r, 4 * kk + 2 + lg));
         af[tm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
       if constexpr (ACT > 0) {
 #pragma unroll
         for (int tn = 0; tn < T::TN; ++tn) {
-          const u32x4 w = *(const u32x4 *)(sb + swz<64>(brow(tn), 2 * kk + lg));
+          const u32x4 w = *(const u32x4 *)(sb + swz<T::ROWB>(brow(tn), 2 * kk + lg));
           bf[tn] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
         }
       }
     };
-    frags(0, af0, bf0);
+    v8i af[2][T::TM], bf[2][T::TN];
+    frags(0, af[0], bf[0]);
     issue(kt_issue, stage_issue);
-    frags(1, af1, bf1);
 #pragma unroll
-    for (int tm = 0; tm < ACT; ++tm)
+    for (int kk = 0; kk < NKK; ++kk) {
+      if (kk + 1 < NKK) frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
 #pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn)
-        acc[tm][tn] = mma<0>(bf0[tn], af0[tm], acc[tm][tn], (int)wsc0[tn], (int)asc[tm]);
+      for (int tm = 0; tm < ACT; ++tm)
 #pragma unroll
-    for (int tm = 0; tm < ACT; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn)
-        acc[tm][tn] = mma<2>(bf1[tn], af1[tm], acc[tm][tn], (int)wsc1[tn], (int)asc[tm]);
+        for (int tn = 0; tn < T::TN; ++tn) {
+          const v8i &wv = bf[kk & 1][tn], &av = af[kk & 1][tm];
+          // past the K range the row's scale word may hold another row's
+          // bytes: 127 puts 2^0 or 2^-127 (never NaN) in the selected byte
+          const int sa = blk0 + 2 * kk < kbend ? (int)asc[tm][kk / 2] : 127;
+          if (kk & 1)
+            acc[tm][tn] = mma<2>(wv, av, acc[tm][tn], (int)wsc[tn][kk], sa);
+          else
+            acc[tm][tn] = mma<0>(wv, av, acc[tm][tn], (int)wsc[tn][kk], sa);
+        }
+    }
   };
 
   // Step kt's copies are done once only the NST - 2 later steps' copies
@@ -350,21 +378,21 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
 }
 
 // LDS of a launch: the stages and the tile's weight scales.
-template <bool UP, int BM, int NST>
+template <bool UP, int BM, int NST, int BK>
 constexpr int lds_bytes(int K) {
-  using T = T8<BM, NST>;
+  using T = T8<BM, NST, BK>;
   return NST * T::STAGE + (UP ? 2 : 1) * ws_region(UP ? T::BNB / 2 : T::BNB, K);
 }
 constexpr int kLdsMax = 160 * 1024 - 256;  // minus the static tile slot
 
-template <bool UP, bool GATHER, int BM, int NST>
+template <bool UP, bool GATHER, int BM, int NST, int BK>
 hipError_t launch_one(const W4A8Params &p, int blocks, hipStream_t st) {
-  using T = T8<BM, NST>;
+  using T = T8<BM, NST, BK>;
   constexpr int NR = UP ? T::BNB / 2 : T::BNB;
-  const int lds = lds_bytes<UP, BM, NST>(p.K);
+  const int lds = lds_bytes<UP, BM, NST, BK>(p.K);
   if (lds > kLdsMax) return hipErrorInvalidValue;
   static_assert(BM * (NR + 16) + BM * 4 <= NST * T::STAGE, "epilogue staging fits the stages");
-  auto kern = w4a8_gemm_kernel<UP, GATHER, BM, NST>;
+  auto kern = w4a8_gemm_kernel<UP, GATHER, BM, NST, BK>;
   // Dynamic LDS above 64 KB must be allowed once per device (at the largest
   // size any call asks for).
   static std::atomic<uint64_t> attr_done{0};
@@ -433,37 +461,26 @@ __global__ __launch_bounds__(256) void quantize_mx8_kernel(const void *x, int ro
 
 }  // namespace
 
-int w4a8_stages(bool up, int bm, int K) {
-  auto fits = [](int lds) { return lds <= kLdsMax; };
-  if (bm == 256) return fits(up ? lds_bytes<true, 256, 2>(K) : lds_bytes<false, 256, 2>(K)) ? 2 : 0;
-  if (bm == 128) {
-    if (fits(up ? lds_bytes<true, 128, 4>(K) : lds_bytes<false, 128, 4>(K))) return 4;
-    if (fits(up ? lds_bytes<true, 128, 3>(K) : lds_bytes<false, 128, 3>(K))) return 3;
-    return 0;
-  }
-  if (bm == 64) return fits(up ? lds_bytes<true, 64, 4>(K) : lds_bytes<false, 64, 4>(K)) ? 4 : 0;
-  return 0;
+bool w4a8_fits(bool up, int bm, int bk, int K) {
+  int lds = kLdsMax + 1;
+  if (bm == 256 && bk == 128) lds = up ? lds_bytes<true, 256, 2, 128>(K) : lds_bytes<false, 256, 2, 128>(K);
+  if (bm == 128 && bk == 256) lds = up ? lds_bytes<true, 128, 2, 256>(K) : lds_bytes<false, 128, 2, 256>(K);
+  return lds <= kLdsMax;
 }
 
-hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, int nst,
+hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, int bk,
                             hipStream_t st) {
   const int m_tiles = (p.R + bm - 1) / bm + (p.E < p.R ? p.E : p.R);
   const int blocks = m_tiles * p.n_tiles * (up ? 1 : (p.splits > 1 ? p.splits : 1));
-  if (p.K > kW4A8MaxK || p.K % 32) return hipErrorInvalidValue;
-#define MOE_W4A8(U, G, M, S) \
-  if (up == U && gather == G && bm == M && nst == S) return launch_one<U, G, M, S>(p, blocks, st);
-  MOE_W4A8(true, true, 256, 2)
-  MOE_W4A8(true, false, 256, 2)
-  MOE_W4A8(false, false, 256, 2)
-  MOE_W4A8(true, true, 128, 3)
-  MOE_W4A8(true, false, 128, 3)
-  MOE_W4A8(false, false, 128, 3)
-  MOE_W4A8(true, true, 128, 4)
-  MOE_W4A8(true, false, 128, 4)
-  MOE_W4A8(false, false, 128, 4)
-  MOE_W4A8(true, true, 64, 4)
-  MOE_W4A8(true, false, 64, 4)
-  MOE_W4A8(false, false, 64, 4)
+  if (p.K > kW4A8MaxK || p.K % 32 || !w4a8_fits(up, bm, bk, p.K)) return hipErrorInvalidValue;
+#define MOE_W4A8(U, G, M, B) \
+  if (up == U && gather == G && bm == M && bk == B) return launch_one<U, G, M, 2, B>(p, blocks, st);
+  MOE_W4A8(true, true, 256, 128)
+  MOE_W4A8(true, false, 256, 128)
+  MOE_W4A8(false, false, 256, 128)
+  MOE_W4A8(true, true, 128, 256)
+  MOE_W4A8(true, false, 128, 256)
+  MOE_W4A8(false, false, 128, 256)
 #undef MOE_W4A8
   return hipErrorInvalidValue;
 }
