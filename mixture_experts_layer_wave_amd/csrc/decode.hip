@@ -43,7 +43,7 @@
 #include <atomic>
 
 #include "common.h"
-#include "gemm_w4a8.h"
+#include "gemm_mxw.h"
 #include "kernels.h"
 
 namespace moe {

@@ -26,8 +26,16 @@
 
 #include "common.h"
 #include "gemm_big.h"
-#include "gemm_w4a8.h"
+#include "gemm_mxw.h"
 #include "kernels.h"
+
+// W4A16 tile of the GEMM with MXFP4 codes in LDS (rows x K step).
+#ifndef MOE_MXW16_BM
+#define MOE_MXW16_BM 128
+#endif
+#ifndef MOE_MXW16_BK
+#define MOE_MXW16_BK 128
+#endif
 
 namespace moe {
 namespace {
@@ -381,7 +389,7 @@ TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_
     // codes (read 1.24 times slower in the 64-byte pieces of a 128-deep
     // step) and 2 KB of scales.
     const int kstep = w4a8 ? cand[i].bk : 64;
-    if (w4a8 && !w4a8_fits(up, cand[i].bm, cand[i].bk, K)) continue;
+    if (w4a8 && !mxw_fits(up, true, cand[i].bm, cand[i].bk, K)) continue;
     const long long nk = (K + kstep - 1) / kstep;
     const int S = cand[i].splits < 1 ? 1 : cand[i].splits;
     if (S > 1 && (up || !a.split_ok || nk < 2 * S)) continue;
@@ -419,14 +427,15 @@ TileChoice down_tile(const FfnArgs &a) {
   static const TileChoice cand_w4a8[] = {{256, 256, 1, 128}, {256, 256, 2, 128},
                                          {256, 256, 3, 128}, {256, 256, 4, 128}};
   if (a.act_quant)
-    return w4a8_fits(false, 128, 256, a.d_ff) ? choose_tile(a, false, cand_w4a8_deep, 3, true)
+    return mxw_fits(false, true, 128, 256, a.d_ff) ? choose_tile(a, false, cand_w4a8_deep, 3, true)
                                               : choose_tile(a, false, cand_w4a8, 4, true);
   return a.w_dtype == 2 ? choose_tile(a, false, cand_mx, 6) : choose_tile(a, false, cand_bf16, 7);
 }
 
-// W4A8 operands: MXFP8 matrix of `rows` rows x `cols` at m.
-W4A8Params w4a8_params(const FfnArgs &a, bool up) {
-  W4A8Params p{};
+// Operands of the GEMM with MXFP4 codes in LDS: W4A8 takes MXFP8 matrices
+// (a of perm ? n : R rows, h of R rows), W4A16 bf16 rows.
+MxwParams mxw_params(const FfnArgs &a, bool up) {
+  MxwParams p{};
   p.offsets = a.offsets;
   p.slot = a.slot;
   p.n_slots = a.n_slots;
@@ -436,9 +445,13 @@ W4A8Params w4a8_params(const FfnArgs &a, bool up) {
   const int K = up ? a.d : a.d_ff;
   const uint8_t *m = (const uint8_t *)(up ? a.a : a.h);
   p.a = m;
-  p.as = m + mx8_scale_offset(rows, K);
-  p.a_bytes = (uint32_t)(rows * K);
-  p.as_bytes = (uint32_t)(rows * mx8_scale_pitch(K));
+  if (a.act_quant) {
+    p.as = m + mx8_scale_offset(rows, K);
+    p.a_bytes = (uint32_t)(rows * K);
+    p.as_bytes = (uint32_t)(rows * mx8_scale_pitch(K));
+  } else {
+    p.a_bytes = (uint32_t)(rows * K * 2);
+  }
   p.K = K;
   if (up) {
     p.perm = a.perm;
@@ -448,7 +461,7 @@ W4A8Params w4a8_params(const FfnArgs &a, bool up) {
     p.s0 = a.s1;
     p.s1 = a.s3;
     p.out = a.h;
-    p.out_s = (uint8_t *)a.h + mx8_scale_offset(a.R, a.d_ff);
+    if (a.act_quant) p.out_s = (uint8_t *)a.h + mx8_scale_offset(a.R, a.d_ff);
   } else {
     p.N = a.d;
     p.b0 = (const uint8_t *)a.w2;
@@ -458,23 +471,36 @@ W4A8Params w4a8_params(const FfnArgs &a, bool up) {
   return p;
 }
 
-hipError_t launch_w4a8_up(const FfnArgs &a, hipStream_t st) {
-  const TileChoice t = w4a8_fits(true, 128, 256, a.d) ? TileChoice{128, 256, 1, 256}
-                                                       : TileChoice{256, 256, 1, 128};
-  W4A8Params p = w4a8_params(a, true);
-  p.n_tiles = (a.d_ff + 127) / 128;
-  return launch_w4a8_gemm(p, true, a.perm != nullptr, t.bm, t.bk, st);
+// W4A16 tiles: 128 rows with 128-deep steps, or 64 rows with 256-deep steps
+// (128-byte pieces of the weight rows).
+TileChoice mxw16_tile(const FfnArgs &a, bool up) {
+  const int K = up ? a.d : a.d_ff;
+  if (mxw_fits(up, false, MOE_MXW16_BM, MOE_MXW16_BK, K))
+    return TileChoice{MOE_MXW16_BM, 256, 1, MOE_MXW16_BK};
+  return TileChoice{0, 0, 0, 0};
 }
 
-hipError_t launch_w4a8_down(const FfnArgs &a, hipStream_t st, bool *fused) {
-  const TileChoice t = down_tile(a);
-  W4A8Params p = w4a8_params(a, false);
+hipError_t launch_mxw_up(const FfnArgs &a, hipStream_t st) {
+  TileChoice t;
+  if (a.act_quant)
+    t = mxw_fits(true, true, 128, 256, a.d) ? TileChoice{128, 256, 1, 256}
+                                            : TileChoice{256, 256, 1, 128};
+  else
+    t = mxw16_tile(a, true);
+  MxwParams p = mxw_params(a, true);
+  p.n_tiles = (a.d_ff + 127) / 128;
+  return launch_mxw_gemm(p, true, a.perm != nullptr, a.act_quant, t.bm, t.bk, st);
+}
+
+hipError_t launch_mxw_down(const FfnArgs &a, hipStream_t st, bool *fused) {
+  const TileChoice t = a.act_quant ? down_tile(a) : mxw16_tile(a, false);
+  MxwParams p = mxw_params(a, false);
   p.n_tiles = (a.d + 255) / 256;
   if (t.splits > 1 && a.split_part && down_split_factor(a) > 1) {
     p.splits = t.splits;
     p.ksplit = ((a.d_ff + t.bk * t.splits - 1) / (t.bk * t.splits)) * t.bk;
     p.part = a.split_part;
-    hipError_t err = launch_w4a8_gemm(p, false, false, t.bm, t.bk, st);
+    hipError_t err = launch_mxw_gemm(p, false, false, a.act_quant, t.bm, t.bk, st);
     if (err != hipSuccess) return err;
     if (a.comb_y) {
       if (fused) *fused = true;
@@ -483,7 +509,15 @@ hipError_t launch_w4a8_down(const FfnArgs &a, hipStream_t st, bool *fused) {
     }
     return launch_splitk_sum(a.split_part, t.splits, a.R, a.d, a.y_perm, st);
   }
-  return launch_w4a8_gemm(p, false, false, t.bm, t.bk, st);
+  return launch_mxw_gemm(p, false, false, a.act_quant, t.bm, t.bk, st);
+}
+
+// Prefill of bf16 rows on MXFP4 weights: the GEMM with the codes in LDS
+// when its tile fits at this shape.
+bool use_mxw16(const FfnArgs &a, bool up) {
+  return a.w_dtype == 2 && !a.act_quant && mxw16_tile(a, up).bm > 0 &&
+         (size_t)(a.perm ? a.n : a.R) * a.d * 2 < ((size_t)1 << 31) &&
+         (size_t)a.R * a.d_ff * 2 < ((size_t)1 << 31);
 }
 
 BigGemmParams big_params(const FfnArgs &a, bool up) {
@@ -537,7 +571,7 @@ int down_split_factor(const FfnArgs &a) {
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   if (a.R == 0) return hipSuccess;
   if (use_decode(a)) return launch_decode_up(a, st);
-  if (a.act_quant) return launch_w4a8_up(a, st);
+  if (a.act_quant || use_mxw16(a, true)) return launch_mxw_up(a, st);
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d_ff;
     ffn_up_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(
@@ -578,7 +612,7 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
   if (fused) *fused = false;
   if (a.R == 0) return hipSuccess;
   if (use_decode(a)) return launch_decode_down(a, st);
-  if (a.act_quant) return launch_w4a8_down(a, st, fused);
+  if (a.act_quant || use_mxw16(a, false)) return launch_mxw_down(a, st, fused);
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d;
     ffn_down_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(

@@ -1,5 +1,5 @@
 // Device helpers shared by the grouped expert GEMMs (gemm_big.hip, bf16 and
-// MXFP4-dequantising; gemm_w4a8.hip, MXFP8 x MXFP4 on the scaled MFMA):
+// MXFP4-dequantising; gemm_mxw.hip, MXFP4 codes in LDS):
 // buffer resources and direct-to-LDS copies, the swizzled LDS row layouts,
 // the block -> (expert, row tile, column tile, K split) map and the f32
 // epilogue of the down projection.
@@ -46,13 +46,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // LDS tile rows, 16-B chunks swizzled so that the 16 consecutive rows read
 // by one 16-lane pass of ds_read_b128 fall in 16 distinct groups of 4 banks:
-//   256-B rows: chunk c of row r at c ^ (r % 16)
+//   512- and 256-B rows: chunk c of row r at c ^ (r % 16)
 //   128-B rows: chunk c of row r at c ^ ((r / 2) % 8)
 //    64-B rows: chunk c of row r at c ^ ((r / 4) % 4)
 template <int ROWB>
 __device__ __forceinline__ int swz_key(int row) {
-  static_assert(ROWB == 256 || ROWB == 128 || ROWB == 64, "row bytes");
-  if constexpr (ROWB == 256) return row & 15;
+  static_assert(ROWB == 512 || ROWB == 256 || ROWB == 128 || ROWB == 64, "row bytes");
+  if constexpr (ROWB >= 256) return row & 15;
   if constexpr (ROWB == 128) return (row >> 1) & 7;
   return (row >> 2) & 3;
 }
@@ -157,6 +157,42 @@ __device__ __forceinline__ void store_f32_tile(const f32x16 (&acc)[TM][TN], floa
           *(f32x4 *)(dst + (size_t)(row0 + r) * N + col) = v;
         }
       }
+  }
+}
+
+// SwiGLU epilogue of an up tile with bf16 output: acc[tm][j] (j < TN/2) are
+// the gate columns and acc[tm][j + TN/2] the matching value columns of the
+// tile's OC outputs.  Values are staged through LDS (8-B writes of four
+// columns) so that global stores are 16-B pieces of rows; the caller has
+// made the stages free (barrier).  out is [R][N] bf16 with N % 8 == 0.
+template <int TM, int TN, int WM, int WN, int BM, int OC>
+__device__ __forceinline__ void store_swiglu_bf16_tile(const f32x16 (&acc)[TM][TN], uint8_t *smem,
+                                                       uint16_t *out, int N, int row0, int rows,
+                                                       int n0, int wm, int wn, int lane, int tid) {
+  constexpr int PITCH = OC * 2 + 16;  // bytes per staged row (padded)
+  const int lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int r = wm * WM + tm * 32 + lr;
+#pragma unroll
+    for (int j = 0; j < TN / 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wn * (WN / 2) + j * 32 + g * 8 + lg * 4;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = silu(acc[tm][j][g * 4 + q]) * acc[tm][j + TN / 2][g * 4 + q];
+        const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *(u32x2 *)(smem + r * PITCH + col * 2) = pk;
+      }
+  }
+  __syncthreads();
+  constexpr int CH = OC / 8;  // 16-B chunks per row
+  for (int idx = tid; idx < BM * CH; idx += kNT) {
+    const int r = idx / CH, ch = idx % CH;
+    const int col = n0 + ch * 8;
+    if (r < rows && col < N)  // N % 8 == 0: a chunk is all in or all out
+      *(u32x4 *)(out + (size_t)(row0 + r) * N + col) = *(const u32x4 *)(smem + r * PITCH + ch * 16);
   }
 }
 

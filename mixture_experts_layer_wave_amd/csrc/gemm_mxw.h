@@ -1,5 +1,7 @@
-// Grouped expert GEMM on MXFP8 activations and MXFP4 weights
-// (gemm_w4a8.hip): host launch interface.
+// Grouped expert GEMM with MXFP4 weights kept as codes in LDS
+// (gemm_mxw.hip): host launch interface.  Two activation modes: MXFP8 rows
+// on the scaled MFMA (W4A8), or bf16 rows with the codes converted to bf16
+// as MFMA fragments are read (W4A16).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,9 +21,10 @@ inline size_t mx8_bytes(size_t rows, int cols) {
   return mx8_scale_offset(rows, cols) + rows * (size_t)mx8_scale_pitch(cols);
 }
 
-struct W4A8Params {
-  const uint8_t *a;         // E4M3 codes: token rows (gathered through perm) or pile rows
-  const uint8_t *as;        // their E8M0 scales, pitch mx8_scale_pitch(K)
+struct MxwParams {
+  const uint8_t *a;         // token rows (gathered through perm) or pile rows: E4M3 codes
+                            // (W4A8) or bf16 (W4A16)
+  const uint8_t *as;        // W4A8: their E8M0 scales, pitch mx8_scale_pitch(K)
   uint32_t a_bytes, as_bytes;  // bytes of the code and scale parts (< 2^31)
   const int32_t *perm;      // up: pile row -> row of a (NULL = contiguous)
   const int32_t *offsets;   // [E+1] pile boundaries (device)
@@ -30,8 +33,8 @@ struct W4A8Params {
   const uint8_t *s0, *s1;   // their E8M0 scales [E][N][K/32]
   const int32_t *slot;      // [E] logical -> physical weight slot, or NULL
   int n_slots;
-  // up: the hidden as MXFP8, codes [R][N] at out and scales [R][pitch(N)]
-  // at out_s; down: f32 [R][N] at out.
+  // up: the hidden, W4A8 as MXFP8 (codes [R][N] at out, scales
+  // [R][pitch(N)] at out_s), W4A16 as bf16 [R][N]; down: f32 [R][N] at out.
   void *out;
   uint8_t *out_s;
   // Split K (down only), as in the bf16 GEMM: block s of a tile covers K
@@ -44,14 +47,14 @@ struct W4A8Params {
 // is kept in LDS).
 constexpr int kW4A8MaxK = 7168;
 
-// up: H = mx8(silu(A W1^T) * (A W3^T)); down: Yp = H W2^T.  Block tile
-// bm x 256 with a K step of bk, two LDS stages: (bm, bk) = (256, 128) or
-// (128, 256).  w4a8_fits tells whether the tile's LDS fits at
-// this K.  Returns hipErrorInvalidValue for a combination not built or too
-// large.
-bool w4a8_fits(bool up, int bm, int bk, int K);
-hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, int bk,
-                            hipStream_t st);
+// up: H = silu(A W1^T) * (A W3^T) (W4A8: encoded as MXFP8); down: Yp =
+// H W2^T.  Block tile bm x 256 with a K step of bk, two LDS stages:
+// W4A8 (bm, bk) = (256, 128) or (128, 256); W4A16 (128, 128) or (64, 256).
+// mxw_fits tells whether the tile's LDS fits at this K.  Returns
+// hipErrorInvalidValue for a combination not built or too large.
+bool mxw_fits(bool up, bool a8, int bm, int bk, int K);
+hipError_t launch_mxw_gemm(const MxwParams &p, bool up, bool gather, bool a8, int bm, int bk,
+                           hipStream_t st);
 
 // MXFP8 encoding of rows x cols bf16 (is_bf16) or f32 values into an
 // MXFP8 matrix (codes at q, scales at q_s).

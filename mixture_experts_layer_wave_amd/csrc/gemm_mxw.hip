@@ -1,9 +1,17 @@
-// Grouped expert GEMM on the gfx950 scaled MFMA: MXFP8 activations times
-// MXFP4 weights, both kept in their stored form (the W4A8 mode of the
+// Grouped expert GEMM with the MXFP4 weights kept as E2M1 codes in LDS (the
 // expert FFN; ffn.hip states the operation and its sources).
 //
-//   up:   H[r]  = mx8(silu(A[r] . W1_e^T) * (A[r] . W3_e^T))   (MXFP8 out)
-//   down: Yp[r] = H[r] . W2_e^T                                (f32 out)
+//   up:   H[r]  = silu(A[r] . W1_e^T) * (A[r] . W3_e^T)   (W4A8: MXFP8 out,
+//                                                          W4A16: bf16 out)
+//   down: Yp[r] = H[r] . W2_e^T                            (f32 out)
+//
+// W4A8 (A8): MXFP8 activations, both operands in stored form on the scaled
+// MFMA (below).  W4A16: bf16 activations on v_mfma_f32_32x32x16_bf16; each
+// lane converts the 32 codes of one weight block from LDS with
+// v_cvt_scalef32_pk_bf16_fp4 (exact in bf16) into four 8-deep fragments,
+// lane half h taking K [32 h, 32 h + 32) of each 64-deep chunk and slice s
+// of it K [32 h + 8 s, 32 h + 8 s + 8); the activation fragments are read
+// in the same K order (any fixed order is valid when both operands agree).
 //
 // v_mfma_scale_f32_32x32x64_f8f6f4 multiplies E2M1 weight codes (first
 // operand, format 4) by E4M3 activation codes (second operand, format 0),
@@ -39,7 +47,7 @@
 #include <type_traits>
 
 #include "gemm_common.h"
-#include "gemm_w4a8.h"
+#include "gemm_mxw.h"
 
 namespace moe {
 namespace {
@@ -50,21 +58,23 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 
 // Tile of BM pile rows x 256 weight rows, K step BK (128 or 256: 64 or 128
 // bytes of each weight row per step), NST LDS stages.
-template <int BM_, int NST_, int BK_>
+template <int BM_, int NST_, int BK_, bool A8_>
 struct T8 {
   static constexpr int BM = BM_, BNB = 256, BK = BK_, NST = NST_;
+  static constexpr bool A8 = A8_;
   static constexpr int WM = BM / 2, WN = BNB / (kNW / 2);
   static constexpr int TM = WM / 32, TN = WN / 32;
-  static constexpr int ROWA = BK, ROWB = BK / 2;  // LDS bytes per row and step
+  static constexpr int EA = A8 ? 1 : 2;  // bytes per activation element
+  static constexpr int ROWA = BK * EA, ROWB = BK / 2;  // LDS bytes per row and step
   static constexpr int RPA = 1024 / ROWA, RPB = 1024 / ROWB;  // rows per 1 KB run
-  static constexpr int A_BYTES = BM * ROWA, B_BYTES = BNB * ROWB, AS_BYTES = kNW * 256;
+  static constexpr int A_BYTES = BM * ROWA, B_BYTES = BNB * ROWB, AS_BYTES = A8 ? kNW * 256 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES;
   static constexpr int A_RUNS = A_BYTES / 1024 / kNW;  // 1 KB runs per wave per stage
   static constexpr int B_RUNS = B_BYTES / 1024 / kNW;
-  static constexpr int NKK = BK / 64;                  // MFMA k-steps per K step
+  static constexpr int NKK = BK / 64;                  // 64-deep chunks per K step
   static constexpr int SB = BK / 32;                   // scale bytes per row and step
   static constexpr int RW = BM / kNW;  // activation-scale rows copied by each wave
-  static constexpr int NV = A_RUNS + B_RUNS + 1;  // copies per wave per step
+  static constexpr int NV = A_RUNS + B_RUNS + (A8 ? 1 : 0);  // copies per wave per step
   static_assert(A_RUNS >= 1 && B_RUNS >= 1 && RW * SB <= 256, "tile shape");
   static_assert(NST >= 2 && (NST - 2) * NV < 64, "stages");
 };
@@ -82,9 +92,9 @@ __device__ __forceinline__ f32x16 mma(const v8i &w, const v8i &a, const f32x16 &
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, 4, 0, 0, sw, OPA, sa);
 }
 
-template <bool UP, bool GATHER, int BM, int NST, int BK_>
-__global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
-  using T = T8<BM, NST, BK_>;
+template <bool UP, bool GATHER, int BM, int NST, int BK_, bool A8>
+__global__ __launch_bounds__(kNT, 1) void mxw_gemm_kernel(MxwParams p) {
+  using T = T8<BM, NST, BK_, A8>;
   constexpr int BNB = T::BNB, BK = T::BK;
   static_assert(BK == 128 || BK == 256, "K step");
   constexpr int NR = UP ? BNB / 2 : BNB;  // weight rows per matrix in the tile
@@ -118,6 +128,7 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
   // are never stored.
   constexpr int CPA = T::ROWA / 16, CPB = T::ROWB / 16;  // 16-B chunks per row and step
   constexpr int SD = T::SB / 4;                            // scale words per row and step
+  constexpr int EA = T::EA, EPC = 16 / EA;                 // bytes and elements per chunk
   const __amdgpu_buffer_rsrc_t ra = rsrc(p.a, p.a_bytes), ras = rsrc(p.as, p.as_bytes);
   uint32_t a_off[T::A_RUNS];
   int a_src[T::A_RUNS], a_chk[T::A_RUNS];
@@ -134,7 +145,7 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
 #pragma unroll
   for (int j = 0; j < T::A_RUNS; ++j) {
     const int r = (wave * T::A_RUNS + j) * T::RPA + lane / CPA;
-    a_off[j] = r < rows ? (uint32_t)a_src[j] * (uint32_t)K + (uint32_t)a_chk[j] * 16u : kOOB;
+    a_off[j] = r < rows ? (uint32_t)a_src[j] * (uint32_t)(K * EA) + (uint32_t)a_chk[j] * 16u : kOOB;
   }
   const int a_live =
       NST > 2 ? T::A_RUNS
@@ -188,14 +199,14 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
     for (int j = 0; j < T::A_RUNS; ++j)
       if (j < a_live)
         dma16(ra, sa + (wave * T::A_RUNS + j) * 1024,
-              (a_off[j] + (uint32_t)k0) | ((k0 + a_chk[j] * 16 < kend) ? 0u : kOOB));
+              (a_off[j] + (uint32_t)(k0 * EA)) | ((k0 + a_chk[j] * EPC < kend) ? 0u : kOOB));
 #pragma unroll
     for (int j = 0; j < T::B_RUNS; ++j) {
       const bool second = UP && (kNW * j + wave) * T::RPB >= NR;
       dma16(second ? rq1 : rq0, sb + (kNW * j + wave) * 1024,
             (b_off[j] + (uint32_t)k0 / 2u) | ((k0 + b_chk[j] * 32 < kend) ? 0u : kOOB));
     }
-    dma4(ras, ss + wave * 256, (as_off + (uint32_t)k0 / 32u) | (k0 < kend ? 0u : kOOB));
+    if constexpr (A8) dma4(ras, ss + wave * 256, (as_off + (uint32_t)k0 / 32u) | (k0 < kend ? 0u : kOOB));
   };
 
   const int wm = wave / (kNW / 2), wn = wave % (kNW / 2);
@@ -240,12 +251,14 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
     // activation scales: word kk / 2 of the row, this half's byte moved to
     // byte 0 (k-step kk even) or 2 (odd)
     uint32_t asc[T::TM][SD], wsc[T::TN][NKK];
+    if constexpr (A8) {
 #pragma unroll
-    for (int tm = 0; tm < ACT; ++tm) {
-      const int r = wm * T::WM + tm * 32 + lr;
-      const uint8_t *q = ss + (r / T::RW) * 256 + (r % T::RW) * T::SB;
+      for (int tm = 0; tm < ACT; ++tm) {
+        const int r = wm * T::WM + tm * 32 + lr;
+        const uint8_t *q = ss + (r / T::RW) * 256 + (r % T::RW) * T::SB;
 #pragma unroll
-      for (int w = 0; w < SD; ++w) asc[tm][w] = ((const uint32_t *)q)[w] >> (8 * lg);
+        for (int w = 0; w < SD; ++w) asc[tm][w] = ((const uint32_t *)q)[w] >> (8 * lg);
+      }
     }
     if constexpr (ACT > 0) {
 #pragma unroll
@@ -273,6 +286,60 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
         }
       }
     };
+    if constexpr (!A8) {
+      // W4A16: per 64-deep chunk, the lane's 32 weight codes (one block) and
+      // the four 16-B activation pieces of its K, then four bf16 MFMA slices
+      u32x4 wq[2][T::TN], aq[2][T::TM][4];
+      float wsf[T::TN][NKK];
+      if constexpr (ACT > 0) {
+#pragma unroll
+        for (int tn = 0; tn < T::TN; ++tn)
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) wsf[tn][kk] = e8m0_to_f32(wsc[tn][kk]);
+      }
+      auto frags16 = [&](int kk, u32x4 *wv, u32x4 (*av)[4]) {
+#pragma unroll
+        for (int tm = 0; tm < ACT; ++tm) {
+          const int r = wm * T::WM + tm * 32 + lr;
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl)
+            av[tm][sl] = *(const u32x4 *)(sa + swz<T::ROWA>(r, 8 * kk + 4 * lg + sl));
+        }
+        if constexpr (ACT > 0) {
+#pragma unroll
+          for (int tn = 0; tn < T::TN; ++tn)
+            wv[tn] = *(const u32x4 *)(sb + swz<T::ROWB>(brow(tn), 2 * kk + lg));
+        }
+      };
+      frags16(0, wq[0], aq[0]);
+      issue(kt_issue, stage_issue);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + 1 < NKK) frags16(kk + 1, wq[(kk + 1) & 1], aq[(kk + 1) & 1]);
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          bf16x8 wf[T::TN];
+#pragma unroll
+          for (int tn = 0; tn < T::TN; ++tn) {
+            const uint32_t word = wq[kk & 1][tn][sl];
+            const float sc = wsf[tn][kk];
+            const u32x4 u = {
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3))};
+            wf[tn] = __builtin_bit_cast(bf16x8, u);
+          }
+#pragma unroll
+          for (int tm = 0; tm < ACT; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < T::TN; ++tn)
+              acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  wf[tn], __builtin_bit_cast(bf16x8, aq[kk & 1][tm][sl]), acc[tm][tn], 0, 0, 0);
+        }
+      }
+      return;
+    }
     v8i af[2][T::TM], bf[2][T::TN];
     frags(0, af[0], bf[0]);
     issue(kt_issue, stage_issue);
@@ -330,6 +397,10 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
   if constexpr (!UP) {
     float *dst = S > 1 ? p.part + (size_t)split * p.R * N : (float *)p.out;
     store_f32_tile<T::TM, T::TN, T::WM, T::WN>(acc, dst, N, row0, rows, n0, wm, wn, lane);
+  } else if constexpr (!A8) {
+    __syncthreads();  // every wave is done reading the stages
+    store_swiglu_bf16_tile<T::TM, T::TN, T::WM, T::WN, BM, NR>(acc, smem, (uint16_t *)p.out, N,
+                                                                row0, rows, n0, wm, wn, lane, tid);
   } else {
     // MXFP8 hidden staged through LDS: codes [BM][128 + 16 pad], then one
     // 4-B word of scales per row (the tile's 128 columns are 4 blocks).
@@ -378,21 +449,22 @@ __global__ __launch_bounds__(kNT, 1) void w4a8_gemm_kernel(W4A8Params p) {
 }
 
 // LDS of a launch: the stages and the tile's weight scales.
-template <bool UP, int BM, int NST, int BK>
+template <bool UP, int BM, int NST, int BK, bool A8>
 constexpr int lds_bytes(int K) {
-  using T = T8<BM, NST, BK>;
+  using T = T8<BM, NST, BK, A8>;
   return NST * T::STAGE + (UP ? 2 : 1) * ws_region(UP ? T::BNB / 2 : T::BNB, K);
 }
 constexpr int kLdsMax = 160 * 1024 - 256;  // minus the static tile slot
 
-template <bool UP, bool GATHER, int BM, int NST, int BK>
-hipError_t launch_one(const W4A8Params &p, int blocks, hipStream_t st) {
-  using T = T8<BM, NST, BK>;
+template <bool UP, bool GATHER, int BM, int NST, int BK, bool A8>
+hipError_t launch_one(const MxwParams &p, int blocks, hipStream_t st) {
+  using T = T8<BM, NST, BK, A8>;
   constexpr int NR = UP ? T::BNB / 2 : T::BNB;
-  const int lds = lds_bytes<UP, BM, NST, BK>(p.K);
+  const int lds = lds_bytes<UP, BM, NST, BK, A8>(p.K);
   if (lds > kLdsMax) return hipErrorInvalidValue;
-  static_assert(BM * (NR + 16) + BM * 4 <= NST * T::STAGE, "epilogue staging fits the stages");
-  auto kern = w4a8_gemm_kernel<UP, GATHER, BM, NST, BK>;
+  static_assert(BM * (NR * (A8 ? 1 : 2) + 16) + BM * 4 <= NST * T::STAGE,
+                "epilogue staging fits the stages");
+  auto kern = mxw_gemm_kernel<UP, GATHER, BM, NST, BK, A8>;
   // Dynamic LDS above 64 KB must be allowed once per device (at the largest
   // size any call asks for).
   static std::atomic<uint64_t> attr_done{0};
@@ -461,27 +533,40 @@ __global__ __launch_bounds__(256) void quantize_mx8_kernel(const void *x, int ro
 
 }  // namespace
 
-bool w4a8_fits(bool up, int bm, int bk, int K) {
+bool mxw_fits(bool up, bool a8, int bm, int bk, int K) {
   int lds = kLdsMax + 1;
-  if (bm == 256 && bk == 128) lds = up ? lds_bytes<true, 256, 2, 128>(K) : lds_bytes<false, 256, 2, 128>(K);
-  if (bm == 128 && bk == 256) lds = up ? lds_bytes<true, 128, 2, 256>(K) : lds_bytes<false, 128, 2, 256>(K);
+#define MOE_MXW_LDS(A8_, M, B) \
+  if (a8 == A8_ && bm == M && bk == B) \
+    lds = up ? lds_bytes<true, M, 2, B, A8_>(K) : lds_bytes<false, M, 2, B, A8_>(K);
+  MOE_MXW_LDS(true, 256, 128)
+  MOE_MXW_LDS(true, 128, 256)
+  MOE_MXW_LDS(false, 128, 128)
+  MOE_MXW_LDS(false, 64, 256)
+#undef MOE_MXW_LDS
   return lds <= kLdsMax;
 }
 
-hipError_t launch_w4a8_gemm(const W4A8Params &p, bool up, bool gather, int bm, int bk,
-                            hipStream_t st) {
+hipError_t launch_mxw_gemm(const MxwParams &p, bool up, bool gather, bool a8, int bm, int bk,
+                           hipStream_t st) {
   const int m_tiles = (p.R + bm - 1) / bm + (p.E < p.R ? p.E : p.R);
   const int blocks = m_tiles * p.n_tiles * (up ? 1 : (p.splits > 1 ? p.splits : 1));
-  if (p.K > kW4A8MaxK || p.K % 32 || !w4a8_fits(up, bm, bk, p.K)) return hipErrorInvalidValue;
-#define MOE_W4A8(U, G, M, B) \
-  if (up == U && gather == G && bm == M && bk == B) return launch_one<U, G, M, 2, B>(p, blocks, st);
-  MOE_W4A8(true, true, 256, 128)
-  MOE_W4A8(true, false, 256, 128)
-  MOE_W4A8(false, false, 256, 128)
-  MOE_W4A8(true, true, 128, 256)
-  MOE_W4A8(true, false, 128, 256)
-  MOE_W4A8(false, false, 128, 256)
-#undef MOE_W4A8
+  if (p.K > kW4A8MaxK || p.K % 32 || !mxw_fits(up, a8, bm, bk, p.K)) return hipErrorInvalidValue;
+#define MOE_MXW(U, G, A8_, M, B)                                  \
+  if (up == U && gather == G && a8 == A8_ && bm == M && bk == B) \
+    return launch_one<U, G, M, 2, B, A8_>(p, blocks, st);
+  MOE_MXW(true, true, true, 256, 128)
+  MOE_MXW(true, false, true, 256, 128)
+  MOE_MXW(false, false, true, 256, 128)
+  MOE_MXW(true, true, true, 128, 256)
+  MOE_MXW(true, false, true, 128, 256)
+  MOE_MXW(false, false, true, 128, 256)
+  MOE_MXW(true, true, false, 128, 128)
+  MOE_MXW(true, false, false, 128, 128)
+  MOE_MXW(false, false, false, 128, 128)
+  MOE_MXW(true, true, false, 64, 256)
+  MOE_MXW(true, false, false, 64, 256)
+  MOE_MXW(false, false, false, 64, 256)
+#undef MOE_MXW
   return hipErrorInvalidValue;
 }
 

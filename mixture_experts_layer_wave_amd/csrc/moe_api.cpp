@@ -7,7 +7,7 @@
 
 #include <algorithm>
 
-#include "gemm_w4a8.h"
+#include "gemm_mxw.h"
 #include "kernels.h"
 
 namespace {
