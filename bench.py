@@ -217,7 +217,12 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     # HBM bytes per launch of this kernel from the committed rocprofv3
     # FETCH_SIZE / WRITE_SIZE summary (null once the kernel's sources change).
-    fam = "w4a8_gemm_kernel" if aq else ("mx_decode_kernel" if decode else "big_gemm_kernel")
+    if decode:
+        fam = "mx_decode_kernel"
+    elif wl.wdt == "mxfp4":
+        fam = "mxw_gemm_kernel"  # MXFP4 prefill: the GEMM with the codes in LDS
+    else:
+        fam = "big_gemm_kernel"
     traffic, src = read_traffic(name, fam, aq)
     roof["traffic"] = traffic
     roof["traffic_source"] = src

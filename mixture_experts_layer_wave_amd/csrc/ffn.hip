@@ -18,7 +18,7 @@
 //
 // W4A8 mode (MXFP4 weights with act_quant): the expert input and the hidden
 // are MXFP8 and both projections run on the scaled MFMA with the weights in
-// their stored form (gemm_w4a8.hip).  The minseoc03.com feed's review of the
+// their stored form (gemm_mxw.hip).  The minseoc03.com feed's review of the
 // vLLM paper (section "What's Next") notes that quantised weights are
 // usually widened before the arithmetic and that the widening eats the
 // gain; here neither operand is widened.

@@ -71,7 +71,7 @@ struct FfnArgs {
   const float *comb_w;
   bool comb_bf16;
   // W4A8 mode (MXFP4 weights only): a and h are MXFP8 matrices (E4M3 codes,
-  // then E8M0 scales; layout in gemm_w4a8.h) of (perm ? n : R) and R rows,
+  // then E8M0 scales; layout in gemm_mxw.h) of (perm ? n : R) and R rows,
   // and both projections run on the scaled MFMA.
   bool act_quant;
 };

@@ -31,9 +31,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "big_gemm_kernel": ["csrc/gemm_big.hip", "csrc/gemm_big.h", "csrc/gemm_common.h",
                         "csrc/common.h"],
-    "w4a8_gemm_kernel": ["csrc/gemm_w4a8.hip", "csrc/gemm_w4a8.h", "csrc/gemm_common.h",
-                         "csrc/common.h"],
-    "mx_decode_kernel": ["csrc/decode.hip", "csrc/gemm_w4a8.h", "csrc/common.h"],
+    "mxw_gemm_kernel": ["csrc/gemm_mxw.hip", "csrc/gemm_mxw.h", "csrc/gemm_common.h",
+                        "csrc/common.h"],
+    "mx_decode_kernel": ["csrc/decode.hip", "csrc/gemm_mxw.h", "csrc/common.h"],
 }
 
 
