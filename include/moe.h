@@ -187,8 +187,13 @@ int moe_router_stats(const moe_shape *s, const float *logits, const int32_t *top
  *   x / x_perm: if x_perm is not NULL, x_perm[r] = x[perm[r]] ([n*k][d],
  *           dtype act) is gathered too (the row size d * sizeof(act) must be
  *           a multiple of 4 bytes); x may be NULL when x_perm is NULL.
- *   ws / ws_bytes: unused, may be NULL / 0.
+ *   ws / ws_bytes: optional device scratch.  With at least
+ *           moe_dispatch_workspace_bytes(s) bytes (16-byte aligned) the piles
+ *           are built by many workgroups in two passes over chunks of 1024
+ *           pairs; otherwise (NULL, or too small) by one workgroup.  The
+ *           result is the same.
  * Results are deterministic (no order-dependent atomics). */
+size_t moe_dispatch_workspace_bytes(const moe_shape *s);
 int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
                  int32_t *offsets, int32_t *perm, int32_t *inv, const void *x,
                  int act, void *x_perm, void *ws, size_t ws_bytes, void *stream);

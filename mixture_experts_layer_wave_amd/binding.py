@@ -73,6 +73,8 @@ lib.moe_router_stats.restype = _I
 lib.moe_router_stats.argtypes = [_SP, _P, _P, ctypes.c_float, _P, _P, _P, _P, _SZ, _P]
 lib.moe_active_experts.restype = _I
 lib.moe_active_experts.argtypes = [_SP, _P, _P, _P, _P]
+lib.moe_dispatch_workspace_bytes.restype = _SZ
+lib.moe_dispatch_workspace_bytes.argtypes = [_SP]
 lib.moe_dispatch.restype = _I
 lib.moe_dispatch.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _I, _P, _P, _SZ, _P]
 lib.moe_grouped_ffn.restype = _I
@@ -89,7 +91,7 @@ lib.moe_forward.argtypes = [_SP, _P, _I, _P, _P, _WP, _P, _I, _P, _P, _P, _SZ, _
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_bytes", "moe_mxfp8_bytes",
            "moe_quantize_mxfp8", "moe_router_topk",
            "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_active_experts",
-           "moe_dispatch", "moe_grouped_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
+           "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_grouped_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
            "moe_forward")
 
 
@@ -170,6 +172,10 @@ def moe_router_stats(shape, logits, topk_idx, alpha, P, f, loss, ws, ws_bytes, s
     _check("moe_router_stats", lib.moe_router_stats(
         ctypes.byref(_shape(shape)), _ptr(logits), _ptr(topk_idx), float(alpha), _ptr(P), _ptr(f),
         _ptr(loss), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def moe_dispatch_workspace_bytes(shape) -> int:
+    return int(lib.moe_dispatch_workspace_bytes(ctypes.byref(_shape(shape))))
 
 
 def moe_dispatch(shape, topk_idx, counts, offsets, perm, inv, x=None, act="bf16", x_perm=None,

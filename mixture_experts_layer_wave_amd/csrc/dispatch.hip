@@ -5,8 +5,13 @@
 // out, in their original order, into that expert's input matrix; a pile can
 // be empty, and pile sizes depend on the data only.
 //
-// One workgroup does the whole job deterministically: one wave for up to 256
-// pairs (dispatch_wave in route_dev.h), else 1024 threads (dispatch_block).
+// Deterministic in all three forms: one wave for up to 256 pairs
+// (dispatch_wave in route_dev.h); one 1024-thread workgroup (dispatch_block)
+// when no scratch is given; otherwise two passes over chunks of 1024 pairs,
+// one workgroup per chunk: (1) each chunk's per-expert counts and each
+// pair's stable rank among its chunk's pairs of the same expert, (2) every
+// workgroup adds up the counts of the chunks before its own and moves its
+// pairs to offsets[e] + (pairs of e in earlier chunks) + rank.
 #include "common.h"
 #include "kernels.h"
 #include "route_dev.h"
@@ -22,6 +27,100 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(const int32_t *__restric
                                                         int32_t *__restrict__ inv) {
   extern __shared__ int smem[];
   dispatch_block<16>(idx, R, k, E, nbits, counts, offsets, perm, inv, smem);
+}
+
+// Pass 1 of the chunked dispatch: chunk b = pairs [1024 b, 1024 b + 1024).
+// A lane's rank among same-expert lanes of its wave comes from ballots on
+// the bits of the expert id; the 16 waves' counts, scanned per expert, give
+// each pair its rank in the chunk (parked in inv) and the chunk's counts
+// (hist[b][E]).
+__global__ __launch_bounds__(kDispThreads) void dispatch_chunk_rank_kernel(
+    const int32_t *__restrict__ idx, int R, int E, int nbits, int32_t *__restrict__ hist,
+    int32_t *__restrict__ inv) {
+  extern __shared__ int smem[];
+  int *s_wc = smem;                    // [16][E] per-wave counts
+  int *s_base = s_wc + kDispWaves * E;  // [16][E] first rank of (wave, expert)
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = blockIdx.x * kDispThreads + tid;
+  for (int i = tid; i < kDispWaves * E; i += kDispThreads) s_wc[i] = 0;
+  const int e = r < R ? idx[r] : -1;
+  const bool valid = e >= 0 && e < E;
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = valid && ((e >> b) & 1);
+    const uint64_t bal = __ballot(bit);
+    same &= bit ? bal : ~bal;
+  }
+  const int rank = __popcll(same & lt_mask);
+  if (valid && rank == 0) s_wc[wave * E + e] = __popcll(same);
+  __syncthreads();
+  for (int ee = tid; ee < E; ee += kDispThreads) {
+    int run = 0;
+#pragma unroll
+    for (int wv = 0; wv < kDispWaves; ++wv) {
+      s_base[wv * E + ee] = run;
+      run += s_wc[wv * E + ee];
+    }
+    hist[(size_t)blockIdx.x * E + ee] = run;
+  }
+  __syncthreads();
+  if (valid) inv[r] = s_base[wave * E + e] + rank;
+}
+
+// Pass 2: every workgroup sums the chunk counts (all chunks for the pile
+// sizes, the chunks before its own for its base), scans the sizes into
+// offsets, and moves its chunk's pairs.  Workgroup 0 writes counts and
+// offsets.
+__global__ __launch_bounds__(kDispThreads) void dispatch_chunk_move_kernel(
+    const int32_t *__restrict__ idx, int R, int k, int E, const int32_t *__restrict__ hist,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+    int32_t *__restrict__ inv) {
+  extern __shared__ int smem[];
+  int *s_tot = smem;       // [E] pile sizes
+  int *s_base = s_tot + E;  // [E] first pile row of this chunk's pairs of e
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = blockIdx.x, nb = gridDim.x;
+  for (int e = tid; e < E; e += kDispThreads) {
+    int tot = 0, pre = 0;
+    for (int c = 0; c < nb; ++c) {
+      const int h = hist[(size_t)c * E + e];
+      pre += c < b ? h : 0;
+      tot += h;
+    }
+    s_tot[e] = tot;
+    s_base[e] = pre;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += MOE_WAVE) {
+      const int e = e0 + lane;
+      const int c = e < E ? s_tot[e] : 0;
+      const int incl = wave_incl_scan(c);
+      if (e < E) {
+        const int off = carry + incl - c;
+        s_base[e] += off;
+        if (b == 0) {
+          counts[e] = c;
+          offsets[e] = off;
+        }
+      }
+      carry += __builtin_amdgcn_readlane(incl, MOE_WAVE - 1);
+    }
+    if (b == 0 && lane == 0) offsets[E] = carry;
+  }
+  __syncthreads();
+  const int r = b * kDispThreads + tid;
+  if (r < R) {
+    const int e = idx[r];
+    if (e >= 0 && e < E) {
+      const int pos = s_base[e] + inv[r];
+      perm[pos] = r / k;
+      inv[r] = pos;
+    }
+  }
 }
 
 // Small batches (n * k <= 256 pairs): one wave builds the piles in LDS
@@ -97,8 +196,28 @@ static hipError_t allow_lds(K kern, size_t lds) {
                              (int)lds);
 }
 
+size_t dispatch_scratch_bytes(int n, int k, int E) {
+  const long long R = (long long)n * k;
+  if (R <= kDispChunkMinR) return 0;
+  return (size_t)((R + kDispThreads - 1) / kDispThreads) * E * sizeof(int32_t);
+}
+
 hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *counts,
-                           int32_t *offsets, int32_t *perm, int32_t *inv, hipStream_t st) {
+                           int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *scratch,
+                           hipStream_t st) {
+  const int R = n * k;
+  if (scratch && R > kDispChunkMinR) {
+    const int nb = (R + kDispThreads - 1) / kDispThreads;
+    const size_t lds1 = sizeof(int) * 2 * (size_t)kDispWaves * E;
+    hipError_t err = allow_lds(dispatch_chunk_rank_kernel, lds1);
+    if (err != hipSuccess) return err;
+    dispatch_chunk_rank_kernel<<<nb, kDispThreads, lds1, st>>>(idx, R, E, id_bits(E), scratch, inv);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    dispatch_chunk_move_kernel<<<nb, kDispThreads, sizeof(int) * 2 * (size_t)E, st>>>(
+        idx, R, k, E, scratch, counts, offsets, perm, inv);
+    return hipGetLastError();
+  }
   if (n * k <= kDispSmallR) {
     const size_t lds_s = sizeof(int) * (2 * (size_t)E + 1 + 2 * (size_t)n * k);
     hipError_t err = allow_lds(dispatch_small_kernel, lds_s);

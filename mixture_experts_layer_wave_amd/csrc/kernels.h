@@ -22,11 +22,15 @@ hipError_t launch_router_topk(const float *part, int splits, int n, int E, int k
                               int32_t *idx, float *w, float *logits, hipStream_t st);
 
 // ---- dispatch -------------------------------------------------------------
-// Up to kDispSmallR pairs one wave builds the piles (dispatch_wave), else one
-// 1024-thread workgroup does (dispatch_block); both give the same piles.
+// Up to kDispSmallR pairs one wave builds the piles (dispatch_wave); above
+// kDispChunkMinR pairs, given scratch of dispatch_scratch_bytes(n, k, E)
+// (per-chunk counts), one workgroup per chunk of 1024 pairs in two passes;
+// else one 1024-thread workgroup (dispatch_block).  All give the same piles.
 constexpr int kDispSmallR = 256;
+constexpr int kDispChunkMinR = 1024;
+size_t dispatch_scratch_bytes(int n, int k, int E);
 hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *counts,
-                           int32_t *offsets, int32_t *perm, int32_t *inv,
+                           int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *scratch,
                            hipStream_t st);
 // Router statistics (stats.hip): P [E], f [E], loss [1]; norm is [n]
 // scratch for the per-token softmax normalisers.

@@ -19,7 +19,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct WsLayout {
-  size_t logits, idx, w, counts, offsets, perm, inv, h, yp, part, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, dscratch, h, yp, part, total;
   int splits;
 };
 
@@ -84,6 +84,7 @@ WsLayout layout(const moe_shape *s, int wdt) {
   L.offsets = take((E + 1) * 4);
   L.perm = take(R * 4);
   L.inv = take(R * 4);
+  L.dscratch = take(moe::dispatch_scratch_bytes(s->n, s->k, s->E));
   // h holds the bf16 hidden, or (W4A8) the MXFP8 hidden; yp holds the pile
   // outputs and, before them, the MXFP8 expert input of the W4A8 mode.
   size_t hb = R * (size_t)s->d_ff * (wdt == MOE_F32 ? 4 : 2);
@@ -244,11 +245,14 @@ int moe_router_stats(const moe_shape *s, const float *logits, const int32_t *top
                                              loss, (float2 *)ws, (hipStream_t)stream));
 }
 
+size_t moe_dispatch_workspace_bytes(const moe_shape *s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return align_up(moe::dispatch_scratch_bytes(s->n, s->k, s->E));
+}
+
 int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
                  int32_t *offsets, int32_t *perm, int32_t *inv, const void *x, int act,
                  void *x_perm, void *ws, size_t ws_bytes, void *stream) {
-  (void)ws;
-  (void)ws_bytes;
   int st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!topk_idx || !counts || !offsets || !perm || !inv) return MOE_ERR_NULL;
@@ -260,7 +264,12 @@ int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
     if (row_bytes % 16 == 0 && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_ALIGN;
   }
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = moe::launch_dispatch(topk_idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
+  // the chunked form when the caller's scratch holds the per-chunk counts
+  const size_t need = moe::dispatch_scratch_bytes(s->n, s->k, s->E);
+  int32_t *scratch = (need > 0 && ws && ws_bytes >= need) ? (int32_t *)ws : nullptr;
+  if (scratch && !aligned16(ws)) return MOE_ERR_ALIGN;
+  hipError_t e = moe::launch_dispatch(topk_idx, s->n, s->k, s->E, counts, offsets, perm, inv,
+                                      scratch, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (x_perm) {
     e = moe::launch_gather_rows(x, perm, x_perm, s->n * s->k, row_bytes, hs);
@@ -379,7 +388,8 @@ int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, cons
     e = moe::launch_router_topk(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt,
                                 nullptr, hs);
     if (e == hipSuccess)
-      e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv, hs);
+      e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv,
+                               (int32_t *)(base + L.dscratch), hs);
   }
   const void *a = x;
   if (e == hipSuccess && w->act_quant) {

@@ -11,7 +11,7 @@ from mixture_experts_layer_wave_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _run_dispatch(idx_np, E, x_np=None):
+def _run_dispatch(idx_np, E, x_np=None, chunked=False):
     import torch
     from mixture_experts_layer_wave_amd import binding as B
     from mixture_experts_layer_wave_amd.device import to_device
@@ -30,7 +30,12 @@ def _run_dispatch(idx_np, E, x_np=None):
         act = "f32" if x_np.dtype == np.float32 else "bf16"
         xp = torch.empty((n * k, x_np.shape[1]), dtype=x.dtype, device="cuda")
     d = 1 if x_np is None else x_np.shape[1]
-    B.moe_dispatch((n, d, E, k, 1, -1), idx, counts, offsets, perm, inv, x, act, xp)
+    shape = (n, d, E, k, 1, -1)
+    ws, ws_bytes = None, 0
+    if chunked:  # scratch for the two-pass form (used above 1024 pairs)
+        ws_bytes = B.moe_dispatch_workspace_bytes(shape)
+        ws = torch.full((max(ws_bytes, 16),), 0x5A, dtype=torch.uint8, device="cuda")
+    B.moe_dispatch(shape, idx, counts, offsets, perm, inv, x, act, xp, ws, ws_bytes)
     torch.cuda.synchronize()
     out = {key: t.cpu().numpy() for key, t in
            (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv", inv))}
@@ -44,22 +49,25 @@ def _check(got, ref):
         assert np.array_equal(got[key], ref[key]), key
 
 
+@pytest.mark.parametrize("chunked", [False, True])
 @pytest.mark.parametrize("name", list(SMALL) + list(W.WORKLOADS))
-def test_dispatch_of_routed_workloads(name):
-    say(f"[dispatch] {name}")
+def test_dispatch_of_routed_workloads(name, chunked):
+    say(f"[dispatch] {name} chunked={chunked}")
     L = layer_of(name)
     ref = oracle_routing(L)
-    got = _run_dispatch(ref["idx"], L["E"], L["x"])
+    got = _run_dispatch(ref["idx"], L["E"], L["x"], chunked)
     _check(got, ref)
     xp = got["x_perm"]
     want = L["x"][ref["perm"]]
     assert np.array_equal(xp.view(want.dtype) if xp.dtype != want.dtype else xp, want)
 
 
+@pytest.mark.parametrize("chunked", [False, True])
 @pytest.mark.parametrize("case", ["one-expert", "empty-experts", "many-chunks", "n1", "e1", "dup-slots",
-                                  "small-256", "small-dups", "small-e1024", "small-257"])
-def test_dispatch_edge_cases(case):
-    say(f"[dispatch-edge] {case}")
+                                  "small-256", "small-dups", "small-e1024", "small-257",
+                                  "chunks-1025", "chunks-2048-e1024"])
+def test_dispatch_edge_cases(case, chunked):
+    say(f"[dispatch-edge] {case} chunked={chunked}")
     rng = np.random.default_rng(sum(map(ord, case)))
     if case == "one-expert":
         E, idx = 8, np.full((3000, 1), 5)
@@ -81,10 +89,14 @@ def test_dispatch_edge_cases(case):
         E, idx = 1024, rng.integers(0, 1024, size=(25, 4))
     elif case == "small-257":  # one pair past the one-wave path
         E, idx = 16, rng.integers(0, 16, size=(257, 1))
+    elif case == "chunks-1025":  # one pair past a single chunk of the two-pass form
+        E, idx = 8, rng.integers(0, 8, size=(1025, 1))
+    elif case == "chunks-2048-e1024":  # two full chunks, most experts empty in each
+        E, idx = 1024, rng.integers(0, 1024, size=(512, 4))
     else:  # a token may list the same expert twice: still a valid grouping input
         E = 4
         idx = rng.integers(0, E, size=(1500, 3))
     idx = idx.astype(np.int32)
     ref = oracle.dispatch(idx, E)
-    got = _run_dispatch(idx, E)
+    got = _run_dispatch(idx, E, chunked=chunked)
     _check(got, ref)
