@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--act-quant", choices=["mxfp8"], default=None,
                     help="W4A8 mode of an MXFP4 layer (MXFP8 expert inputs and hidden)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one HIP graph that holds one step per weight copy "
+                         "(consecutive layers with distinct weights) instead of eager launches")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit; "
                          "run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE")
@@ -151,27 +154,52 @@ def main():
         copies.append(B.ExpertWeights(D.weights.dtype, *(B._ptr(ws[key]) for key in ("w1", "w3", "w2", "s1", "s3", "s2")),
                                       None, 0, D.weights.act_quant))
 
-    def step(i):
+    def step(i, st=stream):
         B.moe_forward(D.shape, D.x, D.act, D.wg, D.bias, copies[i % len(copies)], D.y, D.act,
-                      D.idx, D.topw, D.ws, D.ws_bytes, stream)
+                      D.idx, D.topw, D.ws, D.ws_bytes, st)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # One event per step boundary on the launch stream: the K steps run back
+    per_launch = 1
+    if args.graph:
+        # One graph holds len(copies) consecutive steps, each on its own weight
+        # copy; it is captured on a side stream and replayed on the launch stream.
+        per_launch = len(copies)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            for i in range(per_launch):
+                step(i, cap)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(per_launch):
+                    step(i, cap)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup // per_launch)):
+            graph.replay()
+        torch.cuda.synchronize()
+    launches = max(1, args.steps // per_launch)
+    steps_timed = launches * per_launch
+    # One event per launch boundary on the launch stream: the launches run back
     # to back, and the per-step spread (p10/p50/p90) comes from the same run.
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
     wall0 = time.perf_counter()
     marks[0].record(stream)
-    for i in range(args.steps):
-        step(i)
+    for i in range(launches):
+        if args.graph:
+            graph.replay()
+        else:
+            step(i)
         marks[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
-    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / steps_timed
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(launches)]) / per_launch
     pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+    log(f"[bench] {steps_timed} steps{' in graph replays' if args.graph else ''}: {ms_per_step * 1e3:.1f} us/step (wall {wall / steps_timed * 1e6:.1f} us/step)")
 
     # Routing of this batch (for the work model and the dominant-kernel loop).
     n, E, k = D.n, D.E, D.k
@@ -241,14 +269,14 @@ def main():
     value = n / (ms_per_step * 1e-3)
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "steps": steps_timed, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": (D.act if D.wdt != "mxfp4" else
                   "mxfp8 x mxfp4 (w4a8)" if aq else "bf16 (mxfp4 weights)"),
         "data": "synthetic",
         "config": {"workload": name, "n": wl.n, "d": wl.d, "E": wl.E, "k": wl.k, "d_ff": wl.d_ff,
                    "weights": wl.wdt, "activations": wl.act, "act_quant": aq,
-                   "weight_copies": len(copies),
+                   "weight_copies": len(copies), "hip_graph": bool(args.graph),
                    "layer_tflops": layer_tflops},
         "step_ms": pct,
         "roofline": roof,
