@@ -328,26 +328,33 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
     const uint8_t *lw = smem + st * P.stage_bytes + bmat * code_bytes;  // this lane's codes
     const uint8_t *ls = smem + st * P.stage_bytes + NMAT * code_bytes + bmat * scale_bytes;
     f32x4 acc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // All of the step's LDS reads first (codes and scale of each block), so
+    // that their latencies overlap, then the conversions and MFMAs.
+    u32x4 codes[KS];
+    uint32_t sbyte[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int b = kb_lo + 4 * s + g;
       const bool bv = b < kb_hi;
-      const u32x4 codes = bv ? *(const u32x4 *)(lw + brow * rowb + b * 16) : z4;
+      codes[s] = bv ? *(const u32x4 *)(lw + brow * rowb + b * 16) : z4;
+      // a block past this wave's range has zero codes; its scale byte is
+      // replaced by 1.0 so that no NaN can enter
+      sbyte[s] = bv ? (uint32_t)ls[brow * KB + b] : 127u;
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
       if constexpr (A8) {
-        // a block past this wave's range has zero codes; its scale byte is
-        // replaced by 1.0 so that no NaN can enter
-        const int wsb = bv ? (int)ls[brow * KB + b] : 127;
         const v8i av = {(int)act8[s][0].x, (int)act8[s][0].y, (int)act8[s][0].z, (int)act8[s][0].w,
                         (int)act8[s][1].x, (int)act8[s][1].y, (int)act8[s][1].z, (int)act8[s][1].w};
-        const v8i bw = {(int)codes.x, (int)codes.y, (int)codes.z, (int)codes.w, 0, 0, 0, 0};
+        const v8i bw = {(int)codes[s].x, (int)codes[s].y, (int)codes[s].z, (int)codes[s].w, 0, 0, 0, 0};
         acc2[s & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bw, acc2[s & 1], 0, 4, 0,
-                                                                       (int)asc[s], 0, wsb);
+                                                                       (int)asc[s], 0, (int)sbyte[s]);
         continue;
       }
-      const float sc = bv ? e8m0_to_f32(ls[brow * KB + b]) : 0.f;
+      const float sc = e8m0_to_f32(sbyte[s]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t wv = codes[q];
+        const uint32_t wv = codes[s][q];
         const bf16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 0);
         const bf16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 1);
         const bf16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 2);
