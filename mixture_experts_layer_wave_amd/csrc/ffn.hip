@@ -481,21 +481,24 @@ TileChoice mxw16_tile(const FfnArgs &a, bool up) {
 }
 
 hipError_t launch_mxw_up(const FfnArgs &a, hipStream_t st) {
+  MxwParams p = mxw_params(a, true);
+  p.n_tiles = (a.d_ff + 127) / 128;
+  if (!a.act_quant && mxw16_mixed_fits(true, a.d))
+    return launch_mxw16_mixed(p, true, a.perm != nullptr, st);
   TileChoice t;
   if (a.act_quant)
     t = mxw_fits(true, true, 128, 256, a.d) ? TileChoice{128, 256, 1, 256}
                                             : TileChoice{256, 256, 1, 128};
   else
     t = mxw16_tile(a, true);
-  MxwParams p = mxw_params(a, true);
-  p.n_tiles = (a.d_ff + 127) / 128;
   return launch_mxw_gemm(p, true, a.perm != nullptr, a.act_quant, t.bm, t.bk, st);
 }
 
 hipError_t launch_mxw_down(const FfnArgs &a, hipStream_t st, bool *fused) {
-  const TileChoice t = a.act_quant ? down_tile(a) : mxw16_tile(a, false);
   MxwParams p = mxw_params(a, false);
   p.n_tiles = (a.d + 255) / 256;
+  if (!a.act_quant && mxw16_mixed_fits(false, a.d_ff)) return launch_mxw16_mixed(p, false, false, st);
+  const TileChoice t = a.act_quant ? down_tile(a) : mxw16_tile(a, false);
   if (t.splits > 1 && a.split_part && down_split_factor(a) > 1) {
     p.splits = t.splits;
     p.ksplit = ((a.d_ff + t.bk * t.splits - 1) / (t.bk * t.splits)) * t.bk;

@@ -79,28 +79,31 @@ __device__ __forceinline__ int dma_chunk(int wave, int lane) {
 }
 
 // Where a block works: pile e, rows [row0, row0 + rows), column tile nt,
-// work item (tile index * S + split).  Run by wave 0; e = -1 when the block
-// has no work.  Tiles are ordered expert-major, then column tile, then row
-// tile, the S splits of a tile adjacent; the ordered list is cut into 8
-// contiguous chunks, one per XCD (block b runs on XCD b mod 8), so the
-// tiles that share an expert's weights share one L2.
+// work item (tile index * S + split), row-tile size bm.  Run by wave 0;
+// e = -1 when the block has no work.  A pile of m rows has ceil(m / bm(m))
+// row tiles, bm(m) given by the caller (a constant, or a choice by pile
+// size).  Tiles are ordered expert-major, then column tile, then row tile,
+// the S splits of a tile adjacent; the ordered list is cut into 8
+// contiguous chunks, one per XCD (block b runs on XCD b mod 8), so the tiles
+// that share an expert's weights share one L2.
 struct TileSlot {
-  int e, row0, rows, nt, item;
+  int e, row0, rows, nt, item, bm;
 };
 
-template <int BM>
-__device__ __forceinline__ void map_block(const int32_t *offsets, int E, int n_tiles, int S,
-                                          int lane, TileSlot *out) {
+template <typename RowTile>
+__device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int n_tiles, int S,
+                                             int lane, TileSlot *out, RowTile bm_of) {
   const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
   const int eb = lane * per, ee = min(E, eb + per);
   // With one expert per lane (E <= 64) its offsets are loaded once.
   const int o0 = per == 1 && eb < E ? offsets[eb] : 0;
   const int o1 = per == 1 && eb < E ? offsets[eb + 1] : 0;
+  auto tiles_of = [&](int m) { const int bm = bm_of(m); return (m + bm - 1) / bm; };
   int local = 0;
   if (per == 1)
-    local = (o1 - o0 + BM - 1) / BM;
+    local = tiles_of(o1 - o0);
   else
-    for (int x = eb; x < ee; ++x) local += (offsets[x + 1] - offsets[x] + BM - 1) / BM;
+    for (int x = eb; x < ee; ++x) local += tiles_of(offsets[x + 1] - offsets[x]);
   const int incl = wave_incl_scan(local);
   const int excl = incl - local;
   const int total = __builtin_amdgcn_readlane(incl, MOE_WAVE - 1) * n_tiles * S;
@@ -118,19 +121,26 @@ __device__ __forceinline__ void map_block(const int32_t *offsets, int E, int n_t
     for (int x = eb; x < ee; ++x) {
       const int ox = per == 1 ? o0 : offsets[x];
       const int m = (per == 1 ? o1 : offsets[x + 1]) - ox;
-      const int te = (m + BM - 1) / BM;
+      const int bm = bm_of(m), te = (m + bm - 1) / bm;
       if (L < acc + te * n_tiles) {
         const int loc = L - acc;
         const int mloc = loc % te;
         out->e = x;
         out->nt = loc / te;
-        out->row0 = ox + mloc * BM;
-        out->rows = min(BM, m - mloc * BM);
+        out->row0 = ox + mloc * bm;
+        out->rows = min(bm, m - mloc * bm);
+        out->bm = bm;
         break;
       }
       acc += te * n_tiles;
     }
   }
+}
+
+template <int BM>
+__device__ __forceinline__ void map_block(const int32_t *offsets, int E, int n_tiles, int S,
+                                          int lane, TileSlot *out) {
+  map_block_fn(offsets, E, n_tiles, S, lane, out, [](int) { return BM; });
 }
 
 // f32 stores of a block's accumulators: acc[tm][tn] of wave (wm, wn) holds

@@ -53,6 +53,11 @@ constexpr int kW4A8MaxK = 7168;
 // mxw_fits tells whether the tile's LDS fits at this K.  Returns
 // hipErrorInvalidValue for a combination not built or too large.
 bool mxw_fits(bool up, bool a8, int bm, int bk, int K);
+// W4A16 with two tile shapes in one launch: piles of at most 64 rows take a
+// 64-row tile with 256-deep steps, larger piles 128-row tiles with 128-deep
+// steps (no K split).
+bool mxw16_mixed_fits(bool up, int K);
+hipError_t launch_mxw16_mixed(const MxwParams &p, bool up, bool gather, hipStream_t st);
 hipError_t launch_mxw_gemm(const MxwParams &p, bool up, bool gather, bool a8, int bm, int bk,
                            hipStream_t st);
 

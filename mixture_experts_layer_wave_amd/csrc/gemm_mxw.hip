@@ -43,6 +43,7 @@
 // and 32 columns, shared exponent X = floor(log2 amax) - 8 read from the
 // exponent bits of the float32 amax, elements v * 2^-X (exact) converted by
 // v_cvt_pk_fp8_f32 (round to nearest even) after a clamp to +-448.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -92,27 +93,20 @@ __device__ __forceinline__ f32x16 mma(const v8i &w, const v8i &a, const f32x16 &
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, a, c, 4, 0, 0, sw, OPA, sa);
 }
 
+// One block tile (the work of a block once its tile is known).
 template <bool UP, bool GATHER, int BM, int NST, int BK_, bool A8>
-__global__ __launch_bounds__(kNT, 1) void mxw_gemm_kernel(MxwParams p) {
+__device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, uint8_t *smem,
+                                         int tid, int lane, int wave) {
   using T = T8<BM, NST, BK_, A8>;
   constexpr int BNB = T::BNB, BK = T::BK;
   static_assert(BK == 128 || BK == 256, "K step");
   constexpr int NR = UP ? BNB / 2 : BNB;  // weight rows per matrix in the tile
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  __shared__ TileSlot s_t;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N, K = p.K, KB = K / 32;
   const int S = UP ? 1 : (p.splits > 1 ? p.splits : 1);
-
-  if (wave == 0) map_block<BM>(p.offsets, p.E, p.n_tiles, S, lane, &s_t);
-  __syncthreads();
-  const int e = s_t.e;
-  if (e < 0) return;
-  const int row0 = s_t.row0, rows = s_t.rows;
-  const int n0 = s_t.nt * NR;
-  const int split = s_t.item % S;
+  const int e = t.e;
+  const int row0 = t.row0, rows = t.rows;
+  const int n0 = t.nt * NR;
+  const int split = t.item % S;
   const int kbeg = S > 1 ? split * p.ksplit : 0;
   const int kend = S > 1 ? min(K, kbeg + p.ksplit) : K;
   const int sp = (KB + 3) / 4 * 4;  // activation scale pitch
@@ -448,6 +442,41 @@ __global__ __launch_bounds__(kNT, 1) void mxw_gemm_kernel(MxwParams p) {
   }
 }
 
+template <bool UP, bool GATHER, int BM, int NST, int BK_, bool A8>
+__global__ __launch_bounds__(kNT, 1) void mxw_gemm_kernel(MxwParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ TileSlot s_t;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = UP ? 1 : (p.splits > 1 ? p.splits : 1);
+  if (wave == 0) map_block<BM>(p.offsets, p.E, p.n_tiles, S, lane, &s_t);
+  __syncthreads();
+  if (s_t.e < 0) return;
+  mxw_tile<UP, GATHER, BM, NST, BK_, A8>(p, s_t, smem, tid, lane, wave);
+}
+
+// W4A16 with two tile shapes in one launch: a pile of at most 64 rows takes
+// one 64-row tile with 256-deep steps (128-byte pieces of the weight rows,
+// which stream about a quarter faster), a larger pile 128-row tiles with
+// 128-deep steps (half the weight re-reads per row of the 64-row shape).
+constexpr int kMixedSmallRows = 64;
+template <bool UP, bool GATHER>
+__global__ __launch_bounds__(kNT, 1) void mxw16_mixed_kernel(MxwParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ TileSlot s_t;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave == 0)
+    map_block_fn(p.offsets, p.E, p.n_tiles, 1, lane, &s_t,
+                 [](int m) { return m <= kMixedSmallRows ? kMixedSmallRows : 128; });
+  __syncthreads();
+  if (s_t.e < 0) return;
+  if (s_t.bm == kMixedSmallRows)
+    mxw_tile<UP, GATHER, kMixedSmallRows, 2, 256, false>(p, s_t, smem, tid, lane, wave);
+  else
+    mxw_tile<UP, GATHER, 128, 2, 128, false>(p, s_t, smem, tid, lane, wave);
+}
+
 // LDS of a launch: the stages and the tile's weight scales.
 template <bool UP, int BM, int NST, int BK, bool A8>
 constexpr int lds_bytes(int K) {
@@ -568,6 +597,37 @@ hipError_t launch_mxw_gemm(const MxwParams &p, bool up, bool gather, bool a8, in
   MOE_MXW(false, false, false, 64, 256)
 #undef MOE_MXW
   return hipErrorInvalidValue;
+}
+
+bool mxw16_mixed_fits(bool up, int K) {
+  return mxw_fits(up, false, kMixedSmallRows, 256, K) && mxw_fits(up, false, 128, 128, K);
+}
+
+hipError_t launch_mxw16_mixed(const MxwParams &p, bool up, bool gather, hipStream_t st) {
+  if (p.K > kW4A8MaxK || p.K % 32 || !mxw16_mixed_fits(up, p.K)) return hipErrorInvalidValue;
+  const int m_tiles = (p.R + kMixedSmallRows - 1) / kMixedSmallRows + (p.E < p.R ? p.E : p.R);
+  const int blocks = m_tiles * p.n_tiles;
+  const int lds = up ? std::max(lds_bytes<true, kMixedSmallRows, 2, 256, false>(p.K),
+                                lds_bytes<true, 128, 2, 128, false>(p.K))
+                     : std::max(lds_bytes<false, kMixedSmallRows, 2, 256, false>(p.K),
+                                lds_bytes<false, 128, 2, 128, false>(p.K));
+  auto kern = up ? (gather ? mxw16_mixed_kernel<true, true> : mxw16_mixed_kernel<true, false>)
+                 : mxw16_mixed_kernel<false, false>;
+  if (!up && gather) return hipErrorInvalidValue;
+  static std::atomic<uint64_t> attr_done[3];
+  const int which = up ? (gather ? 0 : 1) : 2;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_done[which].load(std::memory_order_acquire) & bit)) {
+    err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kLdsMax);
+    if (err != hipSuccess) return err;
+    attr_done[which].fetch_or(bit, std::memory_order_release);
+  }
+  kern<<<blocks, kNT, lds, st>>>(p);
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_mx8(const void *x, bool is_bf16, int rows, int cols, uint8_t *q,

@@ -41,6 +41,8 @@ SMALL = {
     # more than 1024 routed rows: the prefill GEMM with MXFP4 codes in LDS;
     # K tails in both projections (320 and 448 are not multiples of 128)
     "mxfp4-gemm-ragged": small("mxfp4-gemm-ragged", 700, 320, 8, 2, 448, "mxfp4", 18),
+    # piles of about 25 rows on the GEMM path (the 64-row tile shape)
+    "mxfp4-gemm-small-piles": small("mxfp4-gemm-small-piles", 600, 192, 48, 2, 320, "mxfp4", 19),
     "f32-small": small("f32-small", 33, 12, 5, 2, 20, "f32", 17, act="f32"),
 }
 
