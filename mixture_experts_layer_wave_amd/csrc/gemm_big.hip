@@ -357,55 +357,43 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
       return;
     }
   }
-  if constexpr (UP || FUSE) {
-    // bf16 output staged through LDS (8-B writes of four columns) so that
-    // global stores are 16-B pieces of rows.
-    constexpr int OC = UP ? BNB / 2 : BNB;  // output columns of the tile
-    constexpr int PITCH = OC * 2 + 16;       // bytes per staged row (padded)
+  if constexpr (UP) {
+    __syncthreads();  // every wave is done reading the stages
+    store_swiglu_bf16_tile<T::TM, T::TN, T::WM, T::WN, BM, BNB / 2>(acc, smem, (uint16_t *)p.out, N,
+                                                                    row0, rows, n0, wm, wn, lane, tid);
+  } else if constexpr (FUSE) {
+    // Combine fused (one expert per token): y[token] = w(token) * row, bf16,
+    // staged through LDS (8-B writes of four columns) so that global stores
+    // are 16-B pieces of rows.
+    constexpr int OC = BNB;             // output columns of the tile
+    constexpr int PITCH = OC * 2 + 16;  // bytes per staged row (padded)
     __syncthreads();  // every wave is done reading the stages
     uint8_t *so = smem;
 #pragma unroll
     for (int tm = 0; tm < T::TM; ++tm) {
       const int r = wm * T::WM + tm * 32 + lr;
-      float scale = 1.f;
-      if constexpr (!UP) scale = p.comb_w[p.perm_out[row0 + min(r, rows - 1)]];
+      const float scale = p.comb_w[p.perm_out[row0 + min(r, rows - 1)]];
 #pragma unroll
-      for (int j = 0; j < (UP ? T::TN / 2 : T::TN); ++j) {
+      for (int j = 0; j < T::TN; ++j) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int col = (UP ? wn * (T::WN / 2) : wn * T::WN) + j * 32 + g * 8 + lg * 4;
+          const int col = wn * T::WN + j * 32 + g * 8 + lg * 4;
           float v[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if constexpr (UP)
-              v[q] = silu(acc[tm][j][g * 4 + q]) * acc[tm][j + T::TN / 2][g * 4 + q];
-            else
-              v[q] = acc[tm][j][g * 4 + q] * scale;
-          }
+          for (int q = 0; q < 4; ++q) v[q] = acc[tm][j][g * 4 + q] * scale;
           const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *(u32x2 *)(so + r * PITCH + col * 2) = pk;
         }
       }
     }
     __syncthreads();
-    constexpr int CH = OC / 8;  // 16-B chunks per row
+    constexpr int CH = OC / 8;  // 16-B chunks per row; N % 8 == 0
     for (int idx = tid; idx < BM * CH; idx += kNT) {
       const int r = idx / CH, ch = idx % CH;
       const int col = n0 + ch * 8;
-      if (r < rows && col < N) {
-        const u32x4 v = *(const u32x4 *)(so + r * PITCH + ch * 16);
-        uint16_t *dst;
-        if constexpr (UP)
-          dst = (uint16_t *)p.out + (size_t)(row0 + r) * N + col;
-        else
-          dst = (uint16_t *)p.out + (size_t)p.perm_out[row0 + r] * N + col;
-        if (col + 8 <= N) {
-          *(u32x4 *)dst = v;
-        } else {
-          const uint16_t *vs = (const uint16_t *)&v;
-          for (int t = 0; t < N - col; ++t) dst[t] = vs[t];
-        }
-      }
+      if (r < rows && col < N)
+        *(u32x4 *)((uint16_t *)p.out + (size_t)p.perm_out[row0 + r] * N + col) =
+            *(const u32x4 *)(so + r * PITCH + ch * 16);
     }
   } else {
     // f32 pile outputs.
