@@ -247,8 +247,10 @@ def main():
     # FETCH_SIZE / WRITE_SIZE summary (null once the kernel's sources change).
     if decode:
         fam = "mx_decode_kernel"
+    elif wl.wdt == "mxfp4" and aq:
+        fam = "mxw_gemm_kernel"  # W4A8 prefill: MXFP4 codes in LDS, MXFP8 activations
     elif wl.wdt == "mxfp4":
-        fam = "mxw_gemm_kernel"  # MXFP4 prefill: the GEMM with the codes in LDS
+        fam = "mxw16_mixed_kernel"  # W4A16 prefill: 64- and 128-row tiles in one launch
     else:
         fam = "big_gemm_kernel"
     traffic, src = read_traffic(name, fam, aq)

@@ -33,6 +33,8 @@ KERNEL_SOURCES = {
                         "csrc/common.h"],
     "mxw_gemm_kernel": ["csrc/gemm_mxw.hip", "csrc/gemm_mxw.h", "csrc/gemm_common.h",
                         "csrc/common.h"],
+    "mxw16_mixed_kernel": ["csrc/gemm_mxw.hip", "csrc/gemm_mxw.h", "csrc/gemm_common.h",
+                           "csrc/common.h"],
     "mx_decode_kernel": ["csrc/decode.hip", "csrc/gemm_mxw.h", "csrc/common.h"],
 }
 
