@@ -74,7 +74,7 @@ __host__ __device__ constexpr int tile_rows(bool up) { return up ? 8 : 16; }
 struct StagePlan {
   int stage_bytes;  // codes + scales of one tile (a multiple of 16)
   int copies;       // 1 KB copies per tile, all waves
-  int table_bytes;  // per-expert pile offsets and group prefix
+  int table_bytes;  // per-expert pile offsets, group prefix and weight slot
   int stages;       // LDS ring depth
   int lds_bytes;    // total per workgroup
 };
@@ -87,7 +87,7 @@ StagePlan stage_plan(int K, bool up, int E) {
   const int code_bytes = tile_rows(up) * (K / 2), scale_bytes = tile_rows(up) * (K / 32);
   s.stage_bytes = mats * (code_bytes + scale_bytes);
   s.copies = mats * ((code_bytes + 1023) / 1024 + (scale_bytes + 1023) / 1024);
-  s.table_bytes = ((2 * (E + 1) * 4) + 15) & ~15;
+  s.table_bytes = ((3 * (E + 1) * 4) + 15) & ~15;
   const int avail = kCuLds / kBlocksPerCu - kRedBytes - s.table_bytes;
   s.stages = avail > 0 ? avail / s.stage_bytes : 0;
   if (s.stages > kMaxStages) s.stages = kMaxStages;
@@ -169,9 +169,14 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   float *red = (float *)(smem + S * P.stage_bytes);  // [4 waves][64][4]
   int *s_off = (int *)((uint8_t *)red + kRedBytes);         // [E+1] pile offsets
   int *s_gpre = s_off + (E + 1);                            // [E+1] groups before expert e
+  int *s_slot = s_gpre + (E + 1);                           // [E] physical weight slot
 
   // ---- work list: groups of 16 pile rows, prefix over experts ---------------
   for (int e = tid; e <= E; e += kWaves * 64) s_off[e] = p.offsets[e];
+  // The slot table is read once here: a copying wave that loaded it from
+  // global memory per tile would wait for all of its copies in flight too
+  // (one in-order counter).
+  for (int e = tid; e < E; e += kWaves * 64) s_slot[e] = phys_slot(p.slot, p.n_slots, e);
   __syncthreads();
   {
     // Thread tid sums experts [lo, hi); a block scan gives each run's base.
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
     }
   };
   auto issue_tile = [&](int e, int tile, int st) {
-    const size_t wrow = (size_t)phys_slot(p.slot, p.n_slots, e) * N + (size_t)tile * ROWS;
+    const size_t wrow = (size_t)s_slot[e] * N + (size_t)tile * ROWS;
     const uint32_t dst = lds_base + st * P.stage_bytes;
     issue_region(p.w0 + wrow * rowb, code_bytes, code_pieces, dst, 0);
     if constexpr (UP) issue_region(p.w1 + wrow * rowb, code_bytes, code_pieces, dst + code_bytes,
@@ -341,6 +346,13 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
       // replaced by 1.0 so that no NaN can enter
       sbyte[s] = bv ? (uint32_t)ls[brow * KB + b] : 127u;
     }
+    // Once every wave holds its share of the tile in registers, stage st is
+    // refilled with tile i + S while the MFMAs and the epilogue run.
+    lds_barrier();
+    if (i + S < n_my) {
+      const int wn = w_lo + i + S;
+      issue_tile(expert_of(wn / T, e_cur), wn % T, st);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if constexpr (A8) {
@@ -367,7 +379,7 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
       }
     }
     *(f32x4 *)(red + (wave * 64 + lane) * 4) = acc2[0] + acc2[1];
-    lds_barrier();  // stage st is free; all partial sums are in LDS
+    lds_barrier();  // all partial sums are in LDS
 
     // ---- wave 0: fixed-order sum (w0 + w1) + (w2 + w3), epilogue ---------
     // Nothing in the loop waits for its stores.
@@ -427,10 +439,6 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
         }
       }
       }
-    }
-    if (i + S < n_my) {
-      const int wn = w_lo + i + S;
-      issue_tile(expert_of(wn / T, e_cur), wn % T, st);
     }
   }
 }
