@@ -346,13 +346,6 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
       // replaced by 1.0 so that no NaN can enter
       sbyte[s] = bv ? (uint32_t)ls[brow * KB + b] : 127u;
     }
-    // Once every wave holds its share of the tile in registers, stage st is
-    // refilled with tile i + S while the MFMAs and the epilogue run.
-    lds_barrier();
-    if (i + S < n_my) {
-      const int wn = w_lo + i + S;
-      issue_tile(expert_of(wn / T, e_cur), wn % T, st);
-    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if constexpr (A8) {
@@ -379,7 +372,7 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
       }
     }
     *(f32x4 *)(red + (wave * 64 + lane) * 4) = acc2[0] + acc2[1];
-    lds_barrier();  // all partial sums are in LDS
+    lds_barrier();  // stage st is free; all partial sums are in LDS
 
     // ---- wave 0: fixed-order sum (w0 + w1) + (w2 + w3), epilogue ---------
     // Nothing in the loop waits for its stores.
@@ -439,6 +432,10 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
         }
       }
       }
+    }
+    if (i + S < n_my) {
+      const int wn = w_lo + i + S;
+      issue_tile(expert_of(wn / T, e_cur), wn % T, st);
     }
   }
 }
