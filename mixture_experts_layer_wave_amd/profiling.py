@@ -6,12 +6,21 @@
         --kernel SUBSTRING --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
         --copy-bytes N --command CMD --out profiles/Y.md
 
+    python -m mixture_experts_layer_wave_amd.profiling mfma --workload NAME \
+        --kernel SUBSTRING --pmc DIR --peak-tflops P --command CMD --out profiles/Z.md
+
 `traffic` turns two counter runs (FETCH_SIZE, then WRITE_SIZE; rocprofv3
 reports KiB per dispatch) into HBM bytes per launch of one kernel.  Each
 counter is scaled by what it reads for a plain device copy of known size
 (copy bytes / counter bytes), measured in the same way.  The summary records
 a digest of the sources that define the kernel; bench.py reports the
 traffic only while those sources are unchanged.
+
+`mfma` reads one counter run (MFMA math ops, MFMA busy cycles and
+GRBM_GUI_ACTIVE, with each dispatch's start and end time) and sets the
+flops the matrix cores executed beside the kernel's algorithmic flops
+(4 R d d_ff for the up projection: routed rows only), with the average
+clock over the dispatch and the fraction of the peak at that clock.
 """
 
 from __future__ import annotations
@@ -94,6 +103,22 @@ def counter_means(path: str, counter: str):
     return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
 
 
+def dispatch_counters(path: str, substring: str):
+    """{counter: mean value per dispatch} and the mean dispatch time (ns) of
+    the one kernel whose name contains substring."""
+    acc, times, names = defaultdict(list), {}, set()
+    for r in csv.DictReader(open(_csv(path, "counter_collection.csv"))):
+        if substring not in r["Kernel_Name"]:
+            continue
+        names.add(r["Kernel_Name"])
+        acc[r["Counter_Name"]].append(float(r["Counter_Value"]))
+        times[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    if len(names) != 1:
+        raise ValueError(f"{len(names)} kernels match {substring!r}: {[short_name(k) for k in names]}")
+    means = {k: sum(v) / len(v) for k, v in acc.items()}
+    return names.pop(), means, sum(times.values()) / len(times), len(times)
+
+
 def _pick(means, substring):
     hits = [(k, v) for k, v in means.items() if substring in k]
     if len(hits) != 1:
@@ -147,6 +172,50 @@ def cmd_traffic(a):
     print(f"wrote {a.out}: {fetch_b + write_b:.0f} bytes per launch")
 
 
+# MI355X: 8 XCDs, 256 CUs of 4 SIMDs; spec clock 2.4 GHz.
+N_XCD, N_SIMD, SPEC_GHZ = 8, 1024, 2.4
+
+
+def up_flops(workload: str) -> float:
+    from mixture_experts_layer_wave_amd import workloads as W
+    wl = W.WORKLOADS[workload]
+    return 4.0 * wl.n * wl.k * wl.d * wl.d_ff
+
+
+def cmd_mfma(a):
+    kname, c, dur_ns, nd = dispatch_counters(a.pmc, a.kernel)
+    mops = sum(v for k, v in c.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+    counted = mops * 512.0
+    alg = up_flops(a.workload) if a.flops is None else a.flops
+    # GRBM_GUI_ACTIVE is summed over the XCDs: cycles of one XCD = sum / 8.
+    cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
+    ghz = cycles / dur_ns
+    busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMD)
+    achieved = alg / (dur_ns * 1e-9) / 1e12
+    peak_clk = a.peak_tflops * ghz / SPEC_GHZ
+    rows = [("dispatches averaged", f"{nd}"),
+            ("dispatch duration (us)", f"{dur_ns / 1e3:.1f}"),
+            ("algorithmic flops per launch", f"{alg:.4e}"),
+            ("MFMA flops counted (MOPS x 512)", f"{counted:.4e}"),
+            ("counted / algorithmic", f"{counted / alg:.3f}"),
+            ("achieved (algorithmic, TFLOP/s)", f"{achieved:.1f}"),
+            ("fraction of the spec peak", f"{achieved / a.peak_tflops:.3f}"),
+            ("average clock (GRBM_GUI_ACTIVE / duration, GHz)", f"{ghz:.3f}"),
+            ("peak at that clock (TFLOP/s)", f"{peak_clk:.1f}"),
+            ("fraction of the peak at that clock", f"{achieved / peak_clk:.3f}"),
+            ("MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs))", f"{busy:.3f}")]
+    rows += [(f"{k} (per dispatch)", f"{v:.4e}") for k, v in sorted(c.items())]
+    lines = [f"# MFMA counters of `{short_name(kname)}` ({a.workload})", "",
+             "Commands (one counter pass, then this summary):", "", "```", a.command, "```", "",
+             "| quantity | value |", "|---|---:|"] + [f"| {k} | {v} |" for k, v in rows]
+    lines += ["", f"workload: {a.workload}", f"act_quant: {a.act_quant or 'none'}",
+              f"kernel: {short_name(kname)}", f"spec_peak_tflops: {a.peak_tflops}",
+              f"sources_sha256: {sources_digest(family(kname))}"]
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print(f"wrote {a.out}: {achieved:.0f} TFLOP/s, clock {ghz:.2f} GHz, MFMA busy {busy:.3f}, "
+          f"counted/alg {counted / alg:.3f}")
+
+
 def read_traffic(workload: str, kernel_family: str, act_quant: str | None = None):
     """(bytes per launch, path) from profiles/ if its sources digest still
     matches the current sources of the kernel, else (None, reason)."""
@@ -181,8 +250,14 @@ def main():
         t.add_argument("--" + k.replace("_", "-"), required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--act-quant", default=None)
+    m = sub.add_parser("mfma")
+    for k in ("workload", "kernel", "pmc", "command", "out"):
+        m.add_argument("--" + k, required=True)
+    m.add_argument("--peak-tflops", type=float, required=True)
+    m.add_argument("--flops", type=float, default=None)
+    m.add_argument("--act-quant", default=None)
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":

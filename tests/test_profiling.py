@@ -39,3 +39,38 @@ def test_read_traffic_keeps_the_modes_apart(tmp_path, monkeypatch):
     (tmp_path / "b_traffic.md").write_text("workload: w1\ntraffic_bytes_per_launch: 5\n" + tail)
     assert P.read_traffic("w1", fam, "mxfp8")[0] == 7.0
     assert P.read_traffic("w1", fam)[0] == 5.0
+
+
+def test_mfma_summary_arithmetic(tmp_path):
+    # Two dispatches of one kernel, 100 us each, with counters chosen so the
+    # derived figures are round: 2.0 GHz (GRBM_GUI_ACTIVE is summed over 8
+    # XCDs), half the SIMD cycles busy, 1.5x the algorithmic flops counted.
+    import csv
+    wl = "switch-top1-n4096-d1024-e8-ff4096-bf16"
+    alg = P.up_flops(wl)
+    cycles = 2.0e9 * 100e-6
+    vals = {"GRBM_GUI_ACTIVE": cycles * 8, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * cycles * 1024,
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16": 1.5 * alg / 512, "SQ_INSTS_VALU_MFMA_MOPS_F8": 0.0}
+    d = tmp_path / "run"
+    d.mkdir()
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"])
+        for disp, t0 in ((1, 1000), (2, 500000)):
+            for k, v in vals.items():
+                w.writerow([disp, "void moe::big_gemm_kernel<true, false>(p)", k, v, t0, t0 + 100000])
+            w.writerow([disp + 10, "other_kernel", "GRBM_GUI_ACTIVE", 1, 0, 1])
+    out = tmp_path / "m.md"
+    import argparse
+    P.cmd_mfma(argparse.Namespace(workload=wl, kernel="big_gemm_kernel<true", pmc=str(d), command="c",
+                                  out=str(out), peak_tflops=2500.0, flops=None, act_quant=None))
+    rows = {}
+    for line in open(out):
+        if line.startswith("| ") and line.count("|") == 3:
+            k, v = line.strip().strip("|").split("|")
+            rows[k.strip()] = v.strip()
+    assert rows["counted / algorithmic"].strip() == "1.500"
+    assert rows["average clock (GRBM_GUI_ACTIVE / duration, GHz)"].strip() == "2.000"
+    assert rows["MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs))"].strip() == "0.500"
+    ach = alg / 100e-6 / 1e12
+    assert abs(float(rows["fraction of the peak at that clock"]) - ach / (2500.0 * 2.0 / 2.4)) < 1e-3
