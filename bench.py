@@ -87,11 +87,26 @@ def cpu_baseline(L, budget_s=15.0, threads=16, act_quant=None):
             oracle.forward(L, L["k"], L["renorm"], rows=np.arange(m), act_quant=act_quant)
             total += time.perf_counter() - t0
             runs += 1
-        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = threadpool_info()
+        used = max([i.get("num_threads", 1) for i in info] + [1])
+    blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip() for i in info
+                             if i.get("user_api") == "blas"})) or "unknown BLAS"
     return {"value": m * runs / total, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
             "sample": f"float64 dense-then-masked oracle on the first {m} of {L['n']} tokens "
                       f"(all {L['E']} experts per token{', W4A8 mode' if act_quant else ''}), "
-                      f"{runs} run(s), {total:.2f} s"}
+                      f"{runs} run(s), {total:.2f} s; host {cpu_model()} "
+                      f"({os.cpu_count()} logical CPUs), numpy {np.__version__} on {blas}"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def main():
