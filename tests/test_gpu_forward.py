@@ -107,6 +107,20 @@ def test_batch_invariance_decode():
         assert np.array_equal(D1.y.cpu().numpy()[0], y64[t])
 
 
+def test_batch_invariance_prefill_routing():
+    """A token's experts and weights in the 4096-token prefill batch are
+    bit-identical to those it gets in a batch of 64 (the router's K splits
+    depend on d alone)."""
+    L = layer_of(W.PREFILL_ZIPF)
+    D = _forward(L)
+    idx, w = D.idx.cpu().numpy(), D.topw.cpu().numpy()
+    for t in (0, 2048, L["n"] - 64):
+        Ls = dict(L, x=L["x"][t:t + 64], n=64)
+        Ds = _forward(Ls)
+        assert np.array_equal(Ds.idx.cpu().numpy(), idx[t:t + 64])
+        assert np.array_equal(Ds.topw.cpu().numpy().view(np.uint32), w[t:t + 64].view(np.uint32))
+
+
 def test_hip_graph_replay_matches_eager():
     import torch
 
