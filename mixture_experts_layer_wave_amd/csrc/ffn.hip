@@ -412,8 +412,8 @@ TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_
   return best;
 }
 
-// The down pass's block tile and K split (the same answer for the up pass,
-// which clears the split counters, and the down pass).
+// The down pass's block tile and K split (a function of the shape alone, so
+// the workspace sizing through down_split_factor and the launch agree).
 TileChoice down_tile(const FfnArgs &a) {
   static const TileChoice cand_bf16[] = {{256, 256, 1}, {320, 256, 1}, {256, 128, 1}, {128, 128, 1},
                                          {256, 256, 2}, {256, 256, 3}, {256, 256, 4}};
