@@ -29,6 +29,13 @@ hipError_t launch_router_topk(const float *part, int splits, int n, int E, int k
 constexpr int kDispSmallR = 256;
 constexpr int kDispChunkMinR = 1024;
 size_t dispatch_scratch_bytes(int n, int k, int E);
+// Top-k and dispatch in one kernel for small batches (n k <= kDispSmallR
+// and one pass of top-k over 256 threads): the same idx, w and piles as
+// launch_router_topk followed by launch_dispatch.
+bool route_small_ok(int n, int k, int E);
+hipError_t launch_route_small(const float *part, int splits, int n, int E, int k, bool renorm,
+                              int32_t *idx, float *w, int32_t *counts, int32_t *offsets,
+                              int32_t *perm, int32_t *inv, hipStream_t st);
 hipError_t launch_dispatch(const int32_t *idx, int n, int k, int E, int32_t *counts,
                            int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *scratch,
                            hipStream_t st);

@@ -384,7 +384,10 @@ int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, cons
   const int splits = splits_of(s, w->dtype);
   hipError_t e = moe::launch_router_logits(x, wg, bias, logits, s->n, s->d, s->E,
                                            act == MOE_BF16, splits, hs);
-  if (e == hipSuccess) {
+  if (e == hipSuccess && moe::route_small_ok(s->n, s->k, s->E)) {
+    e = moe::launch_route_small(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt, counts,
+                                offsets, perm, inv, hs);
+  } else if (e == hipSuccess) {
     e = moe::launch_router_topk(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt,
                                 nullptr, hs);
     if (e == hipSuccess)
