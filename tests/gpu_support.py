@@ -44,6 +44,10 @@ SMALL = {
     # piles of about 25 rows on the GEMM path (the 64-row tile shape)
     "mxfp4-gemm-small-piles": small("mxfp4-gemm-small-piles", 600, 192, 48, 2, 320, "mxfp4", 19),
     "f32-small": small("f32-small", 33, 12, 5, 2, 20, "f32", 17, act="f32"),
+    # top-k and dispatch in one workgroup: one pass of 4 tokens x 64 lanes,
+    # and the 16-slot top-k instance (1024 experts, top-32) at n = 1
+    "mxfp4-n4-e128": small("mxfp4-n4-e128", 4, 128, 128, 4, 96, "mxfp4", 20),
+    "bf16-n1-e1024-k32": small("bf16-n1-e1024-k32", 1, 64, 1024, 32, 32, "bf16", 21),
 }
 
 
