@@ -53,7 +53,7 @@ constexpr int kWaves = 4;      // waves per workgroup, splitting K
 constexpr int kCopyWaves = kWaves - 1;  // waves 1.. issue the copies; wave 0 stores
 constexpr int kMaxSteps = 8;   // 128-deep K steps per wave: K <= 32 * 4 * 4 * 8 = 4096
 constexpr int kBlocksPerCu = 2;  // persistent workgroups per CU
-constexpr int kMaxStages = 8;    // LDS ring depth per workgroup
+constexpr int kMaxStages = 2;    // LDS ring depth per workgroup (2 measured faster than 3)
 constexpr int kCuLds = 160 * 1024;
 
 typedef __attribute__((address_space(3))) void lds_void;
