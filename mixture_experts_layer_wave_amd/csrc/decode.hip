@@ -440,17 +440,6 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   }
 }
 
-int cu_count() {
-  static std::atomic<int> cached{0};
-  int c = cached.load(std::memory_order_relaxed);
-  if (c > 0) return c;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
-    c = 256;
-  cached.store(c, std::memory_order_relaxed);
-  return c;
-}
 
 template <bool UP, int KS, bool A8>
 hipError_t launch_decode_ks(const DecodeParams &p, hipStream_t st) {
@@ -492,6 +481,18 @@ hipError_t launch_decode(DecodeParams p, hipStream_t st) {
 }
 
 }  // namespace
+
+int cu_count() {
+  static std::atomic<int> cached{0};
+  int c = cached.load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+    c = 256;
+  cached.store(c, std::memory_order_relaxed);
+  return c;
+}
 
 // Regions are copied in 16 B pieces: the up tile's 8 rows of scales need
 // d % 64 == 0; the down tile has 16 rows, so d_ff % 32 == 0 suffices.

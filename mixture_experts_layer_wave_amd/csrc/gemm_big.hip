@@ -34,6 +34,7 @@
 
 #include "gemm_big.h"
 #include "gemm_common.h"
+#include "kernels.h"
 
 namespace moe {
 namespace {
@@ -62,7 +63,10 @@ struct Tile {
   static constexpr int MX_UNITS = (MX_ALL + kNT - 1) / kNT;      // per thread
 };
 
-template <bool UP, bool MX, bool GATHER, bool FUSE, int BM, int BNB>
+// LPT: longest-first tile order (map_block_fn), for unsplit down GEMMs of
+// three or more rounds of blocks, where the ragged last row tiles then fill
+// the last round.
+template <bool UP, bool MX, bool GATHER, bool FUSE, int BM, int BNB, bool LPT>
 __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   constexpr int BK = MX ? 64 : MOE_BF16_BK;
   constexpr int NST = MX ? 2 : MOE_BF16_NST;
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   const int S = UP ? 1 : (p.splits > 1 ? p.splits : 1);
 
   // ---- block -> tile ------------------------------------------------------
-  if (wave == 0) map_block<BM>(p.offsets, p.E, p.n_tiles, S, lane, &s_t);
+  if (wave == 0) map_block<BM, LPT>(p.offsets, p.E, p.n_tiles, S, lane, &s_t);
   __syncthreads();
   const int e = s_t.e;
   if (e < 0) return;
@@ -402,14 +406,14 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   }
 }
 
-template <bool UP, bool MX, bool GATHER, bool FUSE, int BM, int BNB>
+template <bool UP, bool MX, bool GATHER, bool FUSE, int BM, int BNB, bool LPT>
 hipError_t launch_one(const BigGemmParams &p, int blocks, hipStream_t st) {
   using T = Tile<BM, BNB, MX ? 64 : MOE_BF16_BK>;
   constexpr int NST = MX ? 2 : MOE_BF16_NST;
   constexpr int OC = UP ? BNB / 2 : BNB;
   constexpr int EPI = (UP || FUSE) ? BM * (OC * 2 + 16) : 0;
   constexpr int lds = NST * T::STAGE > EPI ? NST * T::STAGE : EPI;
-  auto kern = big_gemm_kernel<UP, MX, GATHER, FUSE, BM, BNB>;
+  auto kern = big_gemm_kernel<UP, MX, GATHER, FUSE, BM, BNB, LPT>;
   // Dynamic LDS above 64 KB must be allowed once per device.
   static std::atomic<uint64_t> attr_done{0};
   int dev = 0;
@@ -431,9 +435,15 @@ hipError_t launch_big_gemm(const BigGemmParams &p, bool up, bool mx, bool gather
                            int bm, int bnb, hipStream_t st) {
   const int m_tiles = (p.R + bm - 1) / bm + (p.E < p.R ? p.E : p.R);
   const int blocks = m_tiles * p.n_tiles * (up ? 1 : (p.splits > 1 ? p.splits : 1));
-#define MOE_BIG(U, M, G, F, A, B)                                             \
-  if (up == U && mx == M && gather == G && fuse == F && bm == A && bnb == B) \
-    return launch_one<U, M, G, F, A, B>(p, blocks, st);
+  // Longest first for unsplit bf16 down GEMMs of three or more rounds (16
+  // spare blocks: the two tile lists' per-XCD shares round up separately).
+  const bool lpt = !up && !mx && p.splits <= 1 && blocks > 2 * cu_count();
+#define MOE_BIG(U, M, G, F, A, B)                                                    \
+  if (up == U && mx == M && gather == G && fuse == F && bm == A && bnb == B) {      \
+    if constexpr (!U && !M)                                                          \
+      if (lpt) return launch_one<U, M, G, F, A, B, true>(p, blocks + 16, st);        \
+    return launch_one<U, M, G, F, A, B, false>(p, blocks, st);                       \
+  }
   // up: gather from X or contiguous rows; bf16 or MXFP4 weights
   MOE_BIG(true, false, true, false, 256, 256)
   MOE_BIG(true, false, false, false, 256, 256)

@@ -90,7 +90,13 @@ struct TileSlot {
   int e, row0, rows, nt, item, bm;
 };
 
-template <typename RowTile>
+// LPT (longest first): the tile list is cut in two, the full row tiles of
+// every pile (all but its last) and then the last row tile of each pile,
+// which is the ragged one; each XCD gets a contiguous eighth of each list
+// and runs its full tiles before its last tiles, so the short tiles fill the
+// last round.  The grid needs 16 blocks beyond the tile count (each list's
+// eighths round up separately).
+template <bool LPT = false, typename RowTile>
 __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int n_tiles, int S,
                                              int lane, TileSlot *out, RowTile bm_of) {
   const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
@@ -99,48 +105,68 @@ __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int 
   const int o0 = per == 1 && eb < E ? offsets[eb] : 0;
   const int o1 = per == 1 && eb < E ? offsets[eb + 1] : 0;
   auto tiles_of = [&](int m) { const int bm = bm_of(m); return (m + bm - 1) / bm; };
-  int local = 0;
-  if (per == 1)
-    local = tiles_of(o1 - o0);
-  else
-    for (int x = eb; x < ee; ++x) local += tiles_of(offsets[x + 1] - offsets[x]);
-  const int incl = wave_incl_scan(local);
-  const int excl = incl - local;
-  const int total = __builtin_amdgcn_readlane(incl, MOE_WAVE - 1) * n_tiles * S;
+  // Row tiles of a pile in list 0 (LPT: all but the last) and list 1.
+  auto in_list = [&](int te, bool last) {
+    return LPT ? (last ? (te > 0 ? 1 : 0) : max(te - 1, 0)) : (last ? 0 : te);
+  };
+  int loc0 = 0, loc1 = 0;
+  if (per == 1) {
+    const int te = tiles_of(o1 - o0);
+    loc0 = in_list(te, false);
+    loc1 = in_list(te, true);
+  } else {
+    for (int x = eb; x < ee; ++x) {
+      const int te = tiles_of(offsets[x + 1] - offsets[x]);
+      loc0 += in_list(te, false);
+      loc1 += in_list(te, true);
+    }
+  }
+  const int incl0 = wave_incl_scan(loc0), incl1 = LPT ? wave_incl_scan(loc1) : 0;
+  const int tot0 = __builtin_amdgcn_readlane(incl0, MOE_WAVE - 1) * n_tiles * S;
+  const int tot1 = LPT ? __builtin_amdgcn_readlane(incl1, MOE_WAVE - 1) * n_tiles * S : 0;
   const int b = blockIdx.x;
-  if (lane == 0 && b >= total) out->e = -1;
-  if (b >= total) return;
   const int xcd = b & 7, slot = b >> 3;
-  int base = 0;
-  for (int x = 0; x < xcd; ++x) base += (total - x + 7) >> 3;
-  const int L = (base + slot) / S;
-  if (lane == 0) out->item = base + slot;
-  const int lo = excl * n_tiles, hi = incl * n_tiles;
+  int base0 = 0, base1 = 0;
+  for (int x = 0; x < xcd; ++x) {
+    base0 += (tot0 - x + 7) >> 3;
+    base1 += (tot1 - x + 7) >> 3;
+  }
+  const int cnt0 = (tot0 - xcd + 7) >> 3, cnt1 = (tot1 - xcd + 7) >> 3;
+  if (slot >= cnt0 + cnt1) {
+    if (lane == 0) out->e = -1;
+    return;
+  }
+  const bool last = slot >= cnt0;
+  const int item = last ? base1 + slot - cnt0 : base0 + slot;
+  const int L = item / S;
+  if (lane == 0) out->item = item;
+  const int incl = last ? incl1 : incl0, mine = last ? loc1 : loc0;
+  const int lo = (incl - mine) * n_tiles, hi = incl * n_tiles;
   if (L >= lo && L < hi) {
     int acc = lo;
     for (int x = eb; x < ee; ++x) {
       const int ox = per == 1 ? o0 : offsets[x];
       const int m = (per == 1 ? o1 : offsets[x + 1]) - ox;
-      const int bm = bm_of(m), te = (m + bm - 1) / bm;
-      if (L < acc + te * n_tiles) {
+      const int bm = bm_of(m), te = (m + bm - 1) / bm, c = in_list(te, last);
+      if (L < acc + c * n_tiles) {
         const int loc = L - acc;
-        const int mloc = loc % te;
+        const int mloc = last ? te - 1 : loc % c;
         out->e = x;
-        out->nt = loc / te;
+        out->nt = last ? loc : loc / c;
         out->row0 = ox + mloc * bm;
         out->rows = min(bm, m - mloc * bm);
         out->bm = bm;
         break;
       }
-      acc += te * n_tiles;
+      acc += c * n_tiles;
     }
   }
 }
 
-template <int BM>
+template <int BM, bool LPT = false>
 __device__ __forceinline__ void map_block(const int32_t *offsets, int E, int n_tiles, int S,
                                           int lane, TileSlot *out) {
-  map_block_fn(offsets, E, n_tiles, S, lane, out, [](int) { return BM; });
+  map_block_fn<LPT>(offsets, E, n_tiles, S, lane, out, [](int) { return BM; });
 }
 
 // f32 stores of a block's accumulators: acc[tm][tn] of wave (wm, wn) holds

@@ -95,6 +95,9 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st);    // A -> h
 hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
 hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
 
+// Compute units of the current device (read once and cached).
+int cu_count();
+
 // Small-batch MXFP4 path (decode.hip): persistent workgroups stream 16-row
 // weight tiles through an LDS ring.  decode_ffn_fits tells whether the
 // shape is supported.
