@@ -459,6 +459,8 @@ __global__ __launch_bounds__(kNT, 1) void mxw_gemm_kernel(MxwParams p) {
 // one 64-row tile with 256-deep steps (128-byte pieces of the weight rows,
 // which stream about a quarter faster), a larger pile 128-row tiles with
 // 128-deep steps (half the weight re-reads per row of the 64-row shape).
+// The down pass runs its tiles longest first (measured 0.5-1.3% off the Zipf
+// layer's step; the up pass, 0.6% slower that way, keeps the plain order).
 constexpr int kMixedSmallRows = 64;
 template <bool UP, bool GATHER>
 __global__ __launch_bounds__(kNT, 1) void mxw16_mixed_kernel(MxwParams p) {
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(kNT, 1) void mxw16_mixed_kernel(MxwParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave == 0)
-    map_block_fn(p.offsets, p.E, p.n_tiles, 1, lane, &s_t,
+    map_block_fn<!UP>(p.offsets, p.E, p.n_tiles, 1, lane, &s_t,
                  [](int m) { return m <= kMixedSmallRows ? kMixedSmallRows : 128; });
   __syncthreads();
   if (s_t.e < 0) return;
@@ -606,7 +608,8 @@ bool mxw16_mixed_fits(bool up, int K) {
 hipError_t launch_mxw16_mixed(const MxwParams &p, bool up, bool gather, hipStream_t st) {
   if (p.K > kW4A8MaxK || p.K % 32 || !mxw16_mixed_fits(up, p.K)) return hipErrorInvalidValue;
   const int m_tiles = (p.R + kMixedSmallRows - 1) / kMixedSmallRows + (p.E < p.R ? p.E : p.R);
-  const int blocks = m_tiles * p.n_tiles;
+  // The down pass runs longest first (map_block_fn): 16 spare blocks.
+  const int blocks = m_tiles * p.n_tiles + (up ? 0 : 16);
   const int lds = up ? std::max(lds_bytes<true, kMixedSmallRows, 2, 256, false>(p.K),
                                 lds_bytes<true, 128, 2, 128, false>(p.K))
                      : std::max(lds_bytes<false, kMixedSmallRows, 2, 256, false>(p.K),
