@@ -48,9 +48,10 @@ Readings where the pages are silent (each listed in the design notes):
 * the activation is SwiGLU, ``silu(x W1) * (x W3)`` then ``W2``;
 * with K = 1 the weight is the raw probability; with K > 1 it is
   renormalised over the chosen K;
-* the softmax runs over all E logits (bias included), selection is by
-  descending logit with ties to the lower expert index, and the selection
-  is taken on the logits rounded to float32, the precision of the kernels;
+* the softmax runs over all E logits (bias included), and selection is by
+  descending float64 logit with ties to the lower expert index (generated
+  inputs keep every top-(k+1) gap at >= 1e-4, so float32 kernels make the
+  same choice);
 * within a pile rows are ordered by token, then by slot.
 
 Stored layouts read by this module (the HIP library reads the same bytes):
@@ -278,11 +279,11 @@ def topk_select(z: np.ndarray, k: int) -> np.ndarray:
     [MoE] "Top-K: several experts, added up by weight": keep the K experts
     with the highest scores (K = 1 is the argmax of the routing section).
     Softmax is increasing, so ranking logits ranks probabilities.  The
-    decision is taken on the logits rounded to float32 (the kernels'
-    precision); equal values go to the lower expert index (stable sort).
+    ranking is taken on the float64 logits as given, with no rounding;
+    equal values go to the lower expert index (stable sort).
     """
-    z32 = np.asarray(z, dtype=np.float64).astype(np.float32)
-    order = np.argsort(-z32, axis=1, kind="stable")
+    z64 = np.asarray(z, dtype=np.float64)
+    order = np.argsort(-z64, axis=1, kind="stable")
     return order[:, :k].astype(np.int32)
 
 
