@@ -128,15 +128,16 @@ def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """
     packed = np.asarray(packed, dtype=np.uint8)
     scales = np.asarray(scales, dtype=np.uint8)
-    lo = packed & 0x0F
-    hi = packed >> 4
-    codes = np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
-    K = codes.shape[-1]
+    K = packed.shape[-1] * 2
     if scales.shape[-1] * 32 != K:
         raise ValueError("scale count does not match K/32")
-    vals = decode_e2m1(np.arange(16))[codes]  # the 16 codes decoded once, then looked up
-    blocks = vals.reshape(*vals.shape[:-1], K // 32, 32) * decode_e8m0(scales)[..., None]
-    return blocks.reshape(vals.shape)
+    # Each of the 256 byte values decoded once into its two elements, the
+    # low nibble (even K) first; the bytes then index that table.
+    b = np.arange(256)
+    pair = np.stack([decode_e2m1(b & 0x0F), decode_e2m1(b >> 4)], axis=-1)  # [256][2]
+    vals = pair[packed].reshape(*packed.shape[:-1], K // 32, 32)
+    vals *= decode_e8m0(scales)[..., None]
+    return vals.reshape(*packed.shape[:-1], K)
 
 
 def decode_e4m3(code: np.ndarray) -> np.ndarray:
