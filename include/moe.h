@@ -77,7 +77,10 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_MXFP8 = 3 } moe_dty
  * 0 = use the raw probabilities, -1 = renormalise iff k > 1.
  * Limits: n >= 1, d >= 1, d_ff >= 1, 1 <= E <= 1024, 1 <= k <= min(E, 32),
  * n * k < 2^31.  MXFP4 weights need d % 32 == 0 and d_ff % 32 == 0; bf16
- * activations need d % 8 == 0 and d_ff % 8 == 0. */
+ * activations need d % 8 == 0 and d_ff % 8 == 0.  With BF16 or MXFP4
+ * weights the expert GEMMs address their operands with 32-bit byte
+ * offsets: n * k * max(d, d_ff) < 2^30 and d * d_ff < 2^30 (MOE_ERR_SHAPE
+ * otherwise; a larger batch is split by the caller). */
 typedef struct {
   int32_t n, d, E, k, d_ff;
   int32_t renorm;
@@ -124,8 +127,10 @@ int moe_abi_version(void);
 const char *moe_status_string(int status);
 
 /* Workspace bytes that moe_forward needs for this shape and weight dtype
- * (also enough for moe_grouped_ffn, and for MXFP4 in either mode).  Returns
- * 0 for an invalid shape. */
+ * (also enough for moe_grouped_ffn, and for MXFP4 in either mode).  The
+ * activation dtype is implied by the weight dtype (F32 weights take F32
+ * activations, BF16 and MXFP4 weights BF16), so it is not an argument.
+ * Returns 0 for an invalid shape or dtype. */
 size_t moe_workspace_bytes(const moe_shape *s, int w_dtype);
 
 /* Bytes of an MXFP8 matrix of rows x cols (layout above); 0 when rows < 0
@@ -143,8 +148,9 @@ int moe_quantize_mxfp8(int64_t rows, int32_t cols, const void *x, int act, void 
  *   x      [n][d]   activations (act = MOE_F32 or MOE_BF16)
  *   wg     [E][d]   router matrix W_g stored transposed, same dtype as x
  *   bias   [E] f32  added to every logit, or NULL
- *   logits [n][E] f32 output of x W_g (+ bias); required (the top-k pass
- *          reads it back)
+ *   logits [n][E] f32 output of x W_g (+ bias).  Required (MOE_ERR_NULL
+ *          otherwise): the library keeps no device memory of its own, and
+ *          the top-k pass reads the logits back from this buffer.
  *   topk_idx [n][k] int32 output: chosen experts, best first (descending
  *            logit, equal logits to the lower index)
  *   topk_w   [n][k] f32 output: softmax probability of each chosen expert
@@ -152,7 +158,10 @@ int moe_quantize_mxfp8(int64_t rows, int32_t cols, const void *x, int act, void 
  *            renormalising.
  * The softmax subtracts the row maximum before exponentiating ("Why
  * FlashAttention is So Fast", section "A fused kernel, and an overflow
- * problem"). */
+ * problem").  A NaN logit ranks below every number (as -inf), so every
+ * chosen id lies in [0, E) whatever x holds; a token whose logits are all
+ * NaN gets experts 0 .. k-1 and NaN weights, and other tokens are not
+ * affected.  The same rule holds inside moe_forward. */
 int moe_router_topk(const moe_shape *s, const void *x, int act, const void *wg,
                     const float *bias, float *logits, int32_t *topk_idx,
                     float *topk_w, void *stream);
@@ -179,7 +188,10 @@ int moe_router_stats(const moe_shape *s, const float *logits, const int32_t *top
 /* Dispatch (forward-pass section of the MoE page): regroup the n*k
  * (token, slot) pairs into per-expert piles, expert by expert, each pile in
  * ascending token then slot order; empty piles are allowed.
- *   topk_idx [n][k] int32 input (every value in [0, E))
+ *   topk_idx [n][k] int32 input; a pair whose id is outside [0, E) is put
+ *            in no pile: its inv entry is -1, offsets[E] counts only the
+ *            piled pairs, and the pile rows from offsets[E] to n*k hold
+ *            perm = -1 (x_perm zeros)
  *   counts   [E]    int32 output: pile sizes
  *   offsets  [E+1]  int32 output: pile e is rows offsets[e] .. offsets[e+1]
  *   perm     [n*k]  int32 output: token of each pile row
@@ -218,7 +230,8 @@ int moe_active_experts(const moe_shape *s, const int32_t *counts, int32_t *activ
  *   y_perm[r] = (silu(x_perm[r] W1_e^T) * (x_perm[r] W3_e^T)) W2_e^T
  *   x_perm  [n*k][d] activations (act)
  *   offsets [E+1]    int32, device, as produced by moe_dispatch
- *   y_perm  [n*k][d] float32 output (out must be MOE_F32)
+ *   y_perm  [n*k][d] output, out = MOE_F32, or MOE_BF16 (the f32 pile
+ *           outputs rounded once to nearest even; y_perm 16-byte aligned)
  *   ws      device workspace of at least moe_workspace_bytes(s, w->dtype).
  * offsets is read on the device only; empty experts cost nothing.
  * With BF16/MXFP4 weights, x_perm and y_perm must be 16-byte aligned.
@@ -253,7 +266,9 @@ int moe_expert_down(const moe_shape *s, const void *h, const int32_t *offsets,
  * back in token order and add the k contributions:
  *   y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv[t][j]]
  * summed in slot order in float32, then rounded to `out` (F32 or BF16).
- *   y_perm [n*k][d] f32 (in must be MOE_F32); inv, topk_w [n][k]; y [n][d]. */
+ *   y_perm [n*k][d] f32 (in must be MOE_F32); inv, topk_w [n][k]; y [n][d].
+ * A pair whose inv entry is outside [0, n*k) (moe_dispatch's -1 for an id
+ * outside [0, E)) adds nothing. */
 int moe_combine(const moe_shape *s, const void *y_perm, int in,
                 const int32_t *inv, const float *topk_w, void *y, int out,
                 void *stream);

@@ -223,3 +223,4 @@ def moe_forward(shape, x, act, wg, bias, weights, y, out, topk_idx, topk_w, ws, 
     _check("moe_forward", lib.moe_forward(
         ctypes.byref(_shape(shape)), _ptr(x), _dt(act), _ptr(wg), _ptr(bias), ctypes.byref(w),
         _ptr(y), _dt(out), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws_bytes, _stream(stream)))
+

@@ -10,7 +10,9 @@
 // (After a split-K down pass, y_perm[r] is itself the sum of the partial
 // planes in split order.)
 // A gather-reduce: each output element is written once, with no atomics,
-// so the result does not depend on scheduling.
+// so the result does not depend on scheduling.  A pair whose pile row is
+// outside [0, n k) (its expert id was outside [0, E) at dispatch) adds
+// nothing.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,9 +29,12 @@ __global__ __launch_bounds__(256) void combine_vec4_kernel(const float *__restri
   const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (t >= n || c >= d) return;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const unsigned R = (unsigned)n * (unsigned)k;
   for (int j = 0; j < k; ++j) {
     const float wj = w[(size_t)t * k + j];
-    const f32x4 v = *(const f32x4 *)(yp + (size_t)inv[(size_t)t * k + j] * d + c);
+    const int r = inv[(size_t)t * k + j];
+    if ((unsigned)r >= R) continue;
+    const f32x4 v = *(const f32x4 *)(yp + (size_t)r * d + c);
     acc[0] = fmaf(wj, v[0], acc[0]);
     acc[1] = fmaf(wj, v[1], acc[1]);
     acc[2] = fmaf(wj, v[2], acc[2]);
@@ -51,9 +56,12 @@ __global__ __launch_bounds__(256) void combine_scalar_kernel(const float *__rest
   const int t = blockIdx.y;
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n || c >= d) return;
+  const unsigned R = (unsigned)n * (unsigned)k;
   float acc = 0.f;
-  for (int j = 0; j < k; ++j)
-    acc = fmaf(w[(size_t)t * k + j], yp[(size_t)inv[(size_t)t * k + j] * d + c], acc);
+  for (int j = 0; j < k; ++j) {
+    const int r = inv[(size_t)t * k + j];
+    if ((unsigned)r < R) acc = fmaf(w[(size_t)t * k + j], yp[(size_t)r * d + c], acc);
+  }
   if constexpr (OUT_BF16)
     ((uint16_t *)y)[(size_t)t * d + c] = (uint16_t)f32_to_bf16_bits(acc);
   else
@@ -72,9 +80,12 @@ __global__ __launch_bounds__(256) void splitk_combine_kernel(const float *__rest
   const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (t >= n || c >= d) return;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const unsigned R = (unsigned)n * (unsigned)k;
   for (int j = 0; j < k; ++j) {
     const float wj = w[(size_t)t * k + j];
-    const float *src = part + (size_t)inv[(size_t)t * k + j] * d + c;
+    const int r = inv[(size_t)t * k + j];
+    if ((unsigned)r >= R) continue;
+    const float *src = part + (size_t)r * d + c;
     f32x4 v = *(const f32x4 *)src;
     for (int sp = 1; sp < S; ++sp) v += *(const f32x4 *)(src + sp * plane);
     acc[0] = fmaf(wj, v[0], acc[0]);
@@ -101,7 +112,29 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict
   *(f32x4 *)(yp + i * 4) = v;
 }
 
+// bf16 copy of an f32 array: 8 values a thread in the body, then the tail.
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float *__restrict__ src,
+                                                          uint16_t *__restrict__ dst,
+                                                          size_t count) {
+  const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i + 8 <= count) {
+    const f32x4 a = *(const f32x4 *)(src + i), b = *(const f32x4 *)(src + i + 4);
+    const u32x4 o = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                     pack_bf16x2(b[2], b[3])};
+    *(u32x4 *)(dst + i) = o;
+  } else {
+    for (size_t j = i; j < count; ++j) dst[j] = (uint16_t)f32_to_bf16_bits(src[j]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_f32_to_bf16(const float *src, uint16_t *dst, size_t count, hipStream_t st) {
+  if (count == 0) return hipSuccess;
+  const size_t threads = (count + 7) / 8;
+  f32_to_bf16_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(src, dst, count);
+  return hipGetLastError();
+}
 
 hipError_t launch_splitk_combine(const float *part, int S, int R, const int32_t *inv,
                                  const float *w, int n, int k, int d, void *y, bool out_bf16,

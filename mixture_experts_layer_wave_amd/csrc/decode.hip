@@ -120,7 +120,12 @@ struct DecodeParams {
 // assembly so that the compiler does not order later LDS accesses of the
 // other stages behind it (it would wait for every copy in flight before any
 // LDS access): completion is awaited explicitly with vm_wait before the
-// barrier that publishes a stage.  No other code of the kernel uses M0.
+// barrier that publishes a stage.  M0 is a reserved register: the compiler
+// sets it right before each instruction of its own that reads it and does
+// not honour it in a clobber list, so the asm cannot declare the write.  The
+// generated gfx950 code has no other M0 reader (no movrel, LDS-addtid, GWS
+// or sendmsg instruction); tests/test_isa_cpu.py checks that every M0
+// reference of this file's device code sits inside this asm block.
 __device__ __forceinline__ void copy16_to_lds(const uint8_t *base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :

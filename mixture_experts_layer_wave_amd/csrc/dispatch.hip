@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_chunk_move_kernel(
   extern __shared__ int smem[];
   int *s_tot = smem;       // [E] pile sizes
   int *s_base = s_tot + E;  // [E] first pile row of this chunk's pairs of e
+  __shared__ int s_used;    // rows in all piles together
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int b = blockIdx.x, nb = gridDim.x;
   for (int e = tid; e < E; e += kDispThreads) {
@@ -110,6 +111,7 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_chunk_move_kernel(
       carry += __builtin_amdgcn_readlane(incl, MOE_WAVE - 1);
     }
     if (b == 0 && lane == 0) offsets[E] = carry;
+    if (lane == 0) s_used = carry;
   }
   __syncthreads();
   const int r = b * kDispThreads + tid;
@@ -119,8 +121,13 @@ __global__ __launch_bounds__(kDispThreads) void dispatch_chunk_move_kernel(
       const int pos = s_base[e] + inv[r];
       perm[pos] = r / k;
       inv[r] = pos;
+    } else {
+      inv[r] = -1;  // id outside [0, E): the pair is in no pile
     }
   }
+  // Pile rows past the last pile (one per skipped pair) hold -1; every
+  // workgroup clears the part of that tail inside its own chunk.
+  if (r < R && r >= s_used) perm[r] = -1;
 }
 
 // Small batches (n * k <= 256 pairs): one wave builds the piles in LDS
@@ -197,14 +204,21 @@ __global__ __launch_bounds__(64) void active_experts_kernel(const int32_t *__res
   if (lane == 0) *n_active = base;
 }
 
+// x_perm[r] = x[perm[r]]; a row whose perm entry is outside [0, n) (a pile
+// row past the last pile) is written as zeros.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint32_t *__restrict__ x,
                                                           const int32_t *__restrict__ perm,
                                                           uint32_t *__restrict__ xp, int R,
-                                                          int words) {
+                                                          int n, int words) {
   const int r = blockIdx.x;
   if (r >= R) return;
-  const uint32_t *src = x + (size_t)perm[r] * words;
+  const int t = perm[r];
   uint32_t *dst = xp + (size_t)r * words;
+  if (t < 0 || t >= n) {
+    for (int i = threadIdx.x; i < words; i += blockDim.x) dst[i] = 0u;
+    return;
+  }
+  const uint32_t *src = x + (size_t)t * words;
   if ((words & 3) == 0) {
     const u32x4 *s4 = (const u32x4 *)src;
     u32x4 *d4 = (u32x4 *)dst;
@@ -307,10 +321,10 @@ hipError_t launch_active_experts(const int32_t *counts, int E, int32_t *active,
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const void *x, const int32_t *perm, void *x_perm, int R,
+hipError_t launch_gather_rows(const void *x, const int32_t *perm, void *x_perm, int R, int n,
                               int row_bytes, hipStream_t st) {
   if (R == 0) return hipSuccess;
-  gather_rows_kernel<<<R, 256, 0, st>>>((const uint32_t *)x, perm, (uint32_t *)x_perm, R,
+  gather_rows_kernel<<<R, 256, 0, st>>>((const uint32_t *)x, perm, (uint32_t *)x_perm, R, n,
                                         row_bytes / 4);
   return hipGetLastError();
 }

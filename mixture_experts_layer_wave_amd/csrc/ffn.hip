@@ -95,254 +95,12 @@ __global__ __launch_bounds__(256) void ffn_down_f32_kernel(const float *__restri
   yp[i] = acc;
 }
 
-// ---------------------------------------------------------------------------
-// MFMA grouped GEMM.
-//
-// Block = 256 threads (4 waves as 2 x 2), tile BM = 128 pile rows.  The up
-// kernel covers 64 hidden columns per block and loads the matching 64 rows of
-// W1 and of W3 (128 B-rows); the down kernel covers 128 output columns.
-// K advances by BK = 64 through a double-buffered LDS tile: the next tile's
-// global loads are issued before the MFMAs on the current one.
-// LDS rows are 128 B (64 bf16); the 16-B chunk c of row r sits at chunk
-// c ^ (r & 7) so that the 32 rows read by one MFMA operand spread over banks.
-//
-// The grid is sized for the worst case (ceil(R/BM) + E row tiles) because the
-// pile sizes live on the device; each block maps its row-tile index to
-// (expert, first row) from offsets and surplus blocks exit.
-constexpr int kBM = 128;
-constexpr int kBK = 64;
-
-struct GemmParams {
-  const uint16_t *a;        // bf16 rows
-  const int32_t *perm;      // row -> source row of a (gather), or NULL
-  const int32_t *offsets;   // [E+1]
-  int E, N, K, n_tiles;
-  const void *b0, *b1;      // [E][N][K] (bf16) or [E][N][K/2] (MXFP4); b1 only for up
-  const uint8_t *s0, *s1;   // [E][N][K/32] MXFP4 scales
-  const int32_t *slot;      // [E] logical -> physical slot, or NULL
-  int n_slots;
-  void *out;                // up: bf16 [R][N]; down: f32 [R][N]
-};
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
-}
-
-template <bool UP, bool MX, bool GATHER>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][kBM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][128 * 128];
-  __shared__ int s_e, s_row0, s_rows;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int mt = blockIdx.x / p.n_tiles, nt = blockIdx.x % p.n_tiles;
-
-  // ---- row tile -> (expert, first row, rows) -----------------------------
-  if (wave == 0) {
-    const int per = (p.E + MOE_WAVE - 1) / MOE_WAVE;
-    const int eb = lane * per, ee = min(p.E, eb + per);
-    int local = 0;
-    for (int x = eb; x < ee; ++x) local += (p.offsets[x + 1] - p.offsets[x] + kBM - 1) / kBM;
-    const int incl = wave_incl_scan(local);
-    const int excl = incl - local;
-    const int total = __builtin_amdgcn_readlane(incl, MOE_WAVE - 1);
-    if (lane == 0 && mt >= total) s_e = -1;
-    if (mt >= excl && mt < incl) {
-      int acc = excl;
-      for (int x = eb; x < ee; ++x) {
-        const int m = p.offsets[x + 1] - p.offsets[x];
-        const int te = (m + kBM - 1) / kBM;
-        if (mt < acc + te) {
-          s_e = x;
-          s_row0 = p.offsets[x] + (mt - acc) * kBM;
-          s_rows = min(kBM, m - (mt - acc) * kBM);
-          break;
-        }
-        acc += te;
-      }
-    }
-  }
-  __syncthreads();
-  const int e = s_e;
-  if (e < 0) return;
-  const int row0 = s_row0, rows = s_rows;
-  const int N = p.N, K = p.K;
-  const int n0 = nt * (UP ? 64 : 128);
-
-  // ---- per-thread load assignments ---------------------------------------
-  // A: chunk c = tid + 256 i -> row (tid >> 3) + 32 i, 16-B chunk kc = tid & 7.
-  const int kc = tid & 7;
-  const uint16_t *a_src[4];
-  bool a_ok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    a_ok[i] = r < rows;
-    const int src = a_ok[i] ? (GATHER ? p.perm[row0 + r] : row0 + r) : 0;
-    a_src[i] = p.a + (size_t)src * K + kc * 8;
-  }
-  // B (bf16): same chunk pattern over 128 B-rows.  B (MXFP4): one 32-element
-  // half-row (16 B + 1 scale byte) per thread: row tid >> 1, half tid & 1.
-  const int pe = phys_slot(p.slot, p.n_slots, e);  // physical weight slot
-  const uint16_t *b_src[4];
-  bool b_ok[4];
-  const uint8_t *q_src = nullptr, *sc_src = nullptr;
-  bool q_ok = false;
-  const int mrow = tid >> 1, half = tid & 1;
-  if constexpr (!MX) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int br = (tid >> 3) + 32 * i;
-      const int n = UP ? n0 + (br & 63) : n0 + br;
-      const uint16_t *mat = (const uint16_t *)((UP && br >= 64) ? p.b1 : p.b0);
-      b_ok[i] = n < N;
-      b_src[i] = mat + ((size_t)pe * N + (b_ok[i] ? n : 0)) * K + kc * 8;
-    }
-  } else {
-    const int n = UP ? n0 + (mrow & 63) : n0 + mrow;
-    const uint8_t *mat = (const uint8_t *)((UP && mrow >= 64) ? p.b1 : p.b0);
-    const uint8_t *smat = (UP && mrow >= 64) ? p.s1 : p.s0;
-    q_ok = n < N;
-    const size_t nr = (size_t)pe * N + (q_ok ? n : 0);
-    q_src = mat + nr * (K / 2) + half * 16;
-    sc_src = smat + nr * (K / 32) + half;
-  }
-
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 ra[4], rb[4];
-  uint32_t rs = 0;
-
-  auto load = [&](int kt) {
-    const int k0 = kt * kBK;
-    const bool kok = k0 + kc * 8 < K;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ra[i] = (a_ok[i] && kok) ? *(const u32x4 *)(a_src[i] + k0) : zero;
-    if constexpr (!MX) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        rb[i] = (b_ok[i] && kok) ? *(const u32x4 *)(b_src[i] + k0) : zero;
-    } else {
-      const bool hok = q_ok && (k0 + half * 32 < K);
-      rb[0] = hok ? *(const u32x4 *)(q_src + k0 / 2) : zero;
-      rs = hok ? (uint32_t)sc_src[k0 / 32] : 0u;
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(u32x4 *)(&sA[buf][swz((tid >> 3) + 32 * i, kc)]) = ra[i];
-    if constexpr (!MX) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *(u32x4 *)(&sB[buf][swz((tid >> 3) + 32 * i, kc)]) = rb[i];
-    } else {
-      // 32 E2M1 codes -> 32 bf16 (4 chunks of 8).  rs == 0 only for the
-      // zero-filled tail, whose codes are 0, so the result is 0 there.
-      const float sc = e8m0_to_f32(rs);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t wv = rb[0][q];
-        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 0);
-        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 1);
-        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 2);
-        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wv, sc, 3);
-        u32x4 o = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                   __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-        *(u32x4 *)(&sB[buf][swz(mrow, half * 4 + q)]) = o;
-      }
-    }
-  };
-
-  const int wm = wave >> 1, wn = wave & 1;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-
-  const int lr = lane & 31, lg = lane >> 5;
-  auto compute = [&](int buf) {
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int ch = kk * 2 + lg;
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms)
-        af[ms] = *(const bf16x8 *)(&sA[buf][swz(wm * 64 + ms * 32 + lr, ch)]);
-#pragma unroll
-      for (int ns = 0; ns < 2; ++ns) {
-        const int br = UP ? (ns * 64 + wn * 32 + lr) : (wn * 64 + ns * 32 + lr);
-        bfr[ns] = *(const bf16x8 *)(&sB[buf][swz(br, ch)]);
-      }
-#pragma unroll
-      for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
-          acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bfr[ns], acc[ms][ns], 0, 0, 0);
-    }
-  };
-
-  const int nk = (K + kBK - 1) / kBK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load(kt + 1);
-    compute(kt & 1);
-    if (more) store((kt + 1) & 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue ------------------------------------------------------------
-  // 32x32 accumulator layout: element i of lane l is row (i/4)*8 + (l/32)*4 + i%4,
-  // column l % 32.
-  if constexpr (UP) {
-    uint16_t *h = (uint16_t *)p.out;
-    const int col = n0 + wn * 32 + lr;
-#pragma unroll
-    for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = wm * 64 + ms * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
-        if (r < rows && col < N) {
-          const float g = acc[ms][0][i], u = acc[ms][1][i];
-          h[(size_t)(row0 + r) * N + col] = (uint16_t)f32_to_bf16_bits(silu(g) * u);
-        }
-      }
-  } else {
-    float *y = (float *)p.out;
-#pragma unroll
-    for (int ms = 0; ms < 2; ++ms)
-#pragma unroll
-      for (int ns = 0; ns < 2; ++ns) {
-        const int col = n0 + wn * 64 + ns * 32 + lr;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = wm * 64 + ms * 32 + (i >> 2) * 8 + lg * 4 + (i & 3);
-          if (r < rows && col < N) y[(size_t)(row0 + r) * N + col] = acc[ms][ns][i];
-        }
-      }
-  }
-}
-
-template <bool UP, bool MX>
-hipError_t launch_gemm(const GemmParams &gp, int m_tiles, bool gather, hipStream_t st) {
-  const unsigned blocks = (unsigned)m_tiles * gp.n_tiles;
-  if (gather)
-    grouped_gemm_kernel<UP, MX, true><<<blocks, 256, 0, st>>>(gp);
-  else
-    grouped_gemm_kernel<UP, MX, false><<<blocks, 256, 0, st>>>(gp);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 namespace {
 
-// The large-tile kernel addresses its operands with 32-bit buffer offsets.
+// The large-tile kernel addresses its operands with 32-bit buffer offsets
+// (the host rejects larger shapes before anything is launched).
 bool big_ok(const FfnArgs &a, size_t a_bytes, int N, int K) {
   const size_t lim = (size_t)1 << 31;
   if (a.w_dtype != 1 && a.w_dtype != 2) return false;
@@ -475,7 +233,8 @@ MxwParams mxw_params(const FfnArgs &a, bool up) {
 // (128-byte pieces of the weight rows).
 TileChoice mxw16_tile(const FfnArgs &a, bool up) {
   const int K = up ? a.d : a.d_ff;
-  if (mxw_fits(up, false, MOE_MXW16_BM, MOE_MXW16_BK, K))
+  // (the launcher takes K up to kW4A8MaxK, whatever the LDS would hold)
+  if (K <= kW4A8MaxK && K % 32 == 0 && mxw_fits(up, false, MOE_MXW16_BM, MOE_MXW16_BK, K))
     return TileChoice{MOE_MXW16_BM, 256, 1, MOE_MXW16_BK};
   return TileChoice{0, 0, 0, 0};
 }
@@ -591,24 +350,7 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
 
     return launch_big_gemm(p, true, a.w_dtype == 2, a.perm != nullptr, false, t.bm, t.bnb, st);
   }
-  GemmParams up{};
-  up.a = (const uint16_t *)a.a;
-  up.perm = a.perm;
-  up.offsets = a.offsets;
-  up.E = a.E;
-  up.N = a.d_ff;
-  up.K = a.d;
-  up.n_tiles = (a.d_ff + 63) / 64;
-  up.b0 = a.w1;
-  up.b1 = a.w3;
-  up.s0 = a.s1;
-  up.s1 = a.s3;
-  up.slot = a.slot;
-  up.n_slots = a.n_slots;
-  up.out = a.h;
-  const int m_tiles = (a.R + kBM - 1) / kBM + (a.E < a.R ? a.E : a.R);
-  return a.w_dtype == 2 ? launch_gemm<true, true>(up, m_tiles, a.perm != nullptr, st)
-                        : launch_gemm<true, false>(up, m_tiles, a.perm != nullptr, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
@@ -651,22 +393,7 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
     if (err == hipSuccess && fused) *fused = fuse;
     return err;
   }
-  GemmParams dn{};
-  dn.a = (const uint16_t *)a.h;
-  dn.perm = nullptr;
-  dn.offsets = a.offsets;
-  dn.E = a.E;
-  dn.N = a.d;
-  dn.K = a.d_ff;
-  dn.n_tiles = (a.d + 127) / 128;
-  dn.b0 = a.w2;
-  dn.s0 = a.s2;
-  dn.slot = a.slot;
-  dn.n_slots = a.n_slots;
-  dn.out = a.y_perm;
-  const int m_tiles = (a.R + kBM - 1) / kBM + (a.E < a.R ? a.E : a.R);
-  return a.w_dtype == 2 ? launch_gemm<false, true>(dn, m_tiles, false, st)
-                        : launch_gemm<false, false>(dn, m_tiles, false, st);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st, bool *fused) {

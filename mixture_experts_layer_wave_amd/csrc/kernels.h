@@ -48,8 +48,9 @@ hipError_t launch_router_stats(const float *logits, const int32_t *idx, int n, i
 // active[j] = j-th expert with counts > 0 (ascending), -1 after; *n_active.
 hipError_t launch_active_experts(const int32_t *counts, int E, int32_t *active,
                                  int32_t *n_active, hipStream_t st);
-// x_perm[r] = x[perm[r]] for r < R, rows of row_bytes bytes (multiple of 4).
-hipError_t launch_gather_rows(const void *x, const int32_t *perm, void *x_perm, int R,
+// x_perm[r] = x[perm[r]] for r < R, rows of row_bytes bytes (multiple of 4);
+// rows with perm[r] outside [0, n) are zeros.
+hipError_t launch_gather_rows(const void *x, const int32_t *perm, void *x_perm, int R, int n,
                               int row_bytes, hipStream_t st);
 
 // ---- grouped FFN ----------------------------------------------------------
@@ -114,5 +115,8 @@ hipError_t launch_splitk_combine(const float *part, int S, int R, const int32_t 
 hipError_t launch_splitk_sum(const float *part, int S, int R, int d, float *yp, hipStream_t st);
 hipError_t launch_combine(const float *y_perm, const int32_t *inv, const float *w,
                           int n, int k, int d, void *y, bool out_bf16, hipStream_t st);
+// dst[i] = bf16(src[i]) (round to nearest even) for i < count; both 16-byte
+// aligned.
+hipError_t launch_f32_to_bf16(const float *src, uint16_t *dst, size_t count, hipStream_t st);
 
 }  // namespace moe

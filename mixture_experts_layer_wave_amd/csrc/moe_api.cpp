@@ -7,6 +7,7 @@
 
 #include <algorithm>
 
+#include "api_internal.h"
 #include "gemm_mxw.h"
 #include "kernels.h"
 
@@ -57,6 +58,11 @@ int check_dtypes(const moe_shape *s, int act, int wdt) {
     if (act != MOE_BF16) return MOE_ERR_DTYPE;
     if (s->d % 8 || s->d_ff % 8) return MOE_ERR_SHAPE;
     if (wdt == MOE_MXFP4 && (s->d % 32 || s->d_ff % 32)) return MOE_ERR_SHAPE;
+    // The MFMA GEMMs address the pile matrices (R x d and R x d_ff bf16) and
+    // one expert matrix (d x d_ff) with 32-bit byte offsets.
+    const long long R = (long long)s->n * s->k;
+    if (R * std::max(s->d, s->d_ff) * 2 >= (1ll << 31) || (long long)s->d * s->d_ff * 2 >= (1ll << 31))
+      return MOE_ERR_SHAPE;
   } else {
     return MOE_ERR_DTYPE;
   }
@@ -272,7 +278,7 @@ int moe_dispatch(const moe_shape *s, const int32_t *topk_idx, int32_t *counts,
                                       scratch, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (x_perm) {
-    e = moe::launch_gather_rows(x, perm, x_perm, s->n * s->k, row_bytes, hs);
+    e = moe::launch_gather_rows(x, perm, x_perm, s->n * s->k, s->n, row_bytes, hs);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return MOE_OK;
@@ -296,8 +302,9 @@ int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act, const int32
   st = check_weights(s, act, w, mx8_in);
   if (st != MOE_OK) return st;
   if (!x_perm || !offsets || !y_perm) return MOE_ERR_NULL;
-  if (out != MOE_F32) return MOE_ERR_DTYPE;
+  if (out != MOE_F32 && out != MOE_BF16) return MOE_ERR_DTYPE;
   if (act != MOE_F32 && (!aligned16(x_perm) || !aligned16(y_perm))) return MOE_ERR_ALIGN;
+  if (out == MOE_BF16 && !aligned16(y_perm)) return MOE_ERR_ALIGN;
   const WsLayout L = layout(s, w->dtype);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned16(ws)) return MOE_ERR_ALIGN;
@@ -313,10 +320,16 @@ int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act, const int32
     if (e != hipSuccess) return MOE_ERR_HIP;
     a = xq;
   }
-  moe::FfnArgs f = ffn_args(s, a, nullptr, offsets, w, base + L.h, (float *)y_perm);
+  // BF16 output: the pile outputs are summed in f32 in the workspace, then
+  // rounded once (nearest even) into y_perm.
+  float *yp = out == MOE_BF16 ? (float *)(base + L.yp) : (float *)y_perm;
+  moe::FfnArgs f = ffn_args(s, a, nullptr, offsets, w, base + L.h, yp);
   f.split_ok = true;
   f.split_part = (float *)(base + L.part);
-  return hip_status(moe::launch_grouped_ffn(f, hs));
+  hipError_t e = moe::launch_grouped_ffn(f, hs);
+  if (e == hipSuccess && out == MOE_BF16)
+    e = moe::launch_f32_to_bf16(yp, (uint16_t *)y_perm, (size_t)s->n * s->k * s->d, hs);
+  return hip_status(e);
 }
 
 int moe_expert_up(const moe_shape *s, const void *a, int act, const int32_t *perm,
@@ -359,6 +372,17 @@ int moe_combine(const moe_shape *s, const void *y_perm, int in, const int32_t *i
 int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, const float *bias,
                 const moe_expert_weights *w, void *y, int out, int32_t *topk_idx,
                 float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  return moe::forward_impl(s, x, act, wg, bias, w, y, out, topk_idx, topk_w, ws, ws_bytes,
+                           stream);
+}
+
+}  // extern "C"
+
+namespace moe {
+
+int forward_impl(const moe_shape *s, const void *x, int act, const void *wg, const float *bias,
+                 const moe_expert_weights *w, void *y, int out, int32_t *topk_idx,
+                 float *topk_w, void *ws, size_t ws_bytes, void *stream) {
   int st = check_shape(s);
   if (st != MOE_OK) return st;
   st = check_weights(s, act, w);
@@ -423,4 +447,4 @@ int moe_forward(const moe_shape *s, const void *x, int act, const void *wg, cons
   return hip_status(e);
 }
 
-}  // extern "C"
+}  // namespace moe

@@ -125,12 +125,19 @@ __device__ __forceinline__ void topk_token_t(const float *__restrict__ part, int
       for (int j = 0; j < kTopkPer; ++j)
         if (s0 + u < S) v[j] += q[u][j];
   }
+  if (logits_out) {
+#pragma unroll
+    for (int j = 0; j < kTopkPer; ++j)
+      if (live && gl + G * j < E) logits_out[(size_t)t * E + gl + G * j] = v[j];
+  }
+  // A NaN logit ranks below every number: it takes part as -inf.  A round
+  // whose best value is -inf then picks the lowest untaken expert, so every
+  // chosen id lies in [0, E) whatever the logits hold.
+#pragma unroll
+  for (int j = 0; j < kTopkPer; ++j) v[j] = v[j] == v[j] ? v[j] : NEG;
   float m = NEG;
 #pragma unroll
-  for (int j = 0; j < kTopkPer; ++j) {
-    if (logits_out && live && gl + G * j < E) logits_out[(size_t)t * E + gl + G * j] = v[j];
-    m = fmaxf(m, v[j]);
-  }
+  for (int j = 0; j < kTopkPer; ++j) m = fmaxf(m, v[j]);
   m = group_max(m, G);
   float sum = 0.f;
 #pragma unroll
@@ -189,6 +196,11 @@ __host__ __device__ constexpr int topk_per(int E) {
 constexpr int kDispThreads = 1024;
 constexpr int kDispWaves = kDispThreads / MOE_WAVE;
 
+// Rows in all piles together: offsets[E - 1] + counts[E - 1] from LDS.
+__device__ __forceinline__ int s_cur_total(const int *s_off, const int *s_cur, int E) {
+  return s_off[E - 1] + s_cur[E - 1];
+}
+
 // LDS ints needed by dispatch_block.
 __host__ __device__ constexpr int dispatch_lds_ints(int E) { return E * (2 + 2 * kDispWaves); }
 
@@ -201,7 +213,8 @@ __host__ __device__ constexpr int dispatch_lds_ints(int E) { return E * (2 + 2 *
 //   2. the cursors are now the pile sizes: exclusive scan -> offsets;
 //   3. every pair moves to offsets[e] + rank (perm, inv).
 // No atomics decide positions, so the result is the unique stable grouping.
-// Ids outside [0, E) are skipped.  The ids and ranks of up to RC chunks
+// Ids outside [0, E) are skipped: their pairs get inv = -1, and the pile
+// rows past the last pile get perm = -1.  The ids and ranks of up to RC chunks
 // stay in registers; longer inputs park ranks in inv[] (each thread reads
 // back only its own entries).  Barriers order LDS only.  `idx` may point to
 // LDS or global memory.
@@ -303,6 +316,8 @@ __device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, 
         const int pos = s_off[e] + rk[q];
         perm[pos] = r / k;
         inv[r] = pos;
+      } else if (r < R) {
+        inv[r] = -1;
       }
     }
   } else {
@@ -312,9 +327,14 @@ __device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, 
         const int pos = s_off[e] + inv[r];
         perm[pos] = r / k;
         inv[r] = pos;
+      } else {
+        inv[r] = -1;
       }
     }
   }
+  // Pile rows past the last pile (pairs with ids outside [0, E)) hold -1.
+  const int used = s_cur_total(s_off, s_cur, E);
+  for (int r = used + tid; r < R; r += kDispThreads) perm[r] = -1;
 }
 
 // Stable piles of R <= 4 * 64 (token, slot) pairs built by one wave in LDS
@@ -325,7 +345,8 @@ __device__ __forceinline__ void dispatch_block(const int32_t *__restrict__ idx, 
 // pile offsets, s_perm [R] token of each pile row, s_inv [R] pile row of
 // each pair.  The LDS accesses of one wave complete in order, so a chunk's
 // cursor reads see the previous chunk's updates.  Ids outside [0, E) are
-// skipped.
+// skipped: their pairs get s_inv = -1, and the pile rows past the last pile
+// hold s_perm = -1.
 __device__ __forceinline__ void dispatch_wave(const int32_t *__restrict__ idx, int R, int k,
                                               int E, int nbits, int *s_cnt, int *s_off,
                                               int *s_perm, int *s_inv) {
@@ -366,8 +387,11 @@ __device__ __forceinline__ void dispatch_wave(const int32_t *__restrict__ idx, i
       const int pos = s_off[ids[c]] + rk[c];
       s_perm[pos] = r / k;
       s_inv[r] = pos;
+    } else if (r < R) {
+      s_inv[r] = -1;
     }
   }
+  for (int r = carry + lane; r < R; r += MOE_WAVE) s_perm[r] = -1;
 }
 
 }  // namespace moe

@@ -48,6 +48,11 @@ SMALL = {
     # and the 16-slot top-k instance (1024 experts, top-32) at n = 1
     "mxfp4-n4-e128": small("mxfp4-n4-e128", 4, 128, 128, 4, 96, "mxfp4", 20),
     "bf16-n1-e1024-k32": small("bf16-n1-e1024-k32", 1, 64, 1024, 32, 32, "bf16", 21),
+    # MXFP4 with K past what the GEMM with codes in LDS keeps (7168) and more
+    # than 1024 routed rows: the large-tile GEMM dequantising the codes in
+    # registers, on the up projection (K = d) and on the down (K = d_ff)
+    "mxfp4-wide-d": small("mxfp4-wide-d", 600, 7232, 4, 2, 96, "mxfp4", 22),
+    "mxfp4-wide-ff": small("mxfp4-wide-ff", 600, 128, 4, 2, 7232, "mxfp4", 23),
 }
 
 
@@ -86,3 +91,27 @@ def sample_rows(n: int, idx: np.ndarray, counts: np.ndarray, m: int = 40) -> np.
         t = np.nonzero((idx == e).any(axis=1))[0]
         rows.add(int(t[0]))
     return np.array(sorted(rows))
+
+
+def pile_rows(lo: int, hi: int, e: int, step: int = 32) -> np.ndarray:
+    """Rows of the pile [lo, hi) that touch every `step`-row group of it:
+    the first and last row, plus one row of each group at a phase that
+    varies from group to group.  Row tiles start at a pile's first row and
+    are multiples of 32 rows, so with step = 32 every 32-row MFMA group of
+    every row tile of the pile is compared (all output columns of a row)."""
+    m = hi - lo
+    if m <= 0:
+        return np.zeros(0, dtype=np.int64)
+    rows = {lo, hi - 1}
+    for j in range((m + step - 1) // step):
+        r = lo + j * step + (j * 13 + e * 7) % step
+        rows.add(min(r, hi - 1))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def pile_tokens(offsets: np.ndarray, perm: np.ndarray, step: int = 32) -> np.ndarray:
+    """Tokens behind pile_rows of every pile (deduplicated, ascending)."""
+    E = len(offsets) - 1
+    rows = [pile_rows(int(offsets[e]), int(offsets[e + 1]), e, step) for e in range(E)]
+    rows = np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
+    return np.unique(np.asarray(perm)[rows])

@@ -184,3 +184,38 @@ def test_w4a8_sizes_and_errors_before_launch():
     R = n * k
     ws = B.moe_workspace_bytes((n, d, E, k, f), "mxfp4")
     assert ws >= B.moe_mxfp8_bytes(R, d) + B.moe_mxfp8_bytes(R, f)
+
+
+def test_boundary_choices_before_launch():
+    """The boundary's documented choices, checked before anything launches:
+    moe_router_topk needs a logits buffer (the library holds no device
+    memory of its own); moe_grouped_ffn writes f32 or bf16 pile outputs; the
+    workspace size is a function of the shape and the weight dtype; the
+    expert GEMMs' 32-bit operand offsets bound the batch."""
+    import ctypes
+
+    from mixture_experts_layer_wave_amd import binding as B
+
+    fake = 1 << 20  # never dereferenced: every call below fails before a launch
+    sp = ctypes.byref(B._shape((16, 64, 8, 2, 64)))
+    # logits = NULL is rejected
+    assert B.lib.moe_router_topk(sp, fake, 1, fake, None, None, fake, fake, None) == -1
+    # grouped FFN: F32 and BF16 outputs pass the dtype check (and then stop at
+    # the misaligned output); other output dtypes do not
+    w = B.ExpertWeights(1, fake, fake, fake, None, None, None)
+    big = 1 << 30
+    ffn = lambda out, y: B.lib.moe_grouped_ffn(sp, fake, 1, fake, ctypes.byref(w), y, out, fake, big, None)
+    assert ffn(B.MOE_BF16, fake + 8) == -4
+    assert ffn(B.MOE_F32, fake + 8) == -4
+    assert ffn(B.MOE_MXFP4, fake) == -3
+    assert ffn(B.MOE_MXFP8, fake) == -3
+    # workspace: (shape, weight dtype); MXFP8 is not a weight dtype
+    assert B.moe_workspace_bytes((16, 64, 8, 2, 64), "bf16") > 0
+    assert B.moe_workspace_bytes((16, 64, 8, 2, 64), "mxfp4") > 0
+    assert B.moe_workspace_bytes((16, 64, 8, 2, 64), "mxfp8") == 0
+    # n k max(d, d_ff) must stay below 2^30 with bf16 / MXFP4 weights
+    fwd = lambda shape, wd: B.lib.moe_forward(ctypes.byref(B._shape(shape)), fake, 1, fake, None,
+                                              ctypes.byref(B.ExpertWeights(wd, fake, fake, fake, fake, fake, fake)),
+                                              fake, 1, None, None, fake, 1 << 40, None)
+    assert fwd((65536, 4096, 8, 2, 14336), 1) == -2   # 131072 x 14336 rows of bf16 hidden
+    assert fwd((16, 32768, 8, 2, 32768), 2) == -2     # one expert matrix past 2^30 elements

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_support import SMALL, TOL, layer_of, oracle_routing, row_rel_err, sample_rows, say
+from tests.gpu_support import SMALL, TOL, layer_of, oracle_routing, pile_rows, row_rel_err, say
 from mixture_experts_layer_wave_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -15,7 +15,7 @@ def _expert_ref(L, rows_x, e):
     return oracle.swiglu_expert(rows_x, *m)
 
 
-@pytest.mark.parametrize("name", list(SMALL) + [W.SWITCH, W.DECODE[2], W.PREFILL_ZIPF])
+@pytest.mark.parametrize("name", list(SMALL) + [W.SWITCH, W.MIXTRAL, W.DECODE[2], W.PREFILL_ZIPF])
 def test_grouped_ffn_matches_oracle(name):
     import torch
     from mixture_experts_layer_wave_amd import binding as B
@@ -38,15 +38,35 @@ def test_grouped_ffn_matches_oracle(name):
         lo, hi = int(ref["offsets"][e]), int(ref["offsets"][e + 1])
         if lo == hi:
             continue
-        rows = np.arange(lo, hi)
-        if len(rows) > 24:  # sampled rows of large piles, always incl. the pile edges
-            rows = np.unique(np.concatenate([rows[:4], rows[-4:], np.random.default_rng(e).choice(rows, 16)]))
+        # every 32-row group of the pile's row tiles, with the pile edges
+        rows = np.arange(lo, hi) if hi - lo <= 24 else pile_rows(lo, hi, e)
         want = _expert_ref(L, x[ref["perm"][rows]], e)
         worst = max(worst, row_rel_err(got[rows], want))
-        if e > 24 and name == W.PREFILL_ZIPF:
-            break
     say(f"    max row rel err {worst:.3e}")
     assert worst <= TOL[L["w_dtype"]]
+
+
+@pytest.mark.parametrize("name", ["bf16-ragged", "mxfp4-gemm-ragged", W.DECODE[1]])
+def test_grouped_ffn_bf16_output_is_rounded_f32_output(name):
+    """moe_grouped_ffn with a bf16 output is its f32 output rounded to
+    nearest even, element by element."""
+    import torch
+    from mixture_experts_layer_wave_amd import binding as B
+    from mixture_experts_layer_wave_amd.device import DeviceLayer, to_device
+
+    say(f"[ffn bf16 out] {name}")
+    L = layer_of(name)
+    ref = oracle_routing(L)
+    D = DeviceLayer(L)
+    R = D.n * D.k
+    xp = to_device(L["x"][ref["perm"]])
+    off = to_device(ref["offsets"])
+    y32 = torch.empty((R, D.d), dtype=torch.float32, device="cuda")
+    y16 = torch.full((R, D.d), -1, dtype=torch.int16, device="cuda")
+    B.moe_grouped_ffn(D.shape, xp, D.act, off, D.weights, y32, "f32", D.ws, D.ws_bytes)
+    B.moe_grouped_ffn(D.shape, xp, D.act, off, D.weights, y16, "bf16", D.ws, D.ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(y32.to(torch.bfloat16).view(torch.int16), y16)
 
 
 @pytest.mark.parametrize("k,d,out", [(1, 1024, "bf16"), (2, 4096, "bf16"), (4, 2880, "f32"), (3, 7, "f32"), (2, 10, "bf16")])

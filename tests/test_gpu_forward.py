@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_support import SMALL, TOL, layer_of, oracle_routing, row_rel_err, sample_rows, say
+from tests.gpu_support import (SMALL, TOL, layer_of, oracle_routing, pile_tokens, row_rel_err,
+                               sample_rows, say)
 from mixture_experts_layer_wave_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +36,11 @@ def test_forward_matches_oracle(name):
     ref = oracle_routing(L)
     assert np.array_equal(D.idx.cpu().numpy(), ref["idx"])
     np.testing.assert_allclose(D.topw.double().cpu().numpy(), ref["w"], rtol=2e-5, atol=1e-7)
-    rows = np.arange(L["n"]) if L["n"] <= 512 else sample_rows(L["n"], ref["idx"], ref["counts"])
+    # Large batches: every 32-row group of every pile's row tiles (through the
+    # tokens behind them), plus a spread of tokens.
+    rows = (np.arange(L["n"]) if L["n"] <= 512 else
+            np.union1d(sample_rows(L["n"], ref["idx"], ref["counts"]),
+                       pile_tokens(ref["offsets"], ref["perm"])))
     want = oracle.forward(L, L["k"], L["renorm"], rows=rows)["y"]
     got = D.y_f64()[rows]
     err = row_rel_err(got, want)
