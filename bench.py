@@ -148,7 +148,8 @@ def main():
     from mixture_experts_layer_wave_amd.profiling import read_traffic
     from mixture_experts_layer_wave_amd.device import DeviceLayer, to_device
 
-    name = args.workload or W.SWITCH
+    # Default: the largest single-GPU layer, the Mixtral-shaped top-2 prefill.
+    name = args.workload or W.MIXTRAL
     wl = W.WORKLOADS[name]
     log(f"[bench] workload {name}: generating inputs")
     L = W.make_layer(name, cache=False)
@@ -238,6 +239,7 @@ def main():
         h = torch.empty((R, D.d_ff), dtype=torch.int16 if D.wdt != "f32" else torch.float32, device="cuda")
     torch.cuda.synchronize()
     work = algorithmic_work(L, counts.cpu().numpy(), aq)
+    decode = wl.wdt == "mxfp4" and wl.n <= 64
 
     # Dominant kernel: the grouped up-projection, one launch per call.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -249,7 +251,6 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     up_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    decode = wl.wdt == "mxfp4" and wl.n <= 64
     if decode:
         achieved = work["up_bytes"] / (up_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -275,7 +276,14 @@ def main():
     roof["kernel_us"] = up_ms * 1e3
     log(f"[bench] up kernel {up_ms * 1e3:.1f} us -> {roof['achieved']:.1f} {roof['unit']} ({100 * roof['frac']:.1f}% of peak)")
     layer_tflops = work["flops"] / (ms_per_step * 1e-3) / 1e12
-    log(f"[bench] whole layer {layer_tflops:.1f} TFLOP/s, {work['bytes'] / (ms_per_step * 1e-3) / 1e9:.1f} GB/s algorithmic; active experts {work['active_experts']}")
+    layer_gbs = work["bytes"] / (ms_per_step * 1e-3) / 1e9
+    # The whole step against the same roofline: algorithmic flops (prefill) or
+    # bytes (decode) of the layer per step time.
+    layer_frac = (layer_gbs / PEAK_HBM_GBS if decode else
+                  layer_tflops / (PEAK_FP8_TFLOPS if aq else PEAK_BF16_TFLOPS))
+    roof["layer_frac"] = layer_frac
+    log(f"[bench] whole layer {layer_tflops:.1f} TFLOP/s, {layer_gbs:.1f} GB/s algorithmic "
+        f"({100 * layer_frac:.1f}% of peak); active experts {work['active_experts']}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -300,6 +308,20 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+    # Release the device state before the interpreter exits: the queued work,
+    # the graph and every device buffer go now, while the HIP runtime (and a
+    # profiler attached to it) is still fully up.
+    torch.cuda.synchronize()
+    if args.graph:
+        del graph
+    del copies, keep, D, evs, marks
+    del logits, idx, tw, counts, offsets, perm, inv, h, a_in
+    import gc
+
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":
