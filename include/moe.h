@@ -285,6 +285,27 @@ int moe_forward(const moe_shape *s, const void *x, int act, const void *wg,
                 int out, int32_t *topk_idx, float *topk_w, void *ws,
                 size_t ws_bytes, void *stream);
 
+/* The whole layer, as moe_forward, without a workspace argument: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is
+ * a fixed array of MOE_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * per device, held from the first call on that device until the process
+ * ends; the call itself allocates nothing.
+ *   Arguments and results: as moe_forward.
+ *   MOE_ERR_WORKSPACE when the shape needs more than the array holds
+ *   (moe_workspace_bytes(s, w->dtype) > MOE_NOALLOC_SCRATCH_BYTES, e.g.
+ *   the 128-expert MXFP4 layer at d = d_ff = 2880 up to about 400 tokens);
+ *   argument errors are reported first, as by moe_forward.
+ *   Every call on a device uses that device's one array, and the array
+ *   keeps what the last call left in it (no call depends on that content).
+ *   Calls that can overlap on one device -- on different streams without an
+ *   order between them, or from several host threads -- race on the array;
+ *   such callers use moe_forward with a workspace each. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_forward_noalloc(const moe_shape *s, const void *x, int act, const void *wg,
+                        const float *bias, const moe_expert_weights *w, void *y, int out,
+                        int32_t *topk_idx, float *topk_w, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -87,12 +87,14 @@ lib.moe_combine.restype = _I
 lib.moe_combine.argtypes = [_SP, _P, _I, _P, _P, _P, _I, _P]
 lib.moe_forward.restype = _I
 lib.moe_forward.argtypes = [_SP, _P, _I, _P, _P, _WP, _P, _I, _P, _P, _P, _SZ, _P]
+lib.moe_forward_noalloc.restype = _I
+lib.moe_forward_noalloc.argtypes = [_SP, _P, _I, _P, _P, _WP, _P, _I, _P, _P, _P]
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_bytes", "moe_mxfp8_bytes",
            "moe_quantize_mxfp8", "moe_router_topk",
            "moe_router_stats_workspace_bytes", "moe_router_stats", "moe_active_experts",
            "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_grouped_ffn", "moe_expert_up", "moe_expert_down", "moe_combine",
-           "moe_forward")
+           "moe_forward", "moe_forward_noalloc")
 
 
 def _ptr(t):
@@ -224,3 +226,9 @@ def moe_forward(shape, x, act, wg, bias, weights, y, out, topk_idx, topk_w, ws, 
         ctypes.byref(_shape(shape)), _ptr(x), _dt(act), _ptr(wg), _ptr(bias), ctypes.byref(w),
         _ptr(y), _dt(out), _ptr(topk_idx), _ptr(topk_w), _ptr(ws), ws_bytes, _stream(stream)))
 
+
+def moe_forward_noalloc(shape, x, act, wg, bias, weights, y, out, topk_idx, topk_w, stream=None):
+    w = _weights(weights)
+    _check("moe_forward_noalloc", lib.moe_forward_noalloc(
+        ctypes.byref(_shape(shape)), _ptr(x), _dt(act), _ptr(wg), _ptr(bias), ctypes.byref(w),
+        _ptr(y), _dt(out), _ptr(topk_idx), _ptr(topk_w), _stream(stream)))

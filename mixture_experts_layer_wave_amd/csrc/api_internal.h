@@ -1,5 +1,5 @@
-// Internal entry of the host side: the whole layer behind moe_forward
-// (moe_api.cpp), callable with any workspace.
+// Internal entry of the host side shared by moe_forward (moe_api.cpp) and
+// moe_forward_noalloc (noalloc.hip).
 #pragma once
 
 #include "moe.h"
