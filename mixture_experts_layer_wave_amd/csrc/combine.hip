@@ -112,6 +112,78 @@ __global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict
   *(f32x4 *)(yp + i * 4) = v;
 }
 
+// Pile e's last row tile starts at offsets[e] + (ceil(m / bm) - 1) bm.
+__device__ __forceinline__ int expert_of(const int32_t *__restrict__ off, int E, int r) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+__device__ __forceinline__ int tail_begin(const int32_t *__restrict__ off, int e, int bm) {
+  const int m = off[e + 1] - off[e];
+  return off[e] + ((m + bm - 1) / bm - 1) * bm;
+}
+
+// Four columns of pile row r: from y_perm, or, in a last row tile, the sum
+// of its S partial planes in split order.
+__device__ __forceinline__ f32x4 pile_row4(const float *__restrict__ yp,
+                                           const float *__restrict__ tail, int S, size_t plane,
+                                           const int32_t *__restrict__ off, int E, int bm, int r,
+                                           int d, int c) {
+  const int e = expert_of(off, E, r);
+  const int tb = tail_begin(off, e, bm);
+  if (r < tb) return *(const f32x4 *)(yp + (size_t)r * d + c);
+  const float *q = tail + ((size_t)e * bm + (r - tb)) * d + c;
+  f32x4 v = *(const f32x4 *)q;
+  for (int sp = 1; sp < S; ++sp) v += *(const f32x4 *)(q + sp * plane);
+  return v;
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void combine_tail_kernel(
+    const float *__restrict__ yp, const float *__restrict__ tail, int S, size_t plane,
+    const int32_t *__restrict__ off, int E, int bm, const int32_t *__restrict__ inv,
+    const float *__restrict__ w, int n, int k, int d, void *__restrict__ y) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (t >= n || c >= d) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const unsigned R = (unsigned)n * (unsigned)k;
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const int r = inv[(size_t)t * k + j];
+    if ((unsigned)r >= R) continue;
+    const f32x4 v = pile_row4(yp, tail, S, plane, off, E, bm, r, d, c);
+    acc[0] = fmaf(wj, v[0], acc[0]);
+    acc[1] = fmaf(wj, v[1], acc[1]);
+    acc[2] = fmaf(wj, v[2], acc[2]);
+    acc[3] = fmaf(wj, v[3], acc[3]);
+  }
+  if constexpr (OUT_BF16) {
+    u32x2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *(u32x2 *)((uint16_t *)y + (size_t)t * d + c) = o;
+  } else {
+    *(f32x4 *)((float *)y + (size_t)t * d + c) = acc;
+  }
+}
+
+// Block row (e, i): row i of pile e's last row tile, if the pile has it.
+__global__ __launch_bounds__(256) void tail_sum_kernel(const float *__restrict__ tail, int S,
+                                                       size_t plane,
+                                                       const int32_t *__restrict__ off, int bm,
+                                                       int d, float *__restrict__ yp) {
+  const int e = blockIdx.y / bm, i = blockIdx.y % bm;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int tb = tail_begin(off, e, bm);
+  if (off[e + 1] == off[e] || tb + i >= off[e + 1] || c >= d) return;
+  const float *q = tail + ((size_t)e * bm + i) * d + c;
+  f32x4 v = *(const f32x4 *)q;
+  for (int sp = 1; sp < S; ++sp) v += *(const f32x4 *)(q + sp * plane);
+  *(f32x4 *)(yp + (size_t)(tb + i) * d + c) = v;
+}
+
 // bf16 copy of an f32 array: 8 values a thread in the body, then the tail.
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float *__restrict__ src,
                                                           uint16_t *__restrict__ dst,
@@ -152,6 +224,29 @@ hipError_t launch_splitk_sum(const float *part, int S, int R, int d, float *yp, 
   const size_t total4 = (size_t)R * d / 4;
   splitk_sum_kernel<<<(unsigned)((total4 + 255) / 256), 256, 0, st>>>(part, S, (size_t)R * d,
                                                                        total4, yp);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_tail(const float *y_perm, const float *tail, int S, size_t plane,
+                               const int32_t *offsets, int E, int bm, const int32_t *inv,
+                               const float *w, int n, int k, int d, void *y, bool out_bf16,
+                               hipStream_t st) {
+  if (d % 4) return hipErrorInvalidValue;
+  dim3 grid((d / 4 + 255) / 256, n);
+  if (out_bf16)
+    combine_tail_kernel<true><<<grid, 256, 0, st>>>(y_perm, tail, S, plane, offsets, E, bm, inv,
+                                                    w, n, k, d, y);
+  else
+    combine_tail_kernel<false><<<grid, 256, 0, st>>>(y_perm, tail, S, plane, offsets, E, bm, inv,
+                                                     w, n, k, d, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_sum(const float *tail, int S, size_t plane, const int32_t *offsets, int E,
+                           int bm, int d, float *y_perm, hipStream_t st) {
+  if (d % 4) return hipErrorInvalidValue;
+  dim3 grid((d / 4 + 255) / 256, (unsigned)E * bm);
+  tail_sum_kernel<<<grid, 256, 0, st>>>(tail, S, plane, offsets, bm, d, y_perm);
   return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@
 #include "common.h"
 #include "gemm_mxw.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
@@ -55,6 +56,9 @@ constexpr int kMaxSteps = 8;   // 128-deep K steps per wave: K <= 32 * 4 * 4 * 8
 constexpr int kBlocksPerCu = 2;  // persistent workgroups per CU
 constexpr int kMaxStages = 2;    // LDS ring depth per workgroup (2 measured faster than 3)
 constexpr int kCuLds = 160 * 1024;
+constexpr int kRouteMaxR = 64;   // routed rows (n k) of the folded routing
+constexpr int kRouteMaxE = 128;  // experts of the folded routing (two per lane)
+constexpr int kRoutePer = 2;     // expert slots per lane: topk_per(E) for E <= 128
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -80,6 +84,7 @@ struct StagePlan {
 };
 
 constexpr int kRedBytes = kWaves * 64 * 16;  // one f32x4 per lane per wave
+static_assert(kRedBytes >= (4 * kRouteMaxR + kRouteMaxE) * 4, "folded routing tables fit in red");
 
 StagePlan stage_plan(int K, bool up, int E) {
   StagePlan s{};
@@ -87,7 +92,7 @@ StagePlan stage_plan(int K, bool up, int E) {
   const int code_bytes = tile_rows(up) * (K / 2), scale_bytes = tile_rows(up) * (K / 32);
   s.stage_bytes = mats * (code_bytes + scale_bytes);
   s.copies = mats * ((code_bytes + 1023) / 1024 + (scale_bytes + 1023) / 1024);
-  s.table_bytes = ((3 * (E + 1) * 4) + 15) & ~15;
+  s.table_bytes = ((3 * (E + 1) * 4 + kRouteMaxR * 4) + 15) & ~15;
   const int avail = kCuLds / kBlocksPerCu - kRedBytes - s.table_bytes;
   s.stages = avail > 0 ? avail / s.stage_bytes : 0;
   if (s.stages > kMaxStages) s.stages = kMaxStages;
@@ -112,6 +117,16 @@ struct DecodeParams {
   int sp;
   uint8_t *out_s;          // A8 up: scales of the hidden, pitch mx8_scale_pitch(N)
   StagePlan plan;
+  // Routing folded into the up kernel (small batches, route_part set): every
+  // workgroup takes the top-k of the route_n tokens from the router's S
+  // partial logit planes route_part[s][n][E] and builds the piles itself,
+  // with the functions of the separate top-k and dispatch kernels (so the
+  // results are the same); workgroup 0 writes idx, w, counts, offsets, perm
+  // and inv for the later kernels.  offsets and perm above are not read.
+  const float *route_part;
+  int route_S, route_n, route_k, route_renorm;
+  int32_t *r_idx, *r_counts, *r_offsets, *r_perm, *r_inv;
+  float *r_w;
 };
 
 // Direct copy of 16 B per lane from global memory (wave-uniform base plus
@@ -175,9 +190,48 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   int *s_off = (int *)((uint8_t *)red + kRedBytes);         // [E+1] pile offsets
   int *s_gpre = s_off + (E + 1);                            // [E+1] groups before expert e
   int *s_slot = s_gpre + (E + 1);                           // [E] physical weight slot
+  int *s_perm = s_slot + (E + 1);                           // [kRouteMaxR] folded routing
+
+  // ---- routing (folded) or the piles from dispatch ---------------------------
+  const int32_t *perm = p.perm;
+  if (p.route_part) {
+    // Tables in `red` (free until the first tile): chosen ids, weights and
+    // pile rows of the (token, slot) pairs, and the pile sizes.
+    const int n = p.route_n, k = p.route_k, R = n * k;
+    int *s_idx = (int *)red;
+    int *s_idx_sink = s_idx + kRouteMaxR;
+    float *s_w = (float *)(s_idx_sink + kRouteMaxR);
+    int *s_inv = (int *)(s_w + kRouteMaxR);
+    int *s_cnt = s_inv + kRouteMaxR;
+    const bool publish = blockIdx.x == 0;
+    const int G = topk_group(E);
+    for (int t0 = 0; t0 < n; t0 += kWaves * 64 / G)  // every lane takes part
+      topk_token_t<kRoutePer>(p.route_part, p.route_S, (size_t)n * E, t0 + tid / G, n, E, k,
+                              p.route_renorm, publish ? p.r_idx : s_idx_sink,
+                              publish ? p.r_w : s_w, nullptr, s_idx);
+    __syncthreads();
+    if (wave == 0) {
+      int nbits = 0;
+      while ((1 << nbits) < E) ++nbits;
+      dispatch_wave(s_idx, R, k, E, nbits, s_cnt, s_off, s_perm, s_inv);
+    }
+    __syncthreads();
+    if (publish) {
+      for (int e = tid; e <= E; e += kWaves * 64) {
+        p.r_offsets[e] = s_off[e];
+        if (e < E) p.r_counts[e] = s_cnt[e];
+      }
+      for (int q = tid; q < R; q += kWaves * 64) {
+        p.r_perm[q] = s_perm[q];
+        p.r_inv[q] = s_inv[q];
+      }
+    }
+    perm = s_perm;
+  } else {
+    for (int e = tid; e <= E; e += kWaves * 64) s_off[e] = p.offsets[e];
+  }
 
   // ---- work list: groups of 16 pile rows, prefix over experts ---------------
-  for (int e = tid; e <= E; e += kWaves * 64) s_off[e] = p.offsets[e];
   // The slot table is read once here: a copying wave that loaded it from
   // global memory per tile would wait for all of its copies in flight too
   // (one in-order counter).
@@ -308,7 +362,7 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
       t0 = (gidx - s_gpre[e_cur]) * 16;
       const int t = t0 + r;
       const bool tv = t < m;
-      const int arow = tv ? (p.perm ? p.perm[row0 + t] : row0 + t) : 0;
+      const int arow = tv ? (perm ? perm[row0 + t] : row0 + t) : 0;
       if constexpr (A8) {
         const uint8_t *ap = (const uint8_t *)p.a + (size_t)arow * K;
         const uint8_t *sp = p.as + (size_t)arow * p.sp;
@@ -507,6 +561,12 @@ bool decode_ffn_fits(int d, int d_ff, int E) {
          stage_plan(d_ff, false, E).stages >= 1;
 }
 
+bool decode_route_fold_ok(const FfnArgs &a) {
+  return a.w_dtype == 2 && a.R <= kDecodeMaxRows && decode_ffn_fits(a.d, a.d_ff, a.E) &&
+         a.E <= kRouteMaxE && a.R <= kRouteMaxR && topk_per(a.E) == kRoutePer &&
+         a.n * topk_group(a.E) <= kWaves * 64 && a.perm != nullptr;
+}
+
 hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st) {
   DecodeParams p{};
   p.a = (const uint16_t *)a.a;
@@ -522,6 +582,20 @@ hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st) {
   p.slot = a.slot;
   p.n_slots = a.n_slots;
   p.out = a.h;
+  if (a.route_part) {
+    if (!decode_route_fold_ok(a)) return hipErrorInvalidValue;
+    p.route_part = a.route_part;
+    p.route_S = a.route_S;
+    p.route_n = a.n;
+    p.route_k = a.k;
+    p.route_renorm = a.route_renorm;
+    p.r_idx = a.r_idx;
+    p.r_w = a.r_w;
+    p.r_counts = a.r_counts;
+    p.r_offsets = a.r_offsets;
+    p.r_perm = a.r_perm;
+    p.r_inv = a.r_inv;
+  }
   if (a.act_quant) {
     const size_t rows = (size_t)(a.perm ? a.n : a.R);
     p.as = (const uint8_t *)a.a + mx8_scale_offset(rows, a.d);

@@ -315,11 +315,41 @@ BigGemmParams big_params(const FfnArgs &a, bool up) {
 }  // namespace
 
 // Small batches of MXFP4 experts are bound by reading the weights: they take
-// the weight-streaming kernel instead of the large-tile GEMM.
-constexpr int kDecodeMaxRows = 1024;
+// the weight-streaming kernel instead of the large-tile GEMM (kDecodeMaxRows
+// routed rows at most).
 
 bool use_decode(const FfnArgs &a) {
   return a.w_dtype == 2 && a.R <= kDecodeMaxRows && decode_ffn_fits(a.d, a.d_ff, a.E);
+}
+
+// Tail split of the bf16 down pass: when the pass runs longest first (more
+// than two rounds of blocks) and the last row tiles of the piles fill at
+// most half of the 256 CUs, each of those tiles is computed by two blocks
+// over the two halves of K, so the last round has about twice the blocks,
+// each half as long (one expert per token keeps its fused combine instead).
+struct TailPlan {
+  int splits, bm, bnb;
+};
+
+TailPlan down_tail_plan(const FfnArgs &a) {
+  TailPlan t{1, 0, 0};
+  if (a.w_dtype != 1 || a.act_quant || a.R == 0 || a.k == 1 || !a.split_ok || a.d % 4) return t;
+  if (!big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff)) return t;
+  const TileChoice c = down_tile(a);
+  if (c.splits > 1) return t;
+  const long long piles = a.E < a.R ? a.E : a.R;
+  const long long n_tiles = (a.d + c.bnb - 1) / c.bnb;
+  const long long blocks = ((a.R + c.bm - 1) / c.bm + piles) * n_tiles;
+  if (blocks <= 2 * 256 || piles * n_tiles * 2 > 256 || (a.d_ff + 63) / 64 < 4) return t;
+  t.splits = 2;
+  t.bm = c.bm;
+  t.bnb = c.bnb;
+  return t;
+}
+
+size_t down_tail_bytes(const FfnArgs &a) {
+  const TailPlan t = down_tail_plan(a);
+  return t.splits > 1 ? (size_t)t.splits * a.E * t.bm * a.d * 4 : 0;
 }
 
 int down_split_factor(const FfnArgs &a) {
@@ -384,6 +414,23 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
       return launch_splitk_sum(a.split_part, t.splits, a.R, a.d, a.y_perm, st);
     }
     const bool fuse = a.fuse_y != nullptr && a.k == 1;
+    const TailPlan tp = down_tail_plan(a);
+    if (tp.splits > 1 && a.tail_part && !fuse) {
+      p.tail_splits = tp.splits;
+      p.tail_ksplit = ((a.d_ff + 64 * tp.splits - 1) / (64 * tp.splits)) * 64;
+      p.tail_part = a.tail_part;
+      p.tail_plane = (size_t)a.E * bm * a.d;
+      hipError_t err = launch_big_gemm(p, false, false, false, false, bm, bnb, st);
+      if (err != hipSuccess) return err;
+      if (a.comb_y) {
+        if (fused) *fused = true;
+        return launch_combine_tail(a.y_perm, a.tail_part, tp.splits, p.tail_plane, a.offsets, a.E,
+                                   bm, a.comb_inv, a.comb_w, a.n, a.k, a.d, a.comb_y, a.comb_bf16,
+                                   st);
+      }
+      return launch_tail_sum(a.tail_part, tp.splits, p.tail_plane, a.offsets, a.E, bm, a.d,
+                             a.y_perm, st);
+    }
     if (fuse) {
       p.out = a.fuse_y;
       p.perm_out = a.fuse_perm;

@@ -25,6 +25,15 @@ struct BigGemmParams {
   // and a later kernel adds the planes in split order.
   int splits, ksplit;
   float *part;
+  // Tail split (unsplit down GEMMs run longest first): the last row tile of
+  // each pile is computed by tail_splits blocks over K ranges of tail_ksplit
+  // (a multiple of 64); split s writes its rows of the tile to tail_part +
+  // s * tail_plane, at row e * bm + (row - the tile's first row), [.][N] f32.
+  // The pile outputs of those rows are the sum of the planes in split order
+  // (the combine or launch_tail_sum adds them).
+  int tail_splits, tail_ksplit;
+  float *tail_part;
+  size_t tail_plane;
 };
 
 // up: H = silu(A W1^T) * (A W3^T); down: Yp = H W2^T (or the fused combine).

@@ -80,16 +80,21 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   const int S = UP ? 1 : (p.splits > 1 ? p.splits : 1);
 
   // ---- block -> tile ------------------------------------------------------
-  if (wave == 0) map_block<BM, LPT>(p.offsets, p.E, p.n_tiles, S, lane, &s_t);
+  // The up projection takes balanced row tiles: a pile's blocks then take
+  // about the same time, and the blocks of an XCD that share operands stay
+  // closer in K (measured: L2 hit rate 45% -> 50% on the Mixtral-shaped up).
+  const int S1 = (LPT && !UP && p.tail_splits > 1) ? p.tail_splits : S;
+  if (wave == 0) map_block<BM, LPT, UP>(p.offsets, p.E, p.n_tiles, S, lane, &s_t, S1);
   __syncthreads();
   const int e = s_t.e;
   if (e < 0) return;
   const int row0 = s_t.row0, rows = s_t.rows;
   const int n0 = s_t.nt * (UP ? BNB / 2 : BNB);
-  const int split = s_t.item % S;
+  const int split = s_t.split;
+  const bool tail_split = LPT && !UP && S1 > 1 && s_t.tail;
   // K range of this block: [kbeg, kend), a whole multiple of BK but the end.
-  const int kbeg = S > 1 ? split * p.ksplit : 0;
-  const int kend = S > 1 ? min(K, kbeg + p.ksplit) : K;
+  const int kbeg = S > 1 ? split * p.ksplit : (tail_split ? split * p.tail_ksplit : 0);
+  const int kend = S > 1 ? min(K, kbeg + p.ksplit) : (tail_split ? min(K, kbeg + p.tail_ksplit) : K);
 
   // ---- per-lane DMA offsets -----------------------------------------------
   // Run j of wave w fills LDS chunks q = (4 j + w) * 64 + lane, i.e. row
@@ -353,6 +358,14 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   // column (i/4)*8 + (l/32)*4 + i%4 of the 32-column group: every lane holds
   // runs of four consecutive columns of one row.
   if constexpr (!UP) {
+    if (tail_split) {
+      // This split's partial sums of the pile's last row tile, compactly:
+      // row e * BM + (pile row - row0) of plane `split`.
+      store_f32_tile<T::TM, T::TN, T::WM, T::WN>(
+          acc, p.tail_part + (size_t)split * p.tail_plane + (size_t)e * BM * N, N, 0, rows, n0, wm,
+          wn, lane);
+      return;
+    }
     if (S > 1) {
       // Split K: this block's partial sums go to plane `split` (16-B stores of
       // four columns); a later kernel adds the planes in split order.
@@ -437,11 +450,18 @@ hipError_t launch_big_gemm(const BigGemmParams &p, bool up, bool mx, bool gather
   const int blocks = m_tiles * p.n_tiles * (up ? 1 : (p.splits > 1 ? p.splits : 1));
   // Longest first for unsplit bf16 down GEMMs of three or more rounds (16
   // spare blocks: the two tile lists' per-XCD shares round up separately).
-  const bool lpt = !up && !mx && p.splits <= 1 && blocks > 2 * cu_count();
+  // A tail split (p.tail_splits > 1) runs longest first too; its tail list
+  // has tail_splits blocks per tile.
+  const bool lpt =
+      !up && !mx && p.splits <= 1 && (p.tail_splits > 1 || blocks > 2 * cu_count());
+  if (p.tail_splits > 1 && (up || mx || p.splits > 1 || fuse)) return hipErrorInvalidValue;
+  const int spare = 16 + (p.tail_splits > 1 ? (p.tail_splits - 1) * (p.E < p.R ? p.E : p.R) *
+                                                  p.n_tiles
+                                            : 0);
 #define MOE_BIG(U, M, G, F, A, B)                                                    \
   if (up == U && mx == M && gather == G && fuse == F && bm == A && bnb == B) {      \
     if constexpr (!U && !M)                                                          \
-      if (lpt) return launch_one<U, M, G, F, A, B, true>(p, blocks + 16, st);        \
+      if (lpt) return launch_one<U, M, G, F, A, B, true>(p, blocks + spare, st);     \
     return launch_one<U, M, G, F, A, B, false>(p, blocks, st);                       \
   }
   // up: gather from X or contiguous rows; bf16 or MXFP4 weights

@@ -5,6 +5,8 @@
 // epilogue of the down projection.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -88,6 +90,8 @@ __device__ __forceinline__ int dma_chunk(int wave, int lane) {
 // that share an expert's weights share one L2.
 struct TileSlot {
   int e, row0, rows, nt, item, bm;
+  int split;  // K split of this block (item % its list's split count)
+  int tail;   // LPT: the block is in the list of last row tiles
 };
 
 // LPT (longest first): the tile list is cut in two, the full row tiles of
@@ -96,9 +100,17 @@ struct TileSlot {
 // and runs its full tiles before its last tiles, so the short tiles fill the
 // last round.  The grid needs 16 blocks beyond the tile count (each list's
 // eighths round up separately).
-template <bool LPT = false, typename RowTile>
+// BAL (balanced rows): the ceil(m / bm) row tiles of a pile share its 32-row
+// groups evenly (tile i takes groups [i G / t, (i + 1) G / t) of G), instead
+// of bm-row tiles and a ragged last one, so that a pile's tiles take about
+// the same time and the blocks running on an XCD stay in step through K.
+// S1 (LPT only; 0 = S): K splits of each tile of the last-row-tile list, so
+// that a tail round of few tiles can be spread over more blocks.
+template <bool LPT = false, typename RowTile, bool BAL = false>
 __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int n_tiles, int S,
-                                             int lane, TileSlot *out, RowTile bm_of) {
+                                             int lane, TileSlot *out, RowTile bm_of,
+                                             std::integral_constant<bool, BAL> = {}, int S1 = 0) {
+  if (S1 <= 0) S1 = S;
   const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
   const int eb = lane * per, ee = min(E, eb + per);
   // With one expert per lane (E <= 64) its offsets are loaded once.
@@ -123,7 +135,7 @@ __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int 
   }
   const int incl0 = wave_incl_scan(loc0), incl1 = LPT ? wave_incl_scan(loc1) : 0;
   const int tot0 = __builtin_amdgcn_readlane(incl0, MOE_WAVE - 1) * n_tiles * S;
-  const int tot1 = LPT ? __builtin_amdgcn_readlane(incl1, MOE_WAVE - 1) * n_tiles * S : 0;
+  const int tot1 = LPT ? __builtin_amdgcn_readlane(incl1, MOE_WAVE - 1) * n_tiles * S1 : 0;
   const int b = blockIdx.x;
   const int xcd = b & 7, slot = b >> 3;
   int base0 = 0, base1 = 0;
@@ -138,8 +150,13 @@ __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int 
   }
   const bool last = slot >= cnt0;
   const int item = last ? base1 + slot - cnt0 : base0 + slot;
-  const int L = item / S;
-  if (lane == 0) out->item = item;
+  const int SS = last ? S1 : S;
+  const int L = item / SS;
+  if (lane == 0) {
+    out->item = item;
+    out->split = item % SS;
+    out->tail = last ? 1 : 0;
+  }
   const int incl = last ? incl1 : incl0, mine = last ? loc1 : loc0;
   const int lo = (incl - mine) * n_tiles, hi = incl * n_tiles;
   if (L >= lo && L < hi) {
@@ -153,8 +170,15 @@ __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int 
         const int mloc = last ? te - 1 : loc % c;
         out->e = x;
         out->nt = last ? loc : loc / c;
-        out->row0 = ox + mloc * bm;
-        out->rows = min(bm, m - mloc * bm);
+        if constexpr (BAL) {
+          const int G = (m + 31) / 32;
+          const int g0 = (int)((long long)mloc * G / te), g1 = (int)((long long)(mloc + 1) * G / te);
+          out->row0 = ox + 32 * g0;
+          out->rows = min(m, 32 * g1) - 32 * g0;
+        } else {
+          out->row0 = ox + mloc * bm;
+          out->rows = min(bm, m - mloc * bm);
+        }
         out->bm = bm;
         break;
       }
@@ -163,10 +187,11 @@ __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int 
   }
 }
 
-template <int BM, bool LPT = false>
+template <int BM, bool LPT = false, bool BAL = false>
 __device__ __forceinline__ void map_block(const int32_t *offsets, int E, int n_tiles, int S,
-                                          int lane, TileSlot *out) {
-  map_block_fn<LPT>(offsets, E, n_tiles, S, lane, out, [](int) { return BM; });
+                                          int lane, TileSlot *out, int S1 = 0) {
+  map_block_fn<LPT>(offsets, E, n_tiles, S, lane, out, [](int) { return BM; },
+                    std::integral_constant<bool, BAL>{}, S1);
 }
 
 // f32 stores of a block's accumulators: acc[tm][tn] of wave (wm, wn) holds

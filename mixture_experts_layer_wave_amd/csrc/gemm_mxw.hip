@@ -106,7 +106,7 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
   const int e = t.e;
   const int row0 = t.row0, rows = t.rows;
   const int n0 = t.nt * NR;
-  const int split = t.item % S;
+  const int split = t.split;
   const int kbeg = S > 1 ? split * p.ksplit : 0;
   const int kend = S > 1 ? min(K, kbeg + p.ksplit) : K;
   const int sp = (KB + 3) / 4 * 4;  // activation scale pitch

@@ -82,15 +82,30 @@ struct FfnArgs {
   const int32_t *comb_inv;
   const float *comb_w;
   bool comb_bf16;
+  // Tail split of the down pass (down_tail_bytes > 0): workspace for the
+  // partial sums of each pile's last row tile.
+  float *tail_part;
   // W4A8 mode (MXFP4 weights only): a and h are MXFP8 matrices (E4M3 codes,
   // then E8M0 scales; layout in gemm_mxw.h) of (perm ? n : R) and R rows,
   // and both projections run on the scaled MFMA.
   bool act_quant;
+  // Routing folded into the decode up kernel (decode_route_fold_ok): the
+  // router's route_S partial logit planes [S][n][E]; the up kernel then
+  // writes r_idx, r_w [n][k], r_counts [E], r_offsets [E+1], r_perm [R],
+  // r_inv [n][k] (perm and offsets above must point at r_perm / r_offsets
+  // for the down pass and the combine).
+  const float *route_part;
+  int route_S, route_renorm;
+  int32_t *r_idx, *r_counts, *r_offsets, *r_perm, *r_inv;
+  float *r_w;
 };
 // K splits the down pass takes for these arguments (1 = none); with
 // split_ok set it tells the workspace layout how many partial planes
 // (splits x R x d f32) to reserve.
 int down_split_factor(const FfnArgs &a);
+// Workspace bytes of the down pass's tail split for these arguments (0 when
+// the down pass does not split its tail).
+size_t down_tail_bytes(const FfnArgs &a);
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st);    // A -> h
 // h -> y_perm, or straight into fuse_y; *fused (may be NULL) tells which.
 hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
@@ -103,6 +118,11 @@ int cu_count();
 // weight tiles through an LDS ring.  decode_ffn_fits tells whether the
 // shape is supported.
 bool decode_ffn_fits(int d, int d_ff, int E);
+// The decode up kernel can take the top-k and dispatch of this batch itself
+// (MXFP4 weights on the decode path, E <= 128, n k <= 64, one pass of
+// top-k over the workgroup, rows gathered through perm).
+bool decode_route_fold_ok(const FfnArgs &a);
+constexpr int kDecodeMaxRows = 1024;  // routed rows the decode path takes
 hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st);
 hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st);
 
@@ -115,6 +135,16 @@ hipError_t launch_splitk_combine(const float *part, int S, int R, const int32_t 
 hipError_t launch_splitk_sum(const float *part, int S, int R, int d, float *yp, hipStream_t st);
 hipError_t launch_combine(const float *y_perm, const int32_t *inv, const float *w,
                           int n, int k, int d, void *y, bool out_bf16, hipStream_t st);
+// The same combine when the last row tile of each pile (bm-row tiles from
+// offsets[e]) holds S partial planes tail[s][e * bm + row][d] instead of
+// y_perm rows: those rows are the planes' sum in split order.  d % 4 == 0.
+hipError_t launch_combine_tail(const float *y_perm, const float *tail, int S, size_t plane,
+                               const int32_t *offsets, int E, int bm, const int32_t *inv,
+                               const float *w, int n, int k, int d, void *y, bool out_bf16,
+                               hipStream_t st);
+// y_perm rows of the last row tiles = the sum of their S tail planes.
+hipError_t launch_tail_sum(const float *tail, int S, size_t plane, const int32_t *offsets, int E,
+                           int bm, int d, float *y_perm, hipStream_t st);
 // dst[i] = bf16(src[i]) (round to nearest even) for i < count; both 16-byte
 // aligned.
 hipError_t launch_f32_to_bf16(const float *src, uint16_t *dst, size_t count, hipStream_t st);

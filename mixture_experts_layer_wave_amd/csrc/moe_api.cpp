@@ -20,7 +20,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct WsLayout {
-  size_t logits, idx, w, counts, offsets, perm, inv, dscratch, h, yp, part, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, dscratch, h, yp, part, tail, total;
   int splits;
 };
 
@@ -109,6 +109,7 @@ WsLayout layout(const moe_shape *s, int wdt) {
     L.splits = std::max(L.splits, moe::down_split_factor(q));
   }
   L.part = take(L.splits > 1 ? (size_t)L.splits * R * (size_t)s->d * 4 : 0);
+  L.tail = take(moe::down_tail_bytes(plan_args(s, wdt)));
   L.total = o;
   return L;
 }
@@ -326,6 +327,7 @@ int moe_grouped_ffn(const moe_shape *s, const void *x_perm, int act, const int32
   moe::FfnArgs f = ffn_args(s, a, nullptr, offsets, w, base + L.h, yp);
   f.split_ok = true;
   f.split_part = (float *)(base + L.part);
+  f.tail_part = (float *)(base + L.tail);
   hipError_t e = moe::launch_grouped_ffn(f, hs);
   if (e == hipSuccess && out == MOE_BF16)
     e = moe::launch_f32_to_bf16(yp, (uint16_t *)y_perm, (size_t)s->n * s->k * s->d, hs);
@@ -408,7 +410,13 @@ int forward_impl(const moe_shape *s, const void *x, int act, const void *wg, con
   const int splits = splits_of(s, w->dtype);
   hipError_t e = moe::launch_router_logits(x, wg, bias, logits, s->n, s->d, s->E,
                                            act == MOE_BF16, splits, hs);
-  if (e == hipSuccess && moe::route_small_ok(s->n, s->k, s->E)) {
+  // Small MXFP4 batches: the decode up kernel takes the top-k and the piles
+  // itself (one launch fewer); otherwise top-k and dispatch run first.
+  moe::FfnArgs fold = ffn_args(s, x, perm, offsets, w, nullptr, nullptr);
+  const bool folded = moe::decode_route_fold_ok(fold);
+  if (e == hipSuccess && folded) {
+    // nothing to launch here: the up kernel routes
+  } else if (e == hipSuccess && moe::route_small_ok(s->n, s->k, s->E)) {
     e = moe::launch_route_small(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt, counts,
                                 offsets, perm, inv, hs);
   } else if (e == hipSuccess) {
@@ -431,6 +439,18 @@ int forward_impl(const moe_shape *s, const void *x, int act, const void *wg, con
     moe::FfnArgs f = ffn_args(s, a, perm, offsets, w, base + L.h, yp);
     f.split_ok = true;
     f.split_part = (float *)(base + L.part);
+    f.tail_part = (float *)(base + L.tail);
+    if (folded) {
+      f.route_part = logits;
+      f.route_S = splits;
+      f.route_renorm = renorm_of(s) ? 1 : 0;
+      f.r_idx = idx;
+      f.r_w = wt;
+      f.r_counts = counts;
+      f.r_offsets = offsets;
+      f.r_perm = perm;
+      f.r_inv = inv;
+    }
     f.comb_y = y;
     f.comb_inv = inv;
     f.comb_w = wt;

@@ -53,6 +53,9 @@ SMALL = {
     # registers, on the up projection (K = d) and on the down (K = d_ff)
     "mxfp4-wide-d": small("mxfp4-wide-d", 600, 7232, 4, 2, 96, "mxfp4", 22),
     "mxfp4-wide-ff": small("mxfp4-wide-ff", 600, 128, 4, 2, 7232, "mxfp4", 23),
+    # more than two rounds of down blocks whose last row tiles fill at most
+    # half of the chip: the down pass splits those tiles along K
+    "bf16-tail-split": small("bf16-tail-split", 42000, 512, 2, 2, 256, "bf16", 24),
 }
 
 
