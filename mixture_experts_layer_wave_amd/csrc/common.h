@@ -99,9 +99,10 @@ __device__ __forceinline__ float silu(float g) {
 
 // E8M0 scale code -> float (2^(s-127)); 0 -> 2^-127 (subnormal), 255 -> NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  if (s == 0) return __uint_as_float(0x00400000u);
-  if (s == 255) return __uint_as_float(0x7fc00000u);
-  return __uint_as_float(s << 23);
+  // branch-free: s << 23 is the value for 1..254; s = 0 (2^-127, a float32
+  // subnormal) and s = 255 (NaN) both add the top mantissa bit
+  const uint32_t edge = ((s + 1u) & 255u) <= 1u;
+  return __uint_as_float((s << 23) | (edge << 22));
 }
 
 // ---- MXFP8 encoding (OCP MX v1.0: E4M3 elements, one E8M0 scale per 32) --

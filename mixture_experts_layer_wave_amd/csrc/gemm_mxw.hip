@@ -228,23 +228,42 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
     ws_row[j] = (b >= NR ? RBP : 0) + (b % NR) * KB;
   }
 
-  // One K step: scales, then the fragments of each 64-K MFMA step (those of
+  // Weight scales of K step kt (the whole-K run is in LDS from the tile's
+  // start, so they are read before the step's barrier, off the critical
+  // path).  A block past the K range multiplies zero codes; its byte
+  // (another row's) is replaced by 1.0 so that a NaN scale cannot leak in.
+  const int kbend = (kend + 31) / 32;
+  auto load_wsc = [&](auto actc, int kt, uint32_t (&wsc)[T::TN][T::NKK]) {
+    constexpr int ACT = decltype(actc)::value;
+    if constexpr (ACT > 0) {
+      const int blk0 = kbeg / 32 + kt * T::SB + lg;
+#pragma unroll
+      for (int tn = 0; tn < T::TN; ++tn)
+#pragma unroll
+        for (int kk = 0; kk < T::NKK; ++kk) {
+          const int blk = blk0 + 2 * kk;
+          const uint32_t v = wscl[ws_row[tn] + min(blk, kbend - 1)];
+          wsc[tn][kk] = blk < kbend ? v : 127u;
+        }
+    }
+  };
+  // One K step: activation scales (W4A8), then the fragments of each 64-K MFMA step (those of
   // step kk + 1 read while step kk multiplies; the copies of a later K step
   // are issued after the first reads).  ACT (a compile-time count) is the
   // number of this wave's 32-row groups that hold pile rows; the empty groups
   // of a ragged last row tile are neither read nor multiplied.  A wave with
   // ACT = 0 still copies and meets every barrier.
-  auto step = [&](auto actc, int kt, int stage, int kt_issue, int stage_issue) {
+  auto step = [&](auto actc, int kt, int stage, int kt_issue, int stage_issue,
+                  const uint32_t (&wsc)[T::TN][T::NKK]) {
     constexpr int ACT = decltype(actc)::value;
     constexpr int NKK = T::NKK;
     const uint8_t *sa = smem + stage * T::STAGE;
     const uint8_t *sb = sa + T::A_BYTES;
     const uint8_t *ss = sb + T::B_BYTES;
     const int blk0 = kbeg / 32 + kt * T::SB + lg;  // K block of this lane's half, k-step 0
-    const int kbend = (kend + 31) / 32;
     // activation scales: word kk / 2 of the row, this half's byte moved to
     // byte 0 (k-step kk even) or 2 (odd)
-    uint32_t asc[T::TM][SD], wsc[T::TN][NKK];
+    uint32_t asc[T::TM][SD];
     if constexpr (A8) {
 #pragma unroll
       for (int tm = 0; tm < ACT; ++tm) {
@@ -253,15 +272,6 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
 #pragma unroll
         for (int w = 0; w < SD; ++w) asc[tm][w] = ((const uint32_t *)q)[w] >> (8 * lg);
       }
-    }
-    if constexpr (ACT > 0) {
-#pragma unroll
-      for (int tn = 0; tn < T::TN; ++tn)
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          // a block past the K range multiplies zero codes; its byte (another
-          // row's) is replaced by 1.0 so that a NaN scale cannot leak in
-          wsc[tn][kk] = blk0 + 2 * kk < kbend ? wscl[ws_row[tn] + blk0 + 2 * kk] : 127u;
     }
     auto frags = [&](int kk, v8i *af, v8i *bf) {
 #pragma unroll
@@ -362,9 +372,13 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
   const int nk = (kend - kbeg + BK - 1) / BK;
   auto kloop = [&](auto actc) {
     for (int kt = 0; kt < nk; ++kt) {
+      // the scale run lands with step 0's copies: read it after that barrier
+      uint32_t wsc[T::TN][T::NKK];
+      if (kt > 0) load_wsc(actc, kt, wsc);
       wait_vmcnt<(NST - 2) * T::NV>();
       __syncthreads();
-      step(actc, kt, kt % NST, kt + NST - 1, (kt + NST - 1) % NST);
+      if (kt == 0) load_wsc(actc, kt, wsc);
+      step(actc, kt, kt % NST, kt + NST - 1, (kt + NST - 1) % NST, wsc);
     }
   };
 #pragma unroll
