@@ -106,10 +106,17 @@ struct TileSlot {
 // the same time and the blocks running on an XCD stay in step through K.
 // S1 (LPT only; 0 = S): K splits of each tile of the last-row-tile list, so
 // that a tail round of few tiles can be spread over more blocks.
+// RG (list 0 only; 0 = off): a pile's tiles are taken in groups of RG row
+// tiles, column tile by column tile within a group, so that the blocks
+// running together on an XCD share both the group's pile rows (across
+// column tiles) and each column tile's weights (across the group's row
+// tiles) in L2; without it a large pile's rows are streamed again for every
+// column tile.
 template <bool LPT = false, typename RowTile, bool BAL = false>
 __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int n_tiles, int S,
                                              int lane, TileSlot *out, RowTile bm_of,
-                                             std::integral_constant<bool, BAL> = {}, int S1 = 0) {
+                                             std::integral_constant<bool, BAL> = {}, int S1 = 0,
+                                             int RG = 0) {
   if (S1 <= 0) S1 = S;
   const int per = (E + MOE_WAVE - 1) / MOE_WAVE;
   const int eb = lane * per, ee = min(E, eb + per);
@@ -167,9 +174,15 @@ __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int 
       const int bm = bm_of(m), te = (m + bm - 1) / bm, c = in_list(te, last);
       if (L < acc + c * n_tiles) {
         const int loc = L - acc;
-        const int mloc = last ? te - 1 : loc % c;
+        int mloc = last ? te - 1 : loc % c;
         out->e = x;
         out->nt = last ? loc : loc / c;
+        if (RG > 0 && !last) {
+          const int grp = loc / (RG * n_tiles), within = loc - grp * RG * n_tiles;
+          const int gr = min(RG, c - grp * RG);  // row tiles in this group
+          out->nt = within / gr;
+          mloc = grp * RG + within % gr;
+        }
         if constexpr (BAL) {
           const int G = (m + 31) / 32;
           const int g0 = (int)((long long)mloc * G / te), g1 = (int)((long long)(mloc + 1) * G / te);

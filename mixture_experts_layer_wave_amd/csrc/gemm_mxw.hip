@@ -476,6 +476,8 @@ __global__ __launch_bounds__(kNT, 1) void mxw_gemm_kernel(MxwParams p) {
 // The down pass runs its tiles longest first (measured 0.5-1.3% off the Zipf
 // layer's step; the up pass, 0.6% slower that way, keeps the plain order).
 constexpr int kMixedSmallRows = 64;
+// Row tiles per group in the up pass's tile order (map_block_fn RG).
+constexpr int kMixedRowGroup = 4;
 template <bool UP, bool GATHER>
 __global__ __launch_bounds__(kNT, 1) void mxw16_mixed_kernel(MxwParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -484,7 +486,8 @@ __global__ __launch_bounds__(kNT, 1) void mxw16_mixed_kernel(MxwParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (wave == 0)
     map_block_fn<!UP>(p.offsets, p.E, p.n_tiles, 1, lane, &s_t,
-                 [](int m) { return m <= kMixedSmallRows ? kMixedSmallRows : 128; });
+                      [](int m) { return m <= kMixedSmallRows ? kMixedSmallRows : 128; },
+                      std::integral_constant<bool, false>{}, 0, UP ? kMixedRowGroup : 0);
   __syncthreads();
   if (s_t.e < 0) return;
   if (s_t.bm == kMixedSmallRows)
@@ -621,7 +624,10 @@ bool mxw16_mixed_fits(bool up, int K) {
 
 hipError_t launch_mxw16_mixed(const MxwParams &p, bool up, bool gather, hipStream_t st) {
   if (p.K > kW4A8MaxK || p.K % 32 || !mxw16_mixed_fits(up, p.K)) return hipErrorInvalidValue;
-  const int m_tiles = (p.R + kMixedSmallRows - 1) / kMixedSmallRows + (p.E < p.R ? p.E : p.R);
+  // Row tiles: a pile of m <= 64 rows has one, a larger one ceil(m / 128) <
+  // m / 128 + 1, so at most (non-empty piles) + R / 128 in all; blocks past
+  // the tile count exit after the map.
+  const int m_tiles = (p.R + 127) / 128 + (p.E < p.R ? p.E : p.R);
   // The down pass runs longest first (map_block_fn): 16 spare blocks.
   const int blocks = m_tiles * p.n_tiles + (up ? 0 : 16);
   const int lds = up ? std::max(lds_bytes<true, kMixedSmallRows, 2, 256, false>(p.K),
