@@ -199,20 +199,33 @@ def main():
         torch.cuda.synchronize()
     launches = max(1, args.steps // per_launch)
     steps_timed = launches * per_launch
-    # One event per launch boundary on the launch stream: the launches run back
-    # to back, and the per-step spread (p10/p50/p90) comes from the same run.
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
-    wall0 = time.perf_counter()
-    marks[0].record(stream)
-    for i in range(launches):
+
+    def launch(i):
         if args.graph:
             graph.replay()
         else:
             step(i)
-        marks[i + 1].record(stream)
+
+    # The timed steps run back to back between two events on the launch
+    # stream (an event between steps costs a few microseconds, a tenth of a
+    # small decode step).
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(launches):
+        launch(i)
+    t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms_per_step = marks[0].elapsed_time(marks[-1]) / steps_timed
+    ms_per_step = t0.elapsed_time(t1) / steps_timed
+    # The per-step spread (p10/p50/p90) comes from a second pass with an
+    # event at every launch boundary (so it includes their cost).
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(launches + 1)]
+    marks[0].record(stream)
+    for i in range(launches):
+        launch(i)
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
     per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(launches)]) / per_launch
     pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
     log(f"[bench] {steps_timed} steps{' in graph replays' if args.graph else ''}: {ms_per_step * 1e3:.1f} us/step (wall {wall / steps_timed * 1e6:.1f} us/step)")

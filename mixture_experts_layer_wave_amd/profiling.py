@@ -216,16 +216,19 @@ def cmd_mfma(a):
           f"counted/alg {counted / alg:.3f}")
 
 
-def read_traffic(workload: str, kernel_family: str, act_quant: str | None = None):
-    """(bytes per launch, path) from profiles/ if its sources digest still
-    matches the current sources of the kernel, else (None, reason)."""
+def read_traffic(workload: str, kernel_family: str, act_quant: str | None = None, up: bool = True):
+    """(bytes per launch, path) of the up (or down) kernel of the family from
+    profiles/ if its sources digest still matches the current sources of the
+    kernel, else (None, reason).  Every kernel family takes UP as its first
+    template argument, so the up kernel is `family<true`."""
+    want = f"{kernel_family}<{'true' if up else 'false'}"
     for path in sorted(glob.glob(os.path.join(PROFILES, "*traffic*.md"))):
         kv = {}
         for line in open(path):
             if ":" in line and not line.startswith(("|", "#", " ")):
                 k, _, v = line.partition(":")
                 kv[k.strip()] = v.strip()
-        if kv.get("workload") != workload or kernel_family not in kv.get("kernel", ""):
+        if kv.get("workload") != workload or not kv.get("kernel", "").startswith(want):
             continue
         if kv.get("act_quant", "none") != (act_quant or "none"):
             continue

@@ -1,5 +1,7 @@
 """Host-side checks of the rocprofv3 summary helpers used by bench.py."""
 
+import os
+
 from mixture_experts_layer_wave_amd import profiling as P
 
 
@@ -39,6 +41,27 @@ def test_read_traffic_keeps_the_modes_apart(tmp_path, monkeypatch):
     (tmp_path / "b_traffic.md").write_text("workload: w1\ntraffic_bytes_per_launch: 5\n" + tail)
     assert P.read_traffic("w1", fam, "mxfp8")[0] == 7.0
     assert P.read_traffic("w1", fam)[0] == 5.0
+
+
+def test_read_traffic_keeps_up_and_down_apart(tmp_path, monkeypatch):
+    # the down kernel's summary sorts first; the roofline line needs the up kernel's
+    monkeypatch.setattr(P, "PROFILES", str(tmp_path))
+    fam = "big_gemm_kernel"
+    good = P.sources_digest(fam)
+    (tmp_path / "big_gemm_kernel_down_traffic_w1.md").write_text(
+        f"workload: w1\nkernel: big_gemm_kernel<false, false, 320>\ntraffic_bytes_per_launch: 3\nsources_sha256: {good}\n")
+    (tmp_path / "big_gemm_kernel_up_traffic_w1.md").write_text(
+        f"workload: w1\nkernel: big_gemm_kernel<true, false, 320>\ntraffic_bytes_per_launch: 15\nsources_sha256: {good}\n")
+    assert P.read_traffic("w1", fam) == (15.0, os.path.relpath(str(tmp_path / "big_gemm_kernel_up_traffic_w1.md"), P.ROOT))
+    assert P.read_traffic("w1", fam, up=False)[0] == 3.0
+
+
+def test_committed_up_traffic_is_the_up_kernel():
+    for wl in ("mixtral-top2-n8192-d4096-e8-ff14336-bf16", "e128-top4-mxfp4-decode-n1"):
+        fam = "big_gemm_kernel" if "mixtral" in wl else "mx_decode_kernel"
+        val, src = P.read_traffic(wl, fam)
+        if val is not None:
+            assert "_up_traffic_" in src
 
 
 def test_mfma_summary_arithmetic(tmp_path):
