@@ -14,8 +14,12 @@ namespace moe {
 int router_splits(int n, int E, int d);
 // part[s][n][E] = x[n][d] . wg[E][d] over split s's K range (+ bias[E] in
 // split 0); x, wg are bf16 (is_bf16) or f32 (f32 always uses one split).
+// Large batches get the splits summed in order inside the launch: then one
+// plane, part[0] = p0 + p1 + ..., with the bits the top-k pass would form.
 hipError_t launch_router_logits(const void *x, const void *wg, const float *bias, float *part,
                                 int n, int d, int E, bool is_bf16, int splits, hipStream_t st);
+// Planes launch_router_logits writes for these arguments (1 or splits).
+int router_planes(int n, int E, int d, bool is_bf16, int splits);
 // idx/w[n][k] from the summed logits: softmax over E, top-k, optional
 // renorm; logits[n][E] (may be NULL) receives the summed logits.
 hipError_t launch_router_topk(const float *part, int splits, int n, int E, int k, bool renorm,

@@ -410,6 +410,8 @@ int forward_impl(const moe_shape *s, const void *x, int act, const void *wg, con
   const int splits = splits_of(s, w->dtype);
   hipError_t e = moe::launch_router_logits(x, wg, bias, logits, s->n, s->d, s->E,
                                            act == MOE_BF16, splits, hs);
+  // planes of partial logits the routing sums (the router may sum them)
+  const int planes = moe::router_planes(s->n, s->E, s->d, act == MOE_BF16, splits);
   // Small MXFP4 batches: the decode up kernel takes the top-k and the piles
   // itself (one launch fewer); otherwise top-k and dispatch run first.
   moe::FfnArgs fold = ffn_args(s, x, perm, offsets, w, nullptr, nullptr);
@@ -417,10 +419,10 @@ int forward_impl(const moe_shape *s, const void *x, int act, const void *wg, con
   if (e == hipSuccess && folded) {
     // nothing to launch here: the up kernel routes
   } else if (e == hipSuccess && moe::route_small_ok(s->n, s->k, s->E)) {
-    e = moe::launch_route_small(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt, counts,
+    e = moe::launch_route_small(logits, planes, s->n, s->E, s->k, renorm_of(s), idx, wt, counts,
                                 offsets, perm, inv, hs);
   } else if (e == hipSuccess) {
-    e = moe::launch_router_topk(logits, splits, s->n, s->E, s->k, renorm_of(s), idx, wt,
+    e = moe::launch_router_topk(logits, planes, s->n, s->E, s->k, renorm_of(s), idx, wt,
                                 nullptr, hs);
     if (e == hipSuccess)
       e = moe::launch_dispatch(idx, s->n, s->k, s->E, counts, offsets, perm, inv,
@@ -442,7 +444,7 @@ int forward_impl(const moe_shape *s, const void *x, int act, const void *wg, con
     f.tail_part = (float *)(base + L.tail);
     if (folded) {
       f.route_part = logits;
-      f.route_S = splits;
+      f.route_S = planes;
       f.route_renorm = renorm_of(s) ? 1 : 0;
       f.r_idx = idx;
       f.r_w = wt;

@@ -26,15 +26,17 @@ namespace {
 // experts, z = K splits.  Split z writes part[z][n][E] over K range
 // [z * kc, (z + 1) * kc); split 0 adds the bias.  The top-k pass sums the
 // splits in order.
+// The wave tile of K split z (tokens t0.., experts e0..): acc0 + acc1
+// (+ bias for z = 0), per lane rows (l / 16) * 4 + i of each token block a
+// and column l % 16 of each expert block b.
 template <int TT, int ET>
-__global__ __launch_bounds__(256) void router_logits_bf16_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg,
-    const float *__restrict__ bias, float *__restrict__ part, int n, int d, int E, int kc) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * 16 * TT;
-  const int e0 = (blockIdx.y * 4 + wave) * 16 * ET;
-  if (e0 >= E) return;  // no barriers in this kernel
-  const int kbeg = blockIdx.z * kc, kend = min(d, kbeg + kc);
+__device__ __forceinline__ void router_split_tile(const uint16_t *__restrict__ x,
+                                                  const uint16_t *__restrict__ wg,
+                                                  const float *__restrict__ bias, int n, int d,
+                                                  int E, int kc, int t0, int e0, int z,
+                                                  f32x4 (&res)[TT][ET]) {
+  const int lane = threadIdx.x & 63;
+  const int kbeg = z * kc, kend = min(d, kbeg + kc);
   const int row = lane & 15, kg = lane >> 4;
   const uint16_t *xr[TT], *wr[ET];
   bool tv[TT], ev[ET];
@@ -56,29 +58,55 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
 #pragma unroll
     for (int b = 0; b < ET; ++b) acc0[a][b] = acc1[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  int k0 = kbeg;
-  for (; k0 + 64 <= kend; k0 += 64) {
+  // 64-deep steps, the next step's fragments loaded while this one's MFMAs
+  // run (the addresses of invalid rows are clamped to row 0, so every load
+  // is in bounds and is issued; invalid rows are zeroed after the load).
+  struct Frag {
     u32x4 a0[TT], a1[TT], b0[ET], b1[ET];
+  };
+  auto load = [&](int k, Frag &f) {
 #pragma unroll
     for (int a = 0; a < TT; ++a) {
-      a0[a] = tv[a] ? *(const u32x4 *)(xr[a] + k0) : zero;
-      a1[a] = tv[a] ? *(const u32x4 *)(xr[a] + k0 + 32) : zero;
+      f.a0[a] = *(const u32x4 *)(xr[a] + k);
+      f.a1[a] = *(const u32x4 *)(xr[a] + k + 32);
     }
 #pragma unroll
     for (int b = 0; b < ET; ++b) {
-      b0[b] = ev[b] ? *(const u32x4 *)(wr[b] + k0) : zero;
-      b1[b] = ev[b] ? *(const u32x4 *)(wr[b] + k0 + 32) : zero;
+      f.b0[b] = *(const u32x4 *)(wr[b] + k);
+      f.b1[b] = *(const u32x4 *)(wr[b] + k + 32);
     }
+#pragma unroll
+    for (int a = 0; a < TT; ++a)
+      if (!tv[a]) f.a0[a] = f.a1[a] = zero;
+#pragma unroll
+    for (int b = 0; b < ET; ++b)
+      if (!ev[b]) f.b0[b] = f.b1[b] = zero;
+  };
+  auto mfma = [&](const Frag &f) {
 #pragma unroll
     for (int a = 0; a < TT; ++a)
 #pragma unroll
       for (int b = 0; b < ET; ++b) {
         acc0[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, a0[a]), __builtin_bit_cast(bf16x8, b0[b]), acc0[a][b], 0, 0, 0);
+            __builtin_bit_cast(bf16x8, f.a0[a]), __builtin_bit_cast(bf16x8, f.b0[b]), acc0[a][b], 0, 0, 0);
         acc1[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, a1[a]), __builtin_bit_cast(bf16x8, b1[b]), acc1[a][b], 0, 0, 0);
+            __builtin_bit_cast(bf16x8, f.a1[a]), __builtin_bit_cast(bf16x8, f.b1[b]), acc1[a][b], 0, 0, 0);
       }
+  };
+  const int nfull = (kend - kbeg) / 64;
+  if (nfull > 0) {
+    Frag p, q;
+    load(kbeg, p);
+    for (int i = 0; i < nfull; i += 2) {
+      if (i + 1 < nfull) load(kbeg + 64 * (i + 1), q);
+      mfma(p);
+      if (i + 1 < nfull) {
+        if (i + 2 < nfull) load(kbeg + 64 * (i + 2), p);
+        mfma(q);
+      }
+    }
   }
+  int k0 = kbeg + 64 * nfull;
   for (; k0 < kend; k0 += 32) {
     const bool kv = k0 + kg * 8 < kend;  // d % 8 == 0: a chunk is all in or all out
     u32x4 a0[TT], b0[ET];
@@ -93,20 +121,93 @@ __global__ __launch_bounds__(256) void router_logits_bf16_kernel(
         acc0[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, a0[a]), __builtin_bit_cast(bf16x8, b0[b]), acc0[a][b], 0, 0, 0);
   }
+#pragma unroll
+  for (int b = 0; b < ET; ++b) {
+    const float bb = (bias && z == 0 && ev[b]) ? bias[e0 + 16 * b + row] : 0.f;
+#pragma unroll
+    for (int a = 0; a < TT; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) res[a][b][i] = acc0[a][b][i] + acc1[a][b][i] + bb;
+  }
+}
+
+template <int TT, int ET>
+__global__ __launch_bounds__(256) void router_logits_bf16_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg,
+    const float *__restrict__ bias, float *__restrict__ part, int n, int d, int E, int kc) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t0 = blockIdx.x * 16 * TT;
+  const int e0 = (blockIdx.y * 4 + wave) * 16 * ET;
+  if (e0 >= E) return;  // no barriers in this kernel
+  const int row = lane & 15, kg = lane >> 4;
+  f32x4 res[TT][ET];
+  router_split_tile<TT, ET>(x, wg, bias, n, d, E, kc, t0, e0, blockIdx.z, res);
   // Output layout of a 16x16 tile: lane l holds rows (l / 16) * 4 + i, column l % 16.
   float *out = part + (size_t)blockIdx.z * n * E;
 #pragma unroll
   for (int b = 0; b < ET; ++b) {
-    if (!ev[b]) continue;
     const int e = e0 + 16 * b + row;
-    const float bb = (bias && blockIdx.z == 0) ? bias[e] : 0.f;
+    if (e >= E) continue;
 #pragma unroll
     for (int a = 0; a < TT; ++a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tt = t0 + 16 * a + kg * 4 + i;
-        if (tt < n) out[(size_t)tt * E + e] = acc0[a][b][i] + acc1[a][b][i] + bb;
+        if (tt < n) out[(size_t)tt * E + e] = res[a][b][i];
       }
+  }
+}
+
+// The same logits with the K splits summed inside the launch: one block per
+// tile of 16 TT tokens x 16 ET experts, its NW waves computing splits
+// NW r + w in round r (each exactly as router_logits_bf16_kernel does); the
+// block adds the splits in order, p0 + p1 + ... (the order in which the
+// top-k pass sums split planes), and writes one plane, so the logits carry
+// the same bits while the partial planes never reach memory.
+template <int TT, int ET, int NW>
+__global__ __launch_bounds__(NW * 64) void router_logits_sum_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg,
+    const float *__restrict__ bias, float *__restrict__ logits, int n, int d, int E, int kc,
+    int S) {
+  constexpr int NT = NW * 64;
+  constexpr int TR = 16 * TT, TC = 16 * ET, TILE = TR * TC, PER = (TILE + NT - 1) / NT;
+  __shared__ float pl[NW][TILE];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int row = lane & 15, kg = lane >> 4;
+  const int t0 = blockIdx.x * TR, e0 = blockIdx.y * TC;
+  float tot[PER];
+  for (int r = 0; r * NW < S; ++r) {
+    const int z = NW * r + wave;
+    if (z < S) {
+      f32x4 res[TT][ET];
+      router_split_tile<TT, ET>(x, wg, bias, n, d, E, kc, t0, e0, z, res);
+#pragma unroll
+      for (int a = 0; a < TT; ++a)
+#pragma unroll
+        for (int b = 0; b < ET; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pl[wave][(16 * a + kg * 4 + i) * TC + 16 * b + row] = res[a][b][i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int q = tid + NT * j;
+      if (q < TILE) {
+        for (int u = 0; u < NW && NW * r + u < S; ++u) {
+          if (r == 0 && u == 0)
+            tot[j] = pl[0][q];
+          else
+            tot[j] += pl[u][q];
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int q = tid + NT * j;
+    const int tt = t0 + q / TC, e = e0 + q % TC;
+    if (q < TILE && tt < n && e < E) logits[(size_t)tt * E + e] = tot[j];
   }
 }
 
@@ -166,12 +267,31 @@ int router_splits(int n, int E, int d) {
   return (d + kc - 1) / kc;  // splits that the rounded K range actually yields
 }
 
+// Large batches get the logits of all K splits summed inside the launch
+// (one plane out); small ones (decode) keep one block per split, whose
+// planes the top-k pass sums (more blocks for few tokens).
+int router_planes(int n, int E, int d, bool is_bf16, int splits) {
+  (void)E;
+  return (is_bf16 && d % 8 == 0 && n >= 256) ? 1 : splits;
+}
+
 hipError_t launch_router_logits(const void *x, const void *wg, const float *bias, float *part,
                                 int n, int d, int E, bool is_bf16, int splits, hipStream_t st) {
   if (is_bf16 && d % 8 == 0) {
     const int kc = split_kc(d, splits);
     const int S = (d + kc - 1) / kc;
     const uint16_t *xb = (const uint16_t *)x, *wb = (const uint16_t *)wg;
+    if (router_planes(n, E, d, is_bf16, splits) == 1 && S > 1) {
+      // eight waves (splits) per round: 64 KB of planes for the wide tile
+      if (E > 16) {
+        dim3 grid((n + 31) / 32, (E + 63) / 64);
+        router_logits_sum_kernel<2, 4, 8><<<grid, 512, 0, st>>>(xb, wb, bias, part, n, d, E, kc, S);
+      } else {
+        dim3 grid((n + 15) / 16, (E + 15) / 16);
+        router_logits_sum_kernel<1, 1, 8><<<grid, 512, 0, st>>>(xb, wb, bias, part, n, d, E, kc, S);
+      }
+      return hipGetLastError();
+    }
     // Wave tiles of 32 tokens x 64 experts for wide routers on large
     // batches (the 128-expert prefill step 10 us faster), else 16 x 16.  A
     // 64 x 16 tile for E <= 16 measured 1% slower on the 8-expert layers.
