@@ -476,7 +476,8 @@ __global__ __launch_bounds__(kNT, 1) void mxw_gemm_kernel(MxwParams p) {
 // The down pass runs its tiles longest first (measured 0.5-1.3% off the Zipf
 // layer's step; the up pass, 0.6% slower that way, keeps the plain order).
 constexpr int kMixedSmallRows = 64;
-// Row tiles per group in the up pass's tile order (map_block_fn RG).
+// Row tiles per group in the tile order of both passes (map_block_fn RG;
+// in the down pass's longest-first order, of its full row tiles).
 constexpr int kMixedRowGroup = 4;
 template <bool UP, bool GATHER>
 __global__ __launch_bounds__(kNT, 1) void mxw16_mixed_kernel(MxwParams p) {
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(kNT, 1) void mxw16_mixed_kernel(MxwParams p) {
   if (wave == 0)
     map_block_fn<!UP>(p.offsets, p.E, p.n_tiles, 1, lane, &s_t,
                       [](int m) { return m <= kMixedSmallRows ? kMixedSmallRows : 128; },
-                      std::integral_constant<bool, false>{}, 0, UP ? kMixedRowGroup : 0);
+                      std::integral_constant<bool, false>{}, 0, kMixedRowGroup);
   __syncthreads();
   if (s_t.e < 0) return;
   if (s_t.bm == kMixedSmallRows)
