@@ -202,9 +202,9 @@ __device__ __forceinline__ void map_block_fn(const int32_t *offsets, int E, int 
 
 template <int BM, bool LPT = false, bool BAL = false>
 __device__ __forceinline__ void map_block(const int32_t *offsets, int E, int n_tiles, int S,
-                                          int lane, TileSlot *out, int S1 = 0) {
+                                          int lane, TileSlot *out, int S1 = 0, int RG = 0) {
   map_block_fn<LPT>(offsets, E, n_tiles, S, lane, out, [](int) { return BM; },
-                    std::integral_constant<bool, BAL>{}, S1);
+                    std::integral_constant<bool, BAL>{}, S1, RG);
 }
 
 // f32 stores of a block's accumulators: acc[tm][tn] of wave (wm, wn) holds
