@@ -239,9 +239,17 @@ TileChoice mxw16_tile(const FfnArgs &a, bool up) {
   return TileChoice{0, 0, 0, 0};
 }
 
+// W4A16 up projection on two four-wave workgroups per CU (mxw16_pair_kernel):
+// the 128-expert Zipf layer 2.5% faster than with the eight-wave kernel (the
+// up pass alone ~14%); its down pass was slower that way and keeps the
+// eight-wave kernel.
+constexpr bool kMxw16Pair = true;
+
 hipError_t launch_mxw_up(const FfnArgs &a, hipStream_t st) {
   MxwParams p = mxw_params(a, true);
   p.n_tiles = (a.d_ff + 127) / 128;
+  if (!a.act_quant && kMxw16Pair && mxw16_pair_fits(true, a.d))
+    return launch_mxw16_pair(p, true, a.perm != nullptr, st);
   if (!a.act_quant && mxw16_mixed_fits(true, a.d))
     return launch_mxw16_mixed(p, true, a.perm != nullptr, st);
   TileChoice t;

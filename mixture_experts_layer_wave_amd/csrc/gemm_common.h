@@ -51,12 +51,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 //   512- and 256-B rows: chunk c of row r at c ^ (r % 16)
 //   128-B rows: chunk c of row r at c ^ ((r / 2) % 8)
 //    64-B rows: chunk c of row r at c ^ ((r / 4) % 4)
+//    32-B rows: chunk c of row r at c ^ ((r / 8) % 2)
 template <int ROWB>
 __device__ __forceinline__ int swz_key(int row) {
-  static_assert(ROWB == 512 || ROWB == 256 || ROWB == 128 || ROWB == 64, "row bytes");
+  static_assert(ROWB == 512 || ROWB == 256 || ROWB == 128 || ROWB == 64 || ROWB == 32,
+                "row bytes");
   if constexpr (ROWB >= 256) return row & 15;
   if constexpr (ROWB == 128) return (row >> 1) & 7;
-  return (row >> 2) & 3;
+  if constexpr (ROWB == 64) return (row >> 2) & 3;
+  return (row >> 3) & 1;
 }
 template <int ROWB>
 __device__ __forceinline__ int swz(int row, int chunk) {
@@ -239,7 +242,7 @@ __device__ __forceinline__ void store_f32_tile(const f32x16 (&acc)[TM][TN], floa
 // tile's OC outputs.  Values are staged through LDS (8-B writes of four
 // columns) so that global stores are 16-B pieces of rows; the caller has
 // made the stages free (barrier).  out is [R][N] bf16 with N % 8 == 0.
-template <int TM, int TN, int WM, int WN, int BM, int OC>
+template <int TM, int TN, int WM, int WN, int BM, int OC, int NT = kNT>
 __device__ __forceinline__ void store_swiglu_bf16_tile(const f32x16 (&acc)[TM][TN], uint8_t *smem,
                                                        uint16_t *out, int N, int row0, int rows,
                                                        int n0, int wm, int wn, int lane, int tid) {
@@ -262,7 +265,7 @@ __device__ __forceinline__ void store_swiglu_bf16_tile(const f32x16 (&acc)[TM][T
   }
   __syncthreads();
   constexpr int CH = OC / 8;  // 16-B chunks per row
-  for (int idx = tid; idx < BM * CH; idx += kNT) {
+  for (int idx = tid; idx < BM * CH; idx += NT) {
     const int r = idx / CH, ch = idx % CH;
     const int col = n0 + ch * 8;
     if (r < rows && col < N)  // N % 8 == 0: a chunk is all in or all out

@@ -58,6 +58,10 @@ bool mxw_fits(bool up, bool a8, int bm, int bk, int K);
 // steps (no K split).
 bool mxw16_mixed_fits(bool up, int K);
 hipError_t launch_mxw16_mixed(const MxwParams &p, bool up, bool gather, hipStream_t st);
+// The same tile list on two four-wave workgroups per CU with 64-deep steps
+// (64-row tiles with three stages, 128-row tiles with two).
+bool mxw16_pair_fits(bool up, int K);
+hipError_t launch_mxw16_pair(const MxwParams &p, bool up, bool gather, hipStream_t st);
 hipError_t launch_mxw_gemm(const MxwParams &p, bool up, bool gather, bool a8, int bm, int bk,
                            hipStream_t st);
 

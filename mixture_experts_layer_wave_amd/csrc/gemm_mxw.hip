@@ -57,26 +57,34 @@ using namespace gemm;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-// Tile of BM pile rows x 256 weight rows, K step BK (128 or 256: 64 or 128
-// bytes of each weight row per step), NST LDS stages.
-template <int BM_, int NST_, int BK_, bool A8_>
+// Tile of BM pile rows x 256 weight rows, K step BK (64, 128 or 256: 32, 64
+// or 128 bytes of each weight row per step), NST LDS stages, NW waves per
+// block arranged 2 x NW/2.  WSS: the weight scales travel with each step
+// (an aligned pair of 4-B words per weight row holding the step's BK/32 = 4
+// scale bytes) instead of one run over the whole K range per tile, which
+// makes the LDS of a tile independent of K.
+template <int BM_, int NST_, int BK_, bool A8_, int NW_ = kNW, bool WSS_ = false>
 struct T8 {
-  static constexpr int BM = BM_, BNB = 256, BK = BK_, NST = NST_;
-  static constexpr bool A8 = A8_;
-  static constexpr int WM = BM / 2, WN = BNB / (kNW / 2);
+  static constexpr int BM = BM_, BNB = 256, BK = BK_, NST = NST_, NW = NW_, NT = NW_ * 64;
+  static constexpr bool A8 = A8_, WSS = WSS_;
+  static constexpr int WM = BM / 2, WN = BNB / (NW / 2);
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int EA = A8 ? 1 : 2;  // bytes per activation element
   static constexpr int ROWA = BK * EA, ROWB = BK / 2;  // LDS bytes per row and step
   static constexpr int RPA = 1024 / ROWA, RPB = 1024 / ROWB;  // rows per 1 KB run
-  static constexpr int A_BYTES = BM * ROWA, B_BYTES = BNB * ROWB, AS_BYTES = A8 ? kNW * 256 : 0;
-  static constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES;
-  static constexpr int A_RUNS = A_BYTES / 1024 / kNW;  // 1 KB runs per wave per stage
-  static constexpr int B_RUNS = B_BYTES / 1024 / kNW;
+  static constexpr int A_BYTES = BM * ROWA, B_BYTES = BNB * ROWB, AS_BYTES = A8 ? NW * 256 : 0;
+  static constexpr int WS_BYTES = WSS ? BNB * 8 : 0;  // per-step weight scales
+  static constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + WS_BYTES;
+  static constexpr int A_RUNS = A_BYTES / 1024 / NW;  // 1 KB runs per wave per stage
+  static constexpr int B_RUNS = B_BYTES / 1024 / NW;
   static constexpr int NKK = BK / 64;                  // 64-deep chunks per K step
   static constexpr int SB = BK / 32;                   // scale bytes per row and step
-  static constexpr int RW = BM / kNW;  // activation-scale rows copied by each wave
-  static constexpr int NV = A_RUNS + B_RUNS + (A8 ? 1 : 0);  // copies per wave per step
+  static constexpr int RW = BM / NW;  // activation-scale rows copied by each wave
+  static constexpr int WS_RUNS = WS_BYTES / 256 / NW;  // 4-B copies of 64 lanes per wave
+  static constexpr int NV = A_RUNS + B_RUNS + (A8 ? 1 : 0) + WS_RUNS;  // copies per wave per step
   static_assert(A_RUNS >= 1 && B_RUNS >= 1 && RW * SB <= 256, "tile shape");
+  static_assert(!WSS || (!A8 && SB == 4 && WS_RUNS >= 1 && WS_BYTES % (256 * NW) == 0),
+                "per-step scales: four bytes a row, whole runs per wave");
   static_assert(NST >= 2 && (NST - 2) * NV < 64, "stages");
 };
 
@@ -94,12 +102,12 @@ __device__ __forceinline__ f32x16 mma(const v8i &w, const v8i &a, const f32x16 &
 }
 
 // One block tile (the work of a block once its tile is known).
-template <bool UP, bool GATHER, int BM, int NST, int BK_, bool A8>
+template <bool UP, bool GATHER, int BM, int NST, int BK_, bool A8, int NW = kNW, bool WSS = false>
 __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, uint8_t *smem,
                                          int tid, int lane, int wave) {
-  using T = T8<BM, NST, BK_, A8>;
+  using T = T8<BM, NST, BK_, A8, NW, WSS>;
   constexpr int BNB = T::BNB, BK = T::BK;
-  static_assert(BK == 128 || BK == 256, "K step");
+  static_assert(BK == 64 || BK == 128 || BK == 256, "K step");
   constexpr int NR = UP ? BNB / 2 : BNB;  // weight rows per matrix in the tile
   const int N = p.N, K = p.K, KB = K / 32;
   const int S = UP ? 1 : (p.splits > 1 ? p.splits : 1);
@@ -149,7 +157,7 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
                               ? (uint32_t)s_src * (uint32_t)sp + 4u * (uint32_t)(lane % SD)
                               : kOOB;
 
-  // Weight codes: run j of wave w fills rows (kNW j + w) * RPB + lane / CPB;
+  // Weight codes: run j of wave w fills rows (NW j + w) * RPB + lane / CPB;
   // up rows [0, 128) are W1 rows n0.., rows [128, 256) the same rows of W3.
   const int pe = phys_slot(p.slot, p.n_slots, e);
   const size_t qn = (size_t)N * (K / 2), sn = (size_t)N * KB;
@@ -161,22 +169,37 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
   int b_chk[T::B_RUNS];
 #pragma unroll
   for (int j = 0; j < T::B_RUNS; ++j) {
-    const int run = kNW * j + wave, br = run * T::RPB + lane / CPB;
+    const int run = NW * j + wave, br = run * T::RPB + lane / CPB;
     const int n = n0 + (UP ? br % NR : br);
     b_chk[j] = run_chunk<T::ROWB>(run, lane);
     b_off[j] = n < N ? (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)b_chk[j] * 16u : kOOB;
+  }
+  // Per-step weight scales (WSS): lane l of run j (of wave w) copies word
+  // l % 2 of the aligned pair holding row 32 (NW j + w) + l / 2's four
+  // scale bytes of the step (rows [NR, 2 NR) of an up tile are W3's); the
+  // pair starts at the byte address rounded down to 4, so the step's bytes
+  // sit at offset (n KB + first K block) % 4 of the 8, the same every step.
+  uint32_t ws_off[T::WS_RUNS > 0 ? T::WS_RUNS : 1];
+  if constexpr (WSS) {
+#pragma unroll
+    for (int j = 0; j < T::WS_RUNS; ++j) {
+      const int br = 32 * (NW * j + wave) + (lane >> 1);
+      const int n = n0 + (UP ? br % NR : br);
+      ws_off[j] = n < N ? ((uint32_t)n * (uint32_t)KB + (uint32_t)(kbeg / 32)) & ~3u : kOOB;
+      ws_off[j] += 4u * (uint32_t)(lane & 1);
+    }
   }
 
   // Weight scales of rows [n0, n0 + NR) over all K: one contiguous run of
   // NR * K/32 bytes per matrix (4-B aligned: checked on the host), copied
   // in 256-B pieces; bytes past the matrix read as zero.
   uint8_t *wscl = smem + NST * T::STAGE;
-  const int RB = NR * KB, RBP = ws_region(NR, K);
-  {
+  const int RB = NR * KB, RBP = WSS ? 0 : ws_region(NR, K);
+  if constexpr (!WSS) {
     const uint32_t base = (uint32_t)n0 * (uint32_t)KB;
 #pragma unroll
     for (int g = 0; g < (UP ? 2 : 1); ++g)
-      for (int q = wave; q < RBP / 256; q += kNW) {
+      for (int q = wave; q < RBP / 256; q += NW) {
         const uint32_t o = (uint32_t)q * 256u + (uint32_t)lane * 4u;
         dma4(g ? rs1 : rs0, wscl + g * RBP + q * 256, o < (uint32_t)RB ? base + o : kOOB);
       }
@@ -196,14 +219,22 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
               (a_off[j] + (uint32_t)(k0 * EA)) | ((k0 + a_chk[j] * EPC < kend) ? 0u : kOOB));
 #pragma unroll
     for (int j = 0; j < T::B_RUNS; ++j) {
-      const bool second = UP && (kNW * j + wave) * T::RPB >= NR;
-      dma16(second ? rq1 : rq0, sb + (kNW * j + wave) * 1024,
+      const bool second = UP && (NW * j + wave) * T::RPB >= NR;
+      dma16(second ? rq1 : rq0, sb + (NW * j + wave) * 1024,
             (b_off[j] + (uint32_t)k0 / 2u) | ((k0 + b_chk[j] * 32 < kend) ? 0u : kOOB));
     }
     if constexpr (A8) dma4(ras, ss + wave * 256, (as_off + (uint32_t)k0 / 32u) | (k0 < kend ? 0u : kOOB));
+    if constexpr (WSS) {
+#pragma unroll
+      for (int j = 0; j < T::WS_RUNS; ++j) {
+        const bool second = UP && 32 * (NW * j + wave) >= NR;  // 32 rows a run
+        dma4(second ? rs1 : rs0, ss + T::AS_BYTES + (NW * j + wave) * 256,
+             (ws_off[j] + (uint32_t)(kt * T::SB)) | (k0 < kend ? 0u : kOOB));
+      }
+    }
   };
 
-  const int wm = wave / (kNW / 2), wn = wave % (kNW / 2);
+  const int wm = wave / (NW / 2), wn = wave % (NW / 2);
   const int lr = lane & 31, lg = lane >> 5;
   f32x16 acc[T::TM][T::TN];
 #pragma unroll
@@ -225,7 +256,11 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
 #pragma unroll
   for (int j = 0; j < T::TN; ++j) {
     const int b = brow(j);
-    ws_row[j] = (b >= NR ? RBP : 0) + (b % NR) * KB;
+    if constexpr (WSS)  // within a stage: the row's word pair, at the step's first byte
+      ws_row[j] = T::A_BYTES + T::B_BYTES + T::AS_BYTES + b * 8 +
+                  (int)(((uint32_t)(n0 + b % NR) * (uint32_t)KB + (uint32_t)(kbeg / 32)) & 3u);
+    else
+      ws_row[j] = (b >= NR ? RBP : 0) + (b % NR) * KB;
   }
 
   // Weight scales of K step kt (the whole-K run is in LDS from the tile's
@@ -237,12 +272,14 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
     constexpr int ACT = decltype(actc)::value;
     if constexpr (ACT > 0) {
       const int blk0 = kbeg / 32 + kt * T::SB + lg;
+      const uint8_t *st_ws = smem + (kt % NST) * T::STAGE;  // WSS: this step's stage
 #pragma unroll
       for (int tn = 0; tn < T::TN; ++tn)
 #pragma unroll
         for (int kk = 0; kk < T::NKK; ++kk) {
           const int blk = blk0 + 2 * kk;
-          const uint32_t v = wscl[ws_row[tn] + min(blk, kbend - 1)];
+          const uint32_t v = WSS ? st_ws[ws_row[tn] + lg + 2 * kk]
+                                 : wscl[ws_row[tn] + min(blk, kbend - 1)];
           wsc[tn][kk] = blk < kbend ? v : 127u;
         }
     }
@@ -372,12 +409,13 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
   const int nk = (kend - kbeg + BK - 1) / BK;
   auto kloop = [&](auto actc) {
     for (int kt = 0; kt < nk; ++kt) {
-      // the scale run lands with step 0's copies: read it after that barrier
+      // the scale run lands with step 0's copies (per-step scales, WSS,
+      // with every step's): read it after that barrier
       uint32_t wsc[T::TN][T::NKK];
-      if (kt > 0) load_wsc(actc, kt, wsc);
+      if (kt > 0 && !WSS) load_wsc(actc, kt, wsc);
       wait_vmcnt<(NST - 2) * T::NV>();
       __syncthreads();
-      if (kt == 0) load_wsc(actc, kt, wsc);
+      if (kt == 0 || WSS) load_wsc(actc, kt, wsc);
       step(actc, kt, kt % NST, kt + NST - 1, (kt + NST - 1) % NST, wsc);
     }
   };
@@ -407,8 +445,8 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
     store_f32_tile<T::TM, T::TN, T::WM, T::WN>(acc, dst, N, row0, rows, n0, wm, wn, lane);
   } else if constexpr (!A8) {
     __syncthreads();  // every wave is done reading the stages
-    store_swiglu_bf16_tile<T::TM, T::TN, T::WM, T::WN, BM, NR>(acc, smem, (uint16_t *)p.out, N,
-                                                                row0, rows, n0, wm, wn, lane, tid);
+    store_swiglu_bf16_tile<T::TM, T::TN, T::WM, T::WN, BM, NR, T::NT>(
+        acc, smem, (uint16_t *)p.out, N, row0, rows, n0, wm, wn, lane, tid);
   } else {
     // MXFP8 hidden staged through LDS: codes [BM][128 + 16 pad], then one
     // 4-B word of scales per row (the tile's 128 columns are 4 blocks).
@@ -444,14 +482,14 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
     uint8_t *oq = (uint8_t *)p.out;
     const int spo = (N / 32 + 3) / 4 * 4;
     constexpr int CH = OC / 16;
-    for (int idx = tid; idx < BM * CH; idx += kNT) {
+    for (int idx = tid; idx < BM * CH; idx += T::NT) {
       const int r = idx / CH, ch = idx % CH;
       const int col = n0 + ch * 16;
       if (r < rows && col < N)
         *(u32x4 *)(oq + (size_t)(row0 + r) * N + col) = *(const u32x4 *)(so + r * PITCH + ch * 16);
     }
     // n0 / 32 is a multiple of 4 and at most spo - 4: the word is in the row
-    for (int r = tid; r < rows; r += kNT)
+    for (int r = tid; r < rows; r += T::NT)
       *(uint32_t *)(p.out_s + (size_t)(row0 + r) * spo + n0 / 32) = *(const uint32_t *)(sso + r * 4);
   }
 }
@@ -497,11 +535,38 @@ __global__ __launch_bounds__(kNT, 1) void mxw16_mixed_kernel(MxwParams p) {
     mxw_tile<UP, GATHER, 128, 2, 128, false>(p, s_t, smem, tid, lane, wave);
 }
 
+// W4A16 with two four-wave workgroups per CU, each with its own step
+// barrier, so that one workgroup's barrier and LDS waits overlap the other's
+// MFMAs.  To fit two workgroups in the LDS, a pile of more than 64 rows takes
+// 128-row tiles with 64-deep steps (32-byte pieces of the weight rows), a
+// pile of at most 64 rows a 64-row tile with 128-deep steps whose weight
+// scales travel with each step (64-byte pieces, which stream from HBM
+// faster than 32-byte ones).  Tile list and order as mxw16_mixed_kernel.
+constexpr int kPairNW = 4;
+template <bool UP, bool GATHER>
+__global__ __launch_bounds__(kPairNW * 64, 2) void mxw16_pair_kernel(MxwParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ TileSlot s_t;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave == 0)
+    map_block_fn<!UP>(p.offsets, p.E, p.n_tiles, 1, lane, &s_t,
+                      [](int m) { return m <= kMixedSmallRows ? kMixedSmallRows : 128; },
+                      std::integral_constant<bool, false>{}, 0, kMixedRowGroup);
+  __syncthreads();
+  if (s_t.e < 0) return;
+  if (s_t.bm == kMixedSmallRows)
+    mxw_tile<UP, GATHER, kMixedSmallRows, 2, 128, false, kPairNW, true>(p, s_t, smem, tid, lane,
+                                                                       wave);
+  else
+    mxw_tile<UP, GATHER, 128, 2, 64, false, kPairNW>(p, s_t, smem, tid, lane, wave);
+}
+
 // LDS of a launch: the stages and the tile's weight scales.
-template <bool UP, int BM, int NST, int BK, bool A8>
+template <bool UP, int BM, int NST, int BK, bool A8, bool WSS = false>
 constexpr int lds_bytes(int K) {
-  using T = T8<BM, NST, BK, A8>;
-  return NST * T::STAGE + (UP ? 2 : 1) * ws_region(UP ? T::BNB / 2 : T::BNB, K);
+  using T = T8<BM, NST, BK, A8, kNW, WSS>;
+  return NST * T::STAGE + (WSS ? 0 : (UP ? 2 : 1) * ws_region(UP ? T::BNB / 2 : T::BNB, K));
 }
 constexpr int kLdsMax = 160 * 1024 - 256;  // minus the static tile slot
 
@@ -651,6 +716,45 @@ hipError_t launch_mxw16_mixed(const MxwParams &p, bool up, bool gather, hipStrea
     attr_done[which].fetch_or(bit, std::memory_order_release);
   }
   kern<<<blocks, kNT, lds, st>>>(p);
+  return hipGetLastError();
+}
+
+// Two workgroups per CU: each at most half of the CU's LDS, less the static
+// tile slot.
+constexpr int kPairLdsMax = 80 * 1024 - 256;
+bool mxw16_pair_fits(bool up, int K) {
+  if (K > kW4A8MaxK || K % 32) return false;
+  const int lds = up ? std::max(lds_bytes<true, kMixedSmallRows, 2, 128, false, true>(K),
+                                lds_bytes<true, 128, 2, 64, false>(K))
+                     : std::max(lds_bytes<false, kMixedSmallRows, 2, 128, false, true>(K),
+                                lds_bytes<false, 128, 2, 64, false>(K));
+  return lds <= kPairLdsMax;
+}
+
+hipError_t launch_mxw16_pair(const MxwParams &p, bool up, bool gather, hipStream_t st) {
+  if (!mxw16_pair_fits(up, p.K)) return hipErrorInvalidValue;
+  if (!up && gather) return hipErrorInvalidValue;
+  const int m_tiles = (p.R + 127) / 128 + (p.E < p.R ? p.E : p.R);
+  const int blocks = m_tiles * p.n_tiles + (up ? 0 : 16);  // down: longest first, 16 spare
+  const int lds = up ? std::max(lds_bytes<true, kMixedSmallRows, 2, 128, false, true>(p.K),
+                                lds_bytes<true, 128, 2, 64, false>(p.K))
+                     : std::max(lds_bytes<false, kMixedSmallRows, 2, 128, false, true>(p.K),
+                                lds_bytes<false, 128, 2, 64, false>(p.K));
+  auto kern = up ? (gather ? mxw16_pair_kernel<true, true> : mxw16_pair_kernel<true, false>)
+                 : mxw16_pair_kernel<false, false>;
+  static std::atomic<uint64_t> attr_done[3];
+  const int which = up ? (gather ? 0 : 1) : 2;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_done[which].load(std::memory_order_acquire) & bit)) {
+    err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              kPairLdsMax);
+    if (err != hipSuccess) return err;
+    attr_done[which].fetch_or(bit, std::memory_order_release);
+  }
+  kern<<<blocks, kPairNW * 64, lds, st>>>(p);
   return hipGetLastError();
 }
 
