@@ -279,7 +279,7 @@ def main():
     elif wl.wdt == "mxfp4" and aq:
         fam = "mxw_gemm_kernel"  # W4A8 prefill: MXFP4 codes in LDS, MXFP8 activations
     elif wl.wdt == "mxfp4":
-        fam = "mxw16_mixed_kernel"  # W4A16 prefill: 64- and 128-row tiles in one launch
+        fam = "mxw16_pair_kernel"  # W4A16 prefill up: 64- and 128-row tiles, two workgroups per CU
     else:
         fam = "big_gemm_kernel"
     traffic, src = read_traffic(name, fam, aq)
