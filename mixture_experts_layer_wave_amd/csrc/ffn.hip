@@ -105,6 +105,8 @@ bool big_ok(const FfnArgs &a, size_t a_bytes, int N, int K) {
   const size_t lim = (size_t)1 << 31;
   if (a.w_dtype != 1 && a.w_dtype != 2) return false;
   if (a_bytes >= lim || (size_t)N * K * 2 >= lim) return false;
+  // a tile's f32 output rows are addressed from the tile's first row
+  if ((size_t)512 * N * 4 >= lim) return false;
   return K % 8 == 0;
 }
 
@@ -443,6 +445,7 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
       p.out = a.fuse_y;
       p.perm_out = a.fuse_perm;
       p.comb_w = a.fuse_w;
+      p.fuse_rows = a.n;
     }
     hipError_t err = launch_big_gemm(p, false, a.w_dtype == 2, false, fuse, bm, bnb, st);
     if (err == hipSuccess && fused) *fused = fuse;

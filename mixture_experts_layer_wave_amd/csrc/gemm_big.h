@@ -19,6 +19,7 @@ struct BigGemmParams {
   void *out;                // up: bf16 [R][N]; down: f32 [R][N]; fused: bf16 y [n][N]
   const int32_t *perm_out;  // fused combine: pile row -> token
   const float *comb_w;      // fused combine: token -> weight (one expert per token)
+  int fuse_rows;            // fused combine: rows of y (tokens)
   // Split K (down only): each block tile is computed by `splits` blocks over
   // consecutive K ranges of ksplit (a multiple of 64); block s writes its
   // partial sums to part[s][R][N] f32 (out and the fused combine unused),
@@ -37,8 +38,9 @@ struct BigGemmParams {
 };
 
 // up: H = silu(A W1^T) * (A W3^T); down: Yp = H W2^T (or the fused combine).
-// bm x bnb is the block tile (256x256 for up; 256x256, 256x128 or 128x128
-// for down).  Returns hipErrorInvalidValue for a combination not built.
+// bm x bnb is the block tile (256x256 or 320x256 for up; 320x256, 256x256,
+// 256x128 or 128x128 for down).  Returns hipErrorInvalidValue for a
+// combination not built.
 hipError_t launch_big_gemm(const BigGemmParams &p, bool up, bool mx, bool gather, bool fuse,
                            int bm, int bnb, hipStream_t st);
 
