@@ -266,7 +266,9 @@ int moe_expert_down(const moe_shape *s, const void *h, const int32_t *offsets,
  * back in token order and add the k contributions:
  *   y[t] = sum_{j<k} topk_w[t][j] * y_perm[inv[t][j]]
  * summed in slot order in float32, then rounded to `out` (F32 or BF16).
- *   y_perm [n*k][d] f32 (in must be MOE_F32); inv, topk_w [n][k]; y [n][d].
+ *   y_perm [n*k][d], in = MOE_F32 or MOE_BF16 (bf16 pile outputs, as
+ *   moe_grouped_ffn writes with out = MOE_BF16; then d % 8 == 0, else
+ *   MOE_ERR_SHAPE); inv, topk_w [n][k]; y [n][d].
  * A pair whose inv entry is outside [0, n*k) (moe_dispatch's -1 for an id
  * outside [0, E)) adds nothing. */
 int moe_combine(const moe_shape *s, const void *y_perm, int in,

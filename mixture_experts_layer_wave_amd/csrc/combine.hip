@@ -169,6 +169,78 @@ __global__ __launch_bounds__(256) void combine_tail_kernel(
   }
 }
 
+// The combine of bf16 pile outputs (each the f32 pile output rounded once),
+// eight columns a thread (d % 8 == 0); with TAIL the rows of each pile's
+// last row tile (bm-row tiles from offsets[e]) are instead the sum of their
+// S f32 partial planes tail[s][e * bm + row][d], in split order.
+template <bool OUT_BF16, bool TAIL>
+__global__ __launch_bounds__(256) void combine_bf16in_kernel(
+    const uint16_t *__restrict__ yp, const float *__restrict__ tail, int S, size_t plane,
+    const int32_t *__restrict__ off, int E, int bm, const int32_t *__restrict__ inv,
+    const float *__restrict__ w, int n, int k, int d, void *__restrict__ y) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (t >= n || c >= d) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const unsigned R = (unsigned)n * (unsigned)k;
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const int r = inv[(size_t)t * k + j];
+    if ((unsigned)r >= R) continue;
+    float v[8];
+    bool planes = false;
+    if constexpr (TAIL) {
+      const int e = expert_of(off, E, r);
+      const int tb = tail_begin(off, e, bm);
+      if (r >= tb) {
+        const float *q = tail + ((size_t)e * bm + (r - tb)) * d + c;
+        f32x4 lo = *(const f32x4 *)q, hi = *(const f32x4 *)(q + 4);
+        for (int sp = 1; sp < S; ++sp) {
+          lo += *(const f32x4 *)(q + sp * plane);
+          hi += *(const f32x4 *)(q + sp * plane + 4);
+        }
+        for (int i = 0; i < 4; ++i) {
+          v[i] = lo[i];
+          v[i + 4] = hi[i];
+        }
+        planes = true;
+      }
+    }
+    if (!planes) {
+      const u32x4 raw = *(const u32x4 *)(yp + (size_t)r * d + c);
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_bits_to_f32(raw[i] & 0xffffu);
+        v[2 * i + 1] = bf16_bits_to_f32(raw[i] >> 16);
+      }
+    }
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+  }
+  if constexpr (OUT_BF16) {
+    const u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    *(u32x4 *)((uint16_t *)y + (size_t)t * d + c) = o;
+  } else {
+    float *o = (float *)y + (size_t)t * d + c;
+    *(f32x4 *)o = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4 *)(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+}
+
+template <bool TAIL>
+hipError_t launch_bf16in(const uint16_t *yp, const float *tail, int S, size_t plane,
+                         const int32_t *off, int E, int bm, const int32_t *inv, const float *w,
+                         int n, int k, int d, void *y, bool out_bf16, hipStream_t st) {
+  if (d % 8) return hipErrorInvalidValue;
+  dim3 grid((d / 8 + 255) / 256, n);
+  if (out_bf16)
+    combine_bf16in_kernel<true, TAIL><<<grid, 256, 0, st>>>(yp, tail, S, plane, off, E, bm, inv, w,
+                                                            n, k, d, y);
+  else
+    combine_bf16in_kernel<false, TAIL><<<grid, 256, 0, st>>>(yp, tail, S, plane, off, E, bm, inv,
+                                                             w, n, k, d, y);
+  return hipGetLastError();
+}
+
 // Block row (e, i): row i of pile e's last row tile, if the pile has it.
 __global__ __launch_bounds__(256) void tail_sum_kernel(const float *__restrict__ tail, int S,
                                                        size_t plane,
@@ -227,18 +299,21 @@ hipError_t launch_splitk_sum(const float *part, int S, int R, int d, float *yp, 
   return hipGetLastError();
 }
 
-hipError_t launch_combine_tail(const float *y_perm, const float *tail, int S, size_t plane,
-                               const int32_t *offsets, int E, int bm, const int32_t *inv,
-                               const float *w, int n, int k, int d, void *y, bool out_bf16,
-                               hipStream_t st) {
+hipError_t launch_combine_tail(const void *y_perm, bool in_bf16, const float *tail, int S,
+                               size_t plane, const int32_t *offsets, int E, int bm,
+                               const int32_t *inv, const float *w, int n, int k, int d, void *y,
+                               bool out_bf16, hipStream_t st) {
+  if (in_bf16)
+    return launch_bf16in<true>((const uint16_t *)y_perm, tail, S, plane, offsets, E, bm, inv, w, n,
+                               k, d, y, out_bf16, st);
   if (d % 4) return hipErrorInvalidValue;
   dim3 grid((d / 4 + 255) / 256, n);
   if (out_bf16)
-    combine_tail_kernel<true><<<grid, 256, 0, st>>>(y_perm, tail, S, plane, offsets, E, bm, inv,
-                                                    w, n, k, d, y);
+    combine_tail_kernel<true><<<grid, 256, 0, st>>>((const float *)y_perm, tail, S, plane, offsets,
+                                                    E, bm, inv, w, n, k, d, y);
   else
-    combine_tail_kernel<false><<<grid, 256, 0, st>>>(y_perm, tail, S, plane, offsets, E, bm, inv,
-                                                     w, n, k, d, y);
+    combine_tail_kernel<false><<<grid, 256, 0, st>>>((const float *)y_perm, tail, S, plane, offsets,
+                                                     E, bm, inv, w, n, k, d, y);
   return hipGetLastError();
 }
 
@@ -250,20 +325,24 @@ hipError_t launch_tail_sum(const float *tail, int S, size_t plane, const int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float *y_perm, const int32_t *inv, const float *w, int n, int k,
-                          int d, void *y, bool out_bf16, hipStream_t st) {
+hipError_t launch_combine(const void *y_perm, bool in_bf16, const int32_t *inv, const float *w,
+                          int n, int k, int d, void *y, bool out_bf16, hipStream_t st) {
+  if (in_bf16)
+    return launch_bf16in<false>((const uint16_t *)y_perm, nullptr, 0, 0, nullptr, 0, 0, inv, w, n,
+                                k, d, y, out_bf16, st);
+  const float *yp = (const float *)y_perm;
   if (d % 4 == 0) {
     dim3 grid((d / 4 + 255) / 256, n);
     if (out_bf16)
-      combine_vec4_kernel<true><<<grid, 256, 0, st>>>(y_perm, inv, w, n, k, d, y);
+      combine_vec4_kernel<true><<<grid, 256, 0, st>>>(yp, inv, w, n, k, d, y);
     else
-      combine_vec4_kernel<false><<<grid, 256, 0, st>>>(y_perm, inv, w, n, k, d, y);
+      combine_vec4_kernel<false><<<grid, 256, 0, st>>>(yp, inv, w, n, k, d, y);
   } else {
     dim3 grid((d + 255) / 256, n);
     if (out_bf16)
-      combine_scalar_kernel<true><<<grid, 256, 0, st>>>(y_perm, inv, w, n, k, d, y);
+      combine_scalar_kernel<true><<<grid, 256, 0, st>>>(yp, inv, w, n, k, d, y);
     else
-      combine_scalar_kernel<false><<<grid, 256, 0, st>>>(y_perm, inv, w, n, k, d, y);
+      combine_scalar_kernel<false><<<grid, 256, 0, st>>>(yp, inv, w, n, k, d, y);
   }
   return hipGetLastError();
 }

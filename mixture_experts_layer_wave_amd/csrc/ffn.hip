@@ -393,8 +393,9 @@ hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
+hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused, bool *yp_bf16) {
   if (fused) *fused = false;
+  if (yp_bf16) *yp_bf16 = false;
   if (a.R == 0) return hipSuccess;
   if (use_decode(a)) return launch_decode_down(a, st);
   if (a.act_quant || use_mxw16(a, false)) return launch_mxw_down(a, st, fused);
@@ -425,7 +426,13 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
     }
     const bool fuse = a.fuse_y != nullptr && a.k == 1;
     const TailPlan tp = down_tail_plan(a);
-    if (tp.splits > 1 && a.tail_part && !fuse) {
+    const bool tail = tp.splits > 1 && a.tail_part && !fuse;
+    // bf16 pile outputs where the caller takes them (with a tail split only
+    // when the combine follows here: the tail sums are f32)
+    const bool piles16 =
+        a.yp_bf16_ok && a.w_dtype == 1 && !fuse && (!tail || a.comb_y) && a.d % 8 == 0;
+    p.out_bf16 = piles16 ? 1 : 0;
+    if (tail) {
       p.tail_splits = tp.splits;
       p.tail_ksplit = ((a.d_ff + 64 * tp.splits - 1) / (64 * tp.splits)) * 64;
       p.tail_part = a.tail_part;
@@ -434,9 +441,9 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
       if (err != hipSuccess) return err;
       if (a.comb_y) {
         if (fused) *fused = true;
-        return launch_combine_tail(a.y_perm, a.tail_part, tp.splits, p.tail_plane, a.offsets, a.E,
-                                   bm, a.comb_inv, a.comb_w, a.n, a.k, a.d, a.comb_y, a.comb_bf16,
-                                   st);
+        return launch_combine_tail(a.y_perm, piles16, a.tail_part, tp.splits, p.tail_plane,
+                                   a.offsets, a.E, bm, a.comb_inv, a.comb_w, a.n, a.k, a.d,
+                                   a.comb_y, a.comb_bf16, st);
       }
       return launch_tail_sum(a.tail_part, tp.splits, p.tail_plane, a.offsets, a.E, bm, a.d,
                              a.y_perm, st);
@@ -449,15 +456,16 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused) {
     }
     hipError_t err = launch_big_gemm(p, false, a.w_dtype == 2, false, fuse, bm, bnb, st);
     if (err == hipSuccess && fused) *fused = fuse;
+    if (err == hipSuccess && yp_bf16) *yp_bf16 = piles16;
     return err;
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st, bool *fused) {
+hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st, bool *fused, bool *yp_bf16) {
   hipError_t err = launch_expert_up(a, st);
   if (err != hipSuccess) return err;
-  return launch_expert_down(a, st, fused);
+  return launch_expert_down(a, st, fused, yp_bf16);
 }
 
 }  // namespace moe

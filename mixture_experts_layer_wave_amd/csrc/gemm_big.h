@@ -20,6 +20,8 @@ struct BigGemmParams {
   const int32_t *perm_out;  // fused combine: pile row -> token
   const float *comb_w;      // fused combine: token -> weight (one expert per token)
   int fuse_rows;            // fused combine: rows of y (tokens)
+  int out_bf16;             // down, neither fused nor split: pile outputs as bf16
+                            // (the f32 result rounded once) in out
   // Split K (down only): each block tile is computed by `splits` blocks over
   // consecutive K ranges of ksplit (a multiple of 64); block s writes its
   // partial sums to part[s][R][N] f32 (out and the fused combine unused),

@@ -156,6 +156,39 @@ __device__ __forceinline__ void store_f32_regs(const f32x16 (&acc)[TM][TN],
   }
 }
 
+// Down: bf16 rows [0, rows) of a tile in ro (row pitch N bf16), each value
+// the f32 result rounded once.
+template <int TM, int TN, int WM, int WN>
+__device__ __forceinline__ void store_bf16_regs(const f32x16 (&acc)[TM][TN],
+                                                __amdgpu_buffer_rsrc_t ro, int N, int rows, int n0,
+                                                int wm, int wn) {
+  // (the lane id is read afresh: lane-derived values of the K loop are
+  // not kept live across it for the epilogue)
+  const int lane = __lane_id(), lr = lane & 31, lg = lane >> 5;
+  const uint32_t rowoff = (uint32_t)(wm * WM + lr) * (uint32_t)N;  // row r's first element
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int r = wm * WM + tm * 32 + lr;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        pk[g][0] = pack_bf16x2(acc[tm][j][g * 4], acc[tm][j][g * 4 + 1]);
+        pk[g][1] = pack_bf16x2(acc[tm][j][g * 4 + 2], acc[tm][j][g * 4 + 3]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 o = swap_halves(pk[2 * h][0], pk[2 * h][1], pk[2 * h + 1][0], pk[2 * h + 1][1]);
+        const int col = n0 + wn * WN + j * 32 + 16 * h + lg * 8;
+        const uint32_t off =
+            (r < rows && col < N) ? (rowoff + (uint32_t)(tm * 32 * N) + col) * 2u : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(o, ro, off, 0, 0);
+      }
+    }
+  }
+}
+
 // Down with the combine fused (one expert per token): y[token] = w(token) *
 // row, bf16, in ro = the layer output (row pitch N bf16).
 template <int TM, int TN, int WM, int WN>
@@ -426,11 +459,16 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
     store_scaled_rows_regs<T::TM, T::TN, T::WM, T::WN>(
         acc, rsrc(p.out, (uint32_t)p.fuse_rows * (uint32_t)N * 2u), N, p.perm_out, p.comb_w, row0,
         rows, n0, wm, wn);
+  } else if (p.out_bf16 && !tail_split && S == 1) {
+    // bf16 pile outputs.
+    store_bf16_regs<T::TM, T::TN, T::WM, T::WN>(
+        acc, rsrc((uint16_t *)p.out + (size_t)row0 * N, (uint32_t)rows * (uint32_t)N * 2u), N, rows,
+        n0, wm, wn);
   } else {
     // Tail split: this split's partial sums of the pile's last row tile,
     // compactly at row e * BM + (pile row - row0) of plane `split`; split K:
     // plane `split` of the partial sums, added later in split order; else
-    // the pile outputs.
+    // the f32 pile outputs.
     float *dst = tail_split ? p.tail_part + (size_t)split * p.tail_plane + (size_t)e * BM * N
                             : (S > 1 ? p.part + (size_t)split * p.R * N : (float *)p.out) +
                                   (size_t)row0 * N;

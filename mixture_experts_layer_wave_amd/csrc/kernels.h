@@ -69,7 +69,11 @@ struct FfnArgs {
   const int32_t *slot;    // [E] logical -> physical expert slot, or NULL
   int n_slots;            // physical slots when slot is given
   void *h;                // [R][d_ff] hidden (bf16, or f32 for f32 weights)
-  float *y_perm;          // [R][d] f32
+  float *y_perm;          // [R][d] f32 (or bf16, see yp_bf16_ok)
+  // The caller takes bf16 pile outputs (each the f32 result rounded once)
+  // when the down pass can write them (the unsplit bf16-weight pass);
+  // launch_expert_down reports whether it did.
+  bool yp_bf16_ok;
   int n, k;               // tokens and experts per token
   // Optional combine fused into the down-projection (used when k == 1):
   // y[perm[r]] = w[perm[r]] * (h[r] W2^T), bf16 [n][d].
@@ -111,9 +115,12 @@ int down_split_factor(const FfnArgs &a);
 // the down pass does not split its tail).
 size_t down_tail_bytes(const FfnArgs &a);
 hipError_t launch_expert_up(const FfnArgs &a, hipStream_t st);    // A -> h
-// h -> y_perm, or straight into fuse_y; *fused (may be NULL) tells which.
-hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
-hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st, bool *fused = nullptr);
+// h -> y_perm, or straight into fuse_y; *fused (may be NULL) tells which,
+// and *yp_bf16 (may be NULL) whether y_perm holds bf16 pile outputs.
+hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused = nullptr,
+                              bool *yp_bf16 = nullptr);
+hipError_t launch_grouped_ffn(const FfnArgs &a, hipStream_t st, bool *fused = nullptr,
+                              bool *yp_bf16 = nullptr);
 
 // Compute units of the current device (read once and cached).
 int cu_count();
@@ -137,15 +144,17 @@ hipError_t launch_splitk_combine(const float *part, int S, int R, const int32_t 
                                  const float *w, int n, int k, int d, void *y, bool out_bf16,
                                  hipStream_t st);
 hipError_t launch_splitk_sum(const float *part, int S, int R, int d, float *yp, hipStream_t st);
-hipError_t launch_combine(const float *y_perm, const int32_t *inv, const float *w,
+// y_perm: [R][d] f32, or bf16 with in_bf16 (then d % 8 == 0).
+hipError_t launch_combine(const void *y_perm, bool in_bf16, const int32_t *inv, const float *w,
                           int n, int k, int d, void *y, bool out_bf16, hipStream_t st);
 // The same combine when the last row tile of each pile (bm-row tiles from
-// offsets[e]) holds S partial planes tail[s][e * bm + row][d] instead of
-// y_perm rows: those rows are the planes' sum in split order.  d % 4 == 0.
-hipError_t launch_combine_tail(const float *y_perm, const float *tail, int S, size_t plane,
-                               const int32_t *offsets, int E, int bm, const int32_t *inv,
-                               const float *w, int n, int k, int d, void *y, bool out_bf16,
-                               hipStream_t st);
+// offsets[e]) holds S f32 partial planes tail[s][e * bm + row][d] instead of
+// y_perm rows: those rows are the planes' sum in split order.  d % 4 == 0
+// (d % 8 == 0 with in_bf16).
+hipError_t launch_combine_tail(const void *y_perm, bool in_bf16, const float *tail, int S,
+                               size_t plane, const int32_t *offsets, int E, int bm,
+                               const int32_t *inv, const float *w, int n, int k, int d, void *y,
+                               bool out_bf16, hipStream_t st);
 // y_perm rows of the last row tiles = the sum of their S tail planes.
 hipError_t launch_tail_sum(const float *tail, int S, size_t plane, const int32_t *offsets, int E,
                            int bm, int d, float *y_perm, hipStream_t st);

@@ -365,9 +365,12 @@ int moe_combine(const moe_shape *s, const void *y_perm, int in, const int32_t *i
   int st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!y_perm || !inv || !topk_w || !y) return MOE_ERR_NULL;
-  if (in != MOE_F32 || (out != MOE_F32 && out != MOE_BF16)) return MOE_ERR_DTYPE;
-  if (s->d % 4 == 0 && (!aligned16(y_perm) || !aligned16(y))) return MOE_ERR_ALIGN;
-  return hip_status(moe::launch_combine((const float *)y_perm, inv, topk_w, s->n, s->k, s->d, y,
+  if ((in != MOE_F32 && in != MOE_BF16) || (out != MOE_F32 && out != MOE_BF16))
+    return MOE_ERR_DTYPE;
+  if (in == MOE_BF16 && s->d % 8) return MOE_ERR_SHAPE;
+  if ((in == MOE_BF16 || s->d % 4 == 0) && (!aligned16(y_perm) || !aligned16(y)))
+    return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_combine(y_perm, in == MOE_BF16, inv, topk_w, s->n, s->k, s->d, y,
                                         out == MOE_BF16, (hipStream_t)stream));
 }
 
@@ -436,7 +439,7 @@ int forward_impl(const moe_shape *s, const void *x, int act, const void *wg, con
                                  xq + moe::mx8_scale_offset((size_t)s->n, s->d), hs);
     a = xq;
   }
-  bool fused = false;
+  bool fused = false, yp_bf16 = false;
   if (e == hipSuccess) {
     moe::FfnArgs f = ffn_args(s, a, perm, offsets, w, base + L.h, yp);
     f.split_ok = true;
@@ -457,15 +460,16 @@ int forward_impl(const moe_shape *s, const void *x, int act, const void *wg, con
     f.comb_inv = inv;
     f.comb_w = wt;
     f.comb_bf16 = out == MOE_BF16;
+    f.yp_bf16_ok = true;  // the combine below reads either pile dtype
     if (s->k == 1 && out == MOE_BF16) {  // one expert per token: scale-and-scatter in the down pass
       f.fuse_y = y;
       f.fuse_perm = perm;
       f.fuse_w = wt;
     }
-    e = moe::launch_grouped_ffn(f, hs, &fused);
+    e = moe::launch_grouped_ffn(f, hs, &fused, &yp_bf16);
   }
   if (e == hipSuccess && !fused)
-    e = moe::launch_combine(yp, inv, wt, s->n, s->k, s->d, y, out == MOE_BF16, hs);
+    e = moe::launch_combine(yp, yp_bf16, inv, wt, s->n, s->k, s->d, y, out == MOE_BF16, hs);
   return hip_status(e);
 }
 

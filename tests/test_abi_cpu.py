@@ -189,7 +189,8 @@ def test_w4a8_sizes_and_errors_before_launch():
 def test_boundary_choices_before_launch():
     """The boundary's documented choices, checked before anything launches:
     moe_router_topk needs a logits buffer (the library holds no device
-    memory of its own); moe_grouped_ffn writes f32 or bf16 pile outputs; the
+    memory of its own); moe_grouped_ffn writes f32 or bf16 pile outputs and
+    moe_combine reads either; the
     workspace size is a function of the shape and the weight dtype; the
     expert GEMMs' 32-bit operand offsets bound the batch."""
     import ctypes
@@ -217,5 +218,11 @@ def test_boundary_choices_before_launch():
     fwd = lambda shape, wd: B.lib.moe_forward(ctypes.byref(B._shape(shape)), fake, 1, fake, None,
                                               ctypes.byref(B.ExpertWeights(wd, fake, fake, fake, fake, fake, fake)),
                                               fake, 1, None, None, fake, 1 << 40, None)
+    # combine: f32 or bf16 pile outputs in; bf16 in needs d % 8 == 0
+    comb = lambda shape, din: B.lib.moe_combine(ctypes.byref(B._shape(shape)), fake, din, fake,
+                                                fake, fake, 1, None)
+    assert comb((16, 60, 8, 2, 64), B.MOE_BF16) == -2
+    assert comb((16, 60, 8, 2, 64), B.MOE_MXFP4) == -3
+    assert comb((16, 64, 8, 2, 64), B.MOE_MXFP8) == -3
     assert fwd((65536, 4096, 8, 2, 14336), 1) == -2   # 131072 x 14336 rows of bf16 hidden
     assert fwd((16, 32768, 8, 2, 32768), 2) == -2     # one expert matrix past 2^30 elements

@@ -93,3 +93,31 @@ def test_combine_matches_fp64(k, d, out):
     else:
         got = y.double().cpu().numpy()
         np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("k,d,out", [(2, 4096, "bf16"), (4, 2880, "f32"), (1, 8, "bf16")])
+def test_combine_of_bf16_piles_is_exact(k, d, out):
+    """moe_combine of bf16 pile outputs equals, bit for bit, the combine of
+    the same values widened to f32 (slot order, f32 products and sums), and
+    a pair whose pile row is -1 adds nothing."""
+    import torch
+    from mixture_experts_layer_wave_amd import binding as B
+    from mixture_experts_layer_wave_amd.device import to_device
+
+    say(f"[combine bf16 in] k={k} d={d} out={out}")
+    rng = np.random.default_rng(7 * k + d)
+    n, E = 193, 8
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(n)]).astype(np.int32)
+    dp = oracle.dispatch(idx, E)
+    inv = dp["inv"].copy()
+    inv[5, 0] = -1
+    y16 = torch.from_numpy(rng.standard_normal((n * k, d)).astype(np.float32)).to("cuda").to(torch.bfloat16)
+    w = to_device(rng.random((n, k)).astype(np.float32))
+    ydt = torch.int16 if out == "bf16" else torch.float32
+    ya = torch.empty((n, d), dtype=ydt, device="cuda")
+    yb = torch.empty((n, d), dtype=ydt, device="cuda")
+    shape = (n, d, E, k, 8, -1)
+    B.moe_combine(shape, y16.view(torch.int16), "bf16", to_device(inv), w, ya, out)
+    B.moe_combine(shape, y16.float().contiguous(), "f32", to_device(inv), w, yb, out)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb)
