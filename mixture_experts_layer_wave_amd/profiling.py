@@ -184,11 +184,19 @@ def up_flops(workload: str) -> float:
     return 4.0 * wl.n * wl.k * wl.d * wl.d_ff
 
 
+def projection_flops(workload: str, kernel: str) -> float:
+    """Algorithmic flops of one launch of an expert GEMM: the up projection
+    (W1 and W3, first template argument true) or the down projection (W2,
+    half the up projection's)."""
+    up = short_name(kernel).split("<", 1)[1].startswith("true")
+    return up_flops(workload) if up else up_flops(workload) / 2.0
+
+
 def cmd_mfma(a):
     kname, c, dur_ns, nd = dispatch_counters(a.pmc, a.kernel)
     mops = sum(v for k, v in c.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
     counted = mops * 512.0
-    alg = up_flops(a.workload) if a.flops is None else a.flops
+    alg = projection_flops(a.workload, kname) if a.flops is None else a.flops
     # GRBM_GUI_ACTIVE is summed over the XCDs: cycles of one XCD = sum / 8.
     cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
     ghz = cycles / dur_ns

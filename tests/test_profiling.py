@@ -97,3 +97,12 @@ def test_mfma_summary_arithmetic(tmp_path):
     assert rows["MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs))"].strip() == "0.500"
     ach = alg / 100e-6 / 1e12
     assert abs(float(rows["fraction of the peak at that clock"]) - ach / (2500.0 * 2.0 / 2.4)) < 1e-3
+
+
+def test_projection_flops_by_kernel():
+    # the up projection runs W1 and W3 (4 R d f flops), the down projection W2
+    wl = "mixtral-top2-n8192-d4096-e8-ff14336-bf16"
+    up = P.projection_flops(wl, "void moe::(anonymous namespace)::big_gemm_kernel<true, true, false, 320, 256, false>(moe::BigGemmParams)")
+    down = P.projection_flops(wl, "void moe::(anonymous namespace)::big_gemm_kernel<false, false, false, 320, 256, true>(moe::BigGemmParams)")
+    assert up == 4.0 * 8192 * 2 * 4096 * 14336
+    assert down == up / 2
