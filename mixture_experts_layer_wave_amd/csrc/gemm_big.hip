@@ -63,8 +63,11 @@ struct Tile {
 // Row tiles per group in the tile order (map_block_fn RG): on the
 // Mixtral-shaped up GEMM (7 row tiles per pile) groups of four cut the bytes
 // fetched past L2 from 15.2 to 8.0 GB per launch and the kernel by 1%;
-// groups of two were 3% slower.
+// groups of two were 3% slower.  Its down GEMM (6 full row tiles per pile,
+// K = 14336) takes a pile's full row tiles in one group: 0.4% off the layer
+// against groups of four (groups of two: 0.6% slower).
 constexpr int kBigRowGroup = 4;
+constexpr int kDownRowGroup = 8;
 
 // ---- epilogues from registers ----------------------------------------------
 // The MFMA takes the weight rows as its first operand, so accumulator
@@ -267,7 +270,9 @@ __global__ __launch_bounds__(kNT, 1) void big_gemm_kernel(BigGemmParams p) {
   // about the same time, and the blocks of an XCD that share operands stay
   // closer in K (measured: L2 hit rate 45% -> 50% on the Mixtral-shaped up).
   const int S1 = (LPT && !UP && p.tail_splits > 1) ? p.tail_splits : S;
-  if (wave == 0) map_block<BM, LPT, UP>(p.offsets, p.E, p.n_tiles, S, lane, &s_t, S1, kBigRowGroup);
+  if (wave == 0)
+    map_block<BM, LPT, UP>(p.offsets, p.E, p.n_tiles, S, lane, &s_t, S1,
+                           UP ? kBigRowGroup : kDownRowGroup);
   __syncthreads();
   const int e = s_t.e;
   if (e < 0) return;
