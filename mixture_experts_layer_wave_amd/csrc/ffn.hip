@@ -263,10 +263,17 @@ hipError_t launch_mxw_up(const FfnArgs &a, hipStream_t st) {
   return launch_mxw_gemm(p, true, a.perm != nullptr, a.act_quant, t.bm, t.bk, st);
 }
 
-hipError_t launch_mxw_down(const FfnArgs &a, hipStream_t st, bool *fused) {
+hipError_t launch_mxw_down(const FfnArgs &a, hipStream_t st, bool *fused, bool *yp_bf16) {
   MxwParams p = mxw_params(a, false);
   p.n_tiles = (a.d + 255) / 256;
-  if (!a.act_quant && mxw16_mixed_fits(false, a.d_ff)) return launch_mxw16_mixed(p, false, false, st);
+  // bf16 pile outputs where the caller takes them (unsplit passes only)
+  const bool piles16 = a.yp_bf16_ok && a.d % 8 == 0;
+  if (!a.act_quant && mxw16_mixed_fits(false, a.d_ff)) {
+    p.out_bf16 = piles16 ? 1 : 0;
+    hipError_t err = launch_mxw16_mixed(p, false, false, st);
+    if (err == hipSuccess && yp_bf16) *yp_bf16 = piles16;
+    return err;
+  }
   const TileChoice t = a.act_quant ? down_tile(a) : mxw16_tile(a, false);
   if (t.splits > 1 && a.split_part && down_split_factor(a) > 1) {
     p.splits = t.splits;
@@ -281,7 +288,10 @@ hipError_t launch_mxw_down(const FfnArgs &a, hipStream_t st, bool *fused) {
     }
     return launch_splitk_sum(a.split_part, t.splits, a.R, a.d, a.y_perm, st);
   }
-  return launch_mxw_gemm(p, false, false, a.act_quant, t.bm, t.bk, st);
+  p.out_bf16 = piles16 ? 1 : 0;
+  hipError_t err = launch_mxw_gemm(p, false, false, a.act_quant, t.bm, t.bk, st);
+  if (err == hipSuccess && yp_bf16) *yp_bf16 = piles16;
+  return err;
 }
 
 // Prefill of bf16 rows on MXFP4 weights: the GEMM with the codes in LDS
@@ -398,7 +408,7 @@ hipError_t launch_expert_down(const FfnArgs &a, hipStream_t st, bool *fused, boo
   if (yp_bf16) *yp_bf16 = false;
   if (a.R == 0) return hipSuccess;
   if (use_decode(a)) return launch_decode_down(a, st);
-  if (a.act_quant || use_mxw16(a, false)) return launch_mxw_down(a, st, fused);
+  if (a.act_quant || use_mxw16(a, false)) return launch_mxw_down(a, st, fused, yp_bf16);
   if (a.w_dtype == 0) {
     const long long tot = (long long)a.R * a.d;
     ffn_down_f32_kernel<<<(unsigned)((tot + 255) / 256), 256, 0, st>>>(

@@ -85,16 +85,6 @@ __device__ __forceinline__ void lgkm_wait0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
-// Four f32 pairs packed to bf16 (lo = columns 8g + 4lg + {0,1}, hi = +{2,3})
-// for g = 2h, 2h+1 -> the 16-B piece of eight consecutive columns this lane
-// stores.
-__device__ __forceinline__ u32x4 swap_halves(uint32_t x_lo, uint32_t x_hi, uint32_t y_lo,
-                                             uint32_t y_hi) {
-  const auto lo = __builtin_amdgcn_permlane32_swap(x_lo, y_lo, false, false);
-  const auto hi = __builtin_amdgcn_permlane32_swap(x_hi, y_hi, false, false);
-  return u32x4{lo[0], hi[0], lo[1], hi[1]};
-}
-
 // Up: H rows [row0, row0 + rows) in ro (row pitch N bf16) = silu(gate) * value,
 // gate = acc[tm][j], value = acc[tm][j + TN/2].  TM * TN stores per wave.
 template <int TM, int TN, int WM, int WN>
@@ -156,39 +146,6 @@ __device__ __forceinline__ void store_f32_regs(const f32x16 (&acc)[TM][TN],
                          acc[tm][tn][g * 4 + 3]};
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off, 0, 0);
       }
-  }
-}
-
-// Down: bf16 rows [0, rows) of a tile in ro (row pitch N bf16), each value
-// the f32 result rounded once.
-template <int TM, int TN, int WM, int WN>
-__device__ __forceinline__ void store_bf16_regs(const f32x16 (&acc)[TM][TN],
-                                                __amdgpu_buffer_rsrc_t ro, int N, int rows, int n0,
-                                                int wm, int wn) {
-  // (the lane id is read afresh: lane-derived values of the K loop are
-  // not kept live across it for the epilogue)
-  const int lane = __lane_id(), lr = lane & 31, lg = lane >> 5;
-  const uint32_t rowoff = (uint32_t)(wm * WM + lr) * (uint32_t)N;  // row r's first element
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int r = wm * WM + tm * 32 + lr;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      uint32_t pk[4][2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        pk[g][0] = pack_bf16x2(acc[tm][j][g * 4], acc[tm][j][g * 4 + 1]);
-        pk[g][1] = pack_bf16x2(acc[tm][j][g * 4 + 2], acc[tm][j][g * 4 + 3]);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 o = swap_halves(pk[2 * h][0], pk[2 * h][1], pk[2 * h + 1][0], pk[2 * h + 1][1]);
-        const int col = n0 + wn * WN + j * 32 + 16 * h + lg * 8;
-        const uint32_t off =
-            (r < rows && col < N) ? (rowoff + (uint32_t)(tm * 32 * N) + col) * 2u : kOOB;
-        __builtin_amdgcn_raw_buffer_store_b128(o, ro, off, 0, 0);
-      }
-    }
   }
 }
 

@@ -41,6 +41,8 @@ struct MxwParams {
   // range [s ksplit, (s+1) ksplit) and writes part[s][R][N].
   int splits, ksplit;
   float *part;
+  int out_bf16;  // down without a K split: pile outputs as bf16 [R][N] (the
+                 // f32 result rounded once) instead of f32
 };
 
 // Largest K the kernel takes (the whole K range of a tile's weight scales

@@ -441,8 +441,14 @@ __device__ __forceinline__ void mxw_tile(const MxwParams &p, const TileSlot &t, 
 
   // ---- epilogue ---------------------------------------------------------------
   if constexpr (!UP) {
-    float *dst = S > 1 ? p.part + (size_t)split * p.R * N : (float *)p.out;
-    store_f32_tile<T::TM, T::TN, T::WM, T::WN>(acc, dst, N, row0, rows, n0, wm, wn, lane);
+    if (S == 1 && p.out_bf16) {
+      store_bf16_regs<T::TM, T::TN, T::WM, T::WN>(
+          acc, rsrc((uint16_t *)p.out + (size_t)row0 * N, (uint32_t)rows * (uint32_t)N * 2u), N,
+          rows, n0, wm, wn);
+    } else {
+      float *dst = S > 1 ? p.part + (size_t)split * p.R * N : (float *)p.out;
+      store_f32_tile<T::TM, T::TN, T::WM, T::WN>(acc, dst, N, row0, rows, n0, wm, wn, lane);
+    }
   } else if constexpr (!A8) {
     __syncthreads();  // every wave is done reading the stages
     store_swiglu_bf16_tile<T::TM, T::TN, T::WM, T::WN, BM, NR, T::NT>(

@@ -71,8 +71,8 @@ struct FfnArgs {
   void *h;                // [R][d_ff] hidden (bf16, or f32 for f32 weights)
   float *y_perm;          // [R][d] f32 (or bf16, see yp_bf16_ok)
   // The caller takes bf16 pile outputs (each the f32 result rounded once)
-  // when the down pass can write them (the unsplit bf16-weight pass);
-  // launch_expert_down reports whether it did.
+  // when the down pass can write them (the prefill GEMMs without a K
+  // split); launch_expert_down reports whether it did.
   bool yp_bf16_ok;
   int n, k;               // tokens and experts per token
   // Optional combine fused into the down-projection (used when k == 1):
