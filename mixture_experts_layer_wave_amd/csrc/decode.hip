@@ -55,6 +55,10 @@ constexpr int kCopyWaves = kWaves - 1;  // waves 1.. issue the copies; wave 0 st
 constexpr int kMaxSteps = 8;   // 128-deep K steps per wave: K <= 32 * 4 * 4 * 8 = 4096
 constexpr int kBlocksPerCu = 2;  // persistent workgroups per CU
 constexpr int kMaxStages = 2;    // LDS ring depth per workgroup (2 measured faster than 3)
+// Few routed rows: a workgroup has about as many tiles as stages, and a
+// third stage (where LDS allows) puts them all in flight at once.
+constexpr int kFewRows = 16;
+constexpr int kFewRowsStages = 3;
 constexpr int kCuLds = 160 * 1024;
 constexpr int kRouteMaxR = 64;   // routed rows (n k) of the folded routing
 constexpr int kRouteMaxE = 128;  // experts of the folded routing (two per lane)
@@ -86,7 +90,7 @@ struct StagePlan {
 constexpr int kRedBytes = kWaves * 64 * 16;  // one f32x4 per lane per wave
 static_assert(kRedBytes >= (4 * kRouteMaxR + kRouteMaxE) * 4, "folded routing tables fit in red");
 
-StagePlan stage_plan(int K, bool up, int E) {
+StagePlan stage_plan(int K, bool up, int E, int max_stages = kMaxStages) {
   StagePlan s{};
   const int mats = up ? 2 : 1;
   const int code_bytes = tile_rows(up) * (K / 2), scale_bytes = tile_rows(up) * (K / 32);
@@ -95,7 +99,7 @@ StagePlan stage_plan(int K, bool up, int E) {
   s.table_bytes = ((3 * (E + 1) * 4 + kRouteMaxR * 4) + 15) & ~15;
   const int avail = kCuLds / kBlocksPerCu - kRedBytes - s.table_bytes;
   s.stages = avail > 0 ? avail / s.stage_bytes : 0;
-  if (s.stages > kMaxStages) s.stages = kMaxStages;
+  if (s.stages > max_stages) s.stages = max_stages;
   // Copies a wave may leave in flight: (stages - 1) tiles, < 64.
   const int per_wave = (s.copies + kCopyWaves - 1) / kCopyWaves;
   while (s.stages > 1 && (s.stages - 1) * per_wave > 63) --s.stages;
@@ -170,6 +174,25 @@ __device__ __forceinline__ void vm_wait_dyn(int n) {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
+// The work list's table, by one wave: s_gpre[e] = 16-row groups of the
+// piles before expert e (a pile of m rows has ceil(m / 16)), s_gpre[E] the
+// total.  Lane l sums a run of consecutive experts; a wave scan gives each
+// run its base.
+__device__ __forceinline__ void group_prefix_wave(const int *s_off, int *s_gpre, int E) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) >> 6;
+  const int lo = min(E, lane * per), hi = min(E, lo + per);
+  int run = 0;
+  for (int e = lo; e < hi; ++e) run += (s_off[e + 1] - s_off[e] + 15) >> 4;
+  const int incl = wave_incl_scan(run);
+  int base = incl - run;
+  for (int e = lo; e < hi; ++e) {
+    s_gpre[e] = base;
+    base += (s_off[e + 1] - s_off[e] + 15) >> 4;
+  }
+  if (lane == 63) s_gpre[E] = incl;
+}
+
 // KS = 128-deep K steps per wave (decode_steps(K)); A8: MXFP8 pile rows.
 template <bool UP, int KS, bool A8>
 __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
@@ -193,6 +216,11 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   int *s_perm = s_slot + (E + 1);                           // [kRouteMaxR] folded routing
 
   // ---- routing (folded) or the piles from dispatch ---------------------------
+  // Either way the LDS tables end up holding the pile offsets s_off, the
+  // 16-row groups before each expert s_gpre (the work list below) and the
+  // weight slots s_slot.  The slot table is read once here: a copying wave
+  // that loaded it from global memory per tile would wait for all of its
+  // copies in flight too (one in-order counter).
   const int32_t *perm = p.perm;
   if (p.route_part) {
     // Tables in `red` (free until the first tile): chosen ids, weights and
@@ -211,10 +239,16 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
                               publish ? p.r_w : s_w, nullptr, s_idx);
     __syncthreads();
     if (wave == 0) {
-      int nbits = 0;
-      while ((1 << nbits) < E) ++nbits;
-      dispatch_wave(s_idx, R, k, E, nbits, s_cnt, s_off, s_perm, s_inv);
+      if (R <= kDispTinyR) {
+        dispatch_wave_small<kRoutePer>(s_idx, R, k, E, s_cnt, s_off, s_perm, s_inv, s_gpre);
+      } else {
+        int nbits = 0;
+        while ((1 << nbits) < E) ++nbits;
+        dispatch_wave(s_idx, R, k, E, nbits, s_cnt, s_off, s_perm, s_inv);
+        group_prefix_wave(s_off, s_gpre, E);
+      }
     }
+    for (int e = tid; e < E; e += kWaves * 64) s_slot[e] = phys_slot(p.slot, p.n_slots, e);
     __syncthreads();
     if (publish) {
       for (int e = tid; e <= E; e += kWaves * 64) {
@@ -229,40 +263,18 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
     perm = s_perm;
   } else {
     for (int e = tid; e <= E; e += kWaves * 64) s_off[e] = p.offsets[e];
-  }
-
-  // ---- work list: groups of 16 pile rows, prefix over experts ---------------
-  // The slot table is read once here: a copying wave that loaded it from
-  // global memory per tile would wait for all of its copies in flight too
-  // (one in-order counter).
-  for (int e = tid; e < E; e += kWaves * 64) s_slot[e] = phys_slot(p.slot, p.n_slots, e);
-  __syncthreads();
-  {
-    // Thread tid sums experts [lo, hi); a block scan gives each run's base.
-    const int per = (E + kWaves * 64 - 1) / (kWaves * 64);
-    const int lo = min(E, tid * per), hi = min(E, lo + per);
-    int run = 0;
-    for (int e = lo; e < hi; ++e) run += (s_off[e + 1] - s_off[e] + 15) >> 4;
-    const int incl = wave_incl_scan(run);
-    int *s_wsum = (int *)red;  // wave totals (red is free until the first tile)
-    if (lane == 63) s_wsum[wave] = incl;
+    for (int e = tid; e < E; e += kWaves * 64) s_slot[e] = phys_slot(p.slot, p.n_slots, e);
     __syncthreads();
-    int base = incl - run;
-    for (int w = 0; w < wave; ++w) base += s_wsum[w];
-    for (int e = lo; e < hi; ++e) {
-      s_gpre[e] = base;
-      base += (s_off[e + 1] - s_off[e] + 15) >> 4;
-    }
-    if (tid == kWaves * 64 - 1) s_gpre[E] = base;
+    if (wave == 0) group_prefix_wave(s_off, s_gpre, E);
     __syncthreads();
   }
   const int W = s_gpre[E] * T;  // work items
   const int G = gridDim.x;
   // A8 up: ranges in whole quads of tiles (T % 4 == 0, so quads never
-  // straddle a group).
+  // straddle a group).  32-bit products: the host checks W * G < 2^32.
   constexpr int QT = (UP && A8) ? 4 : 1;
-  const int w_lo = QT * (int)(((long long)blockIdx.x * (W / QT)) / G);
-  const int w_hi = QT * (int)(((long long)(blockIdx.x + 1) * (W / QT)) / G);
+  const int w_lo = QT * (int)((uint32_t)blockIdx.x * (uint32_t)(W / QT) / (uint32_t)G);
+  const int w_hi = QT * (int)((uint32_t)(blockIdx.x + 1) * (uint32_t)(W / QT) / (uint32_t)G);
   const int n_my = w_hi - w_lo;
   if (n_my <= 0) return;
 
@@ -273,18 +285,17 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
     while (s_gpre[e + 1] <= gidx) ++e;
     return e;
   };
-  // The first item's expert: binary search for the largest e with
-  // s_gpre[e] <= g0, then the walk skips empty experts.
+  // The first item's expert: the number of experts e with s_gpre[e] <= g0,
+  // less one (s_gpre does not decrease, so they are a prefix of [0, E), and
+  // the last of them has a group, since s_gpre[e + 1] > g0); ballots over
+  // chunks of 64 experts, in every wave.
   int e_first;
   {
     const int g0 = w_lo / T;
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_gpre[mid] <= g0) lo = mid;
-      else hi = mid - 1;
-    }
-    e_first = expert_of(g0, lo);
+    int c = 0;
+    for (int e0 = 0; e0 < E; e0 += 64)
+      c += __popcll(__ballot(e0 + lane < E && s_gpre[e0 + lane] <= g0));
+    e_first = c - 1;
   }
 
   // ---- copy of one tile into stage st -------------------------------------
@@ -350,7 +361,12 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
     const int w = w_lo + i, gidx = w / T, tile = w % T, st = i % S;
     // A copying wave's copies of tile i have landed once at most the copies
     // of the tiles issued after it are outstanding (they complete in order).
-    if (wave > 0) vm_wait_dyn(min(S - 1, n_my - 1 - i) * my_copies);
+    // The first item always opens a group.  When the prologue put all of
+    // the workgroup's tiles in flight, its activation loads go out right
+    // behind those copies and the one wait below covers both (one trip to
+    // memory instead of two); with more tiles, waiting for all of the
+    // prologue's copies before tile 0 measured slower.
+    if (wave > 0 && (i > 0 || n_my > S)) vm_wait_dyn(min(S - 1, n_my - 1 - i) * my_copies);
     if (gidx != cur_group) {
       // ---- activations of the new group (rows t0..t0+15 of the pile) ----
       // Pile rows are gathered from the token matrix when perm is given
@@ -522,10 +538,17 @@ hipError_t launch_decode_ks(const DecodeParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// R = routed rows (an upper bound on the pile rows).
 template <bool UP, bool A8>
-hipError_t launch_decode(DecodeParams p, hipStream_t st) {
-  p.plan = stage_plan(p.K, UP, p.E);
+hipError_t launch_decode(DecodeParams p, int R, hipStream_t st) {
+  p.plan = stage_plan(p.K, UP, p.E, R <= kFewRows ? kFewRowsStages : kMaxStages);
   if (p.plan.stages < 1) return hipErrorInvalidValue;
+  // The kernel cuts the work list with 32-bit products (workgroup index
+  // times items): at most R / 16 + min(E, R) groups of N / tile_rows tiles.
+  const uint64_t groups = (uint64_t)R / 16 + (uint64_t)(R < p.E ? R : p.E) + 1;
+  if (groups * (uint64_t)(p.N / tile_rows(UP)) * (uint64_t)(kBlocksPerCu * cu_count() + 1) >=
+      ((uint64_t)1 << 32))
+    return hipErrorInvalidValue;
   switch (decode_steps(p.K)) {
     case 1: return launch_decode_ks<UP, 1, A8>(p, st);
     case 2: return launch_decode_ks<UP, 2, A8>(p, st);
@@ -601,9 +624,9 @@ hipError_t launch_decode_up(const FfnArgs &a, hipStream_t st) {
     p.as = (const uint8_t *)a.a + mx8_scale_offset(rows, a.d);
     p.sp = mx8_scale_pitch(a.d);
     p.out_s = (uint8_t *)a.h + mx8_scale_offset(a.R, a.d_ff);
-    return launch_decode<true, true>(p, st);
+    return launch_decode<true, true>(p, a.R, st);
   }
-  return launch_decode<true, false>(p, st);
+  return launch_decode<true, false>(p, a.R, st);
 }
 
 hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st) {
@@ -622,9 +645,9 @@ hipError_t launch_decode_down(const FfnArgs &a, hipStream_t st) {
   if (a.act_quant) {
     p.as = (const uint8_t *)a.h + mx8_scale_offset(a.R, a.d_ff);
     p.sp = mx8_scale_pitch(a.d_ff);
-    return launch_decode<false, true>(p, st);
+    return launch_decode<false, true>(p, a.R, st);
   }
-  return launch_decode<false, false>(p, st);
+  return launch_decode<false, false>(p, a.R, st);
 }
 
 }  // namespace moe

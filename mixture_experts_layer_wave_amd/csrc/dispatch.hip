@@ -6,7 +6,8 @@
 // be empty, and pile sizes depend on the data only.
 //
 // Deterministic in all three forms: one wave for up to 256 pairs
-// (dispatch_wave in route_dev.h); one 1024-thread workgroup (dispatch_block)
+// (dispatch_wave in route_dev.h, or dispatch_wave_small for a few pairs
+// of at most 128 experts); one 1024-thread workgroup (dispatch_block)
 // when no scratch is given; otherwise two passes over chunks of 1024 pairs,
 // one workgroup per chunk: (1) each chunk's per-expert counts and each
 // pair's stable rank among its chunk's pairs of the same expert, (2) every
@@ -140,7 +141,12 @@ __global__ __launch_bounds__(256) void dispatch_small_kernel(const int32_t *__re
                                                              int32_t *__restrict__ inv) {
   extern __shared__ int smem[];
   int *s_cnt = smem, *s_off = s_cnt + E, *s_perm = s_off + E + 1, *s_inv = s_perm + R;
-  if (threadIdx.x < MOE_WAVE) dispatch_wave(idx, R, k, E, nbits, s_cnt, s_off, s_perm, s_inv);
+  if (threadIdx.x < MOE_WAVE) {
+    if (R <= kDispTinyR && E <= 2 * MOE_WAVE)
+      dispatch_wave_small<2>(idx, R, k, E, s_cnt, s_off, s_perm, s_inv, nullptr);
+    else
+      dispatch_wave(idx, R, k, E, nbits, s_cnt, s_off, s_perm, s_inv);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e <= E; e += blockDim.x) {
     if (e < E) counts[e] = s_cnt[e];
@@ -173,7 +179,12 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     topk_token_t<PER>(part, S, (size_t)n * E, t0 + (int)threadIdx.x / G, n, E, k, renorm, idx, w,
                       nullptr, s_idx);
   __syncthreads();
-  if (threadIdx.x < MOE_WAVE) dispatch_wave(s_idx, R, k, E, nbits, s_cnt, s_off, s_perm, s_inv);
+  if (threadIdx.x < MOE_WAVE) {
+    if (R <= kDispTinyR && E <= 2 * MOE_WAVE)
+      dispatch_wave_small<2>(s_idx, R, k, E, s_cnt, s_off, s_perm, s_inv, nullptr);
+    else
+      dispatch_wave(s_idx, R, k, E, nbits, s_cnt, s_off, s_perm, s_inv);
+  }
   __syncthreads();
   for (int e = threadIdx.x; e <= E; e += blockDim.x) {
     if (e < E) counts[e] = s_cnt[e];

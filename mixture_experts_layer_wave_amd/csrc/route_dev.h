@@ -107,11 +107,14 @@ __device__ __forceinline__ void topk_token_t(const float *__restrict__ part, int
   float v[kTopkPer];
   const float *pz = part + (size_t)t * E + gl;
   // Split-major: each split's loads for all expert slots are independent,
-  // and every slot accumulates its splits in order (deterministic).
+  // and every slot accumulates its splits in order (deterministic).  The
+  // sum starts from -0, which added to any value gives that value, so the
+  // first split needs no load of its own ahead of the batch (one round trip
+  // to memory instead of two when the splits fit one batch).
 #pragma unroll
-  for (int j = 0; j < kTopkPer; ++j) v[j] = (live && gl + G * j < E) ? pz[G * j] : NEG;
+  for (int j = 0; j < kTopkPer; ++j) v[j] = (live && gl + G * j < E) ? -0.f : NEG;
   constexpr int kBatch = kTopkPer >= 32 ? 1 : 32 / kTopkPer;  // splits loaded per batch
-  for (int s0 = 1; s0 < S; s0 += kBatch) {
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
     float q[kBatch][kTopkPer];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
@@ -392,6 +395,81 @@ __device__ __forceinline__ void dispatch_wave(const int32_t *__restrict__ idx, i
     }
   }
   for (int r = carry + lane; r < R; r += MOE_WAVE) s_perm[r] = -1;
+}
+
+// The same piles for R <= kDispTinyR pairs and E <= 64 * PE experts, by one
+// wave with no LDS round trips in between: lane r holds pair r, and the
+// pairs are read one at a time across the wave (readlane, a uniform value
+// per step).  A pair's rank is the number of earlier pairs with its expert,
+// and its pile row is the number of pairs with a smaller expert plus that
+// rank, so the grouping is the unique stable one, as dispatch_wave builds
+// it.  Lane l also counts, for its experts l + 64 j, the pairs of smaller
+// experts (s_off) and of the expert itself (s_cnt).  When s_gpre is given it
+// also receives, per expert, the number of 16-row groups of the piles before
+// it (a pile of m rows has ceil(m / 16); the pairs of rank 0, 16, 32 ...
+// each open one), with the total in s_gpre[E].  Same outputs as
+// dispatch_wave otherwise, including the -1 entries for ids outside [0, E).
+// Its cost grows with R (two steps per pair), while dispatch_wave's is about
+// flat up to 64 pairs: measured faster for 4 pairs, slower for 32.
+constexpr int kDispTinyR = 8;
+
+template <int PE>
+__device__ __forceinline__ void dispatch_wave_small(const int32_t *__restrict__ idx, int R, int k,
+                                                    int E, int *s_cnt, int *s_off, int *s_perm,
+                                                    int *s_inv, int *s_gpre) {
+  const int lane = threadIdx.x & 63;
+  const int my_e = lane < R ? idx[lane] : -1;
+  const bool my_valid = my_e >= 0 && my_e < E;
+  // pass 1: the lane's own pair (rank, pairs of smaller experts); ids
+  // outside [0, E) count nowhere (an invalid er matches no valid my_e, and
+  // is not below one only when er >= E, so both tests carry the range)
+  int rank = 0, below = 0;
+  for (int r = 0; r < R; ++r) {
+    const int er = __builtin_amdgcn_readlane(my_e, r);
+    const bool vr = er >= 0 && er < E;
+    rank += (vr && r < lane && er == my_e) ? 1 : 0;
+    below += (vr && er < my_e) ? 1 : 0;
+  }
+  // pass 2: per expert of the lane, counts and group prefix
+  int cnt[PE], less[PE], gless[PE];
+#pragma unroll
+  for (int j = 0; j < PE; ++j) cnt[j] = less[j] = gless[j] = 0;
+  int used = 0, groups = 0;
+  for (int r = 0; r < R; ++r) {
+    const int er = __builtin_amdgcn_readlane(my_e, r);
+    const bool vr = er >= 0 && er < E;
+    const bool opens = vr && (__builtin_amdgcn_readlane(rank, r) & 15) == 0;
+    used += vr ? 1 : 0;
+    groups += opens ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < PE; ++j) {
+      const int e = lane + MOE_WAVE * j;
+      cnt[j] += (vr && er == e) ? 1 : 0;
+      less[j] += (vr && er < e) ? 1 : 0;
+      gless[j] += (opens && er < e) ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PE; ++j) {
+    const int e = lane + MOE_WAVE * j;
+    if (e < E) {
+      s_cnt[e] = cnt[j];
+      s_off[e] = less[j];
+      if (s_gpre) s_gpre[e] = gless[j];
+    }
+  }
+  if (lane == 0) {
+    s_off[E] = used;
+    if (s_gpre) s_gpre[E] = groups;
+  }
+  if (my_valid) {
+    const int pos = below + rank;
+    s_perm[pos] = lane / k;
+    s_inv[lane] = pos;
+  } else if (lane < R) {
+    s_inv[lane] = -1;
+  }
+  if (lane >= used && lane < R) s_perm[lane] = -1;
 }
 
 }  // namespace moe

@@ -65,6 +65,7 @@ def test_dispatch_of_routed_workloads(name, chunked):
 @pytest.mark.parametrize("chunked", [False, True])
 @pytest.mark.parametrize("case", ["one-expert", "empty-experts", "many-chunks", "n1", "e1", "dup-slots",
                                   "small-256", "small-dups", "small-e1024", "small-257",
+                                  "tiny-dups", "tiny-e128",
                                   "chunks-1025", "chunks-2048-e1024"])
 def test_dispatch_edge_cases(case, chunked):
     say(f"[dispatch-edge] {case} chunked={chunked}")
@@ -83,6 +84,10 @@ def test_dispatch_edge_cases(case, chunked):
         E, idx = 1, np.zeros((50, 1))
     elif case == "small-256":  # the one-wave path at its largest: 4 chunks of 64 pairs
         E, idx = 128, rng.integers(0, 128, size=(64, 4))
+    elif case == "tiny-dups":  # at most 8 pairs (the readlane form): repeats, empty experts
+        E, idx = 5, rng.choice([1, 3, 4], size=(4, 2))
+    elif case == "tiny-e128":  # at most 8 pairs over 128 experts (two per lane)
+        E, idx = 128, rng.integers(0, 128, size=(2, 4))
     elif case == "small-dups":  # one-wave path, few experts, repeated slots
         E, idx = 3, rng.integers(0, 3, size=(70, 3))
     elif case == "small-e1024":  # one-wave path, offsets scanned over 16 chunks of experts
