@@ -137,6 +137,19 @@ double expected_row_tiles(const FfnArgs &a, int bm) {
   return piles * t;
 }
 
+// Whether the unsplit bf16 down pass with block tile bm x bnb takes the
+// tail split (TailPlan below): it runs longest first over more than two
+// rounds of blocks, and the piles' last row tiles, split in two along K,
+// fill at most the 256 CUs.
+bool tail_split_fits(const FfnArgs &a, int bm, int bnb) {
+  if (a.w_dtype != 1 || a.act_quant || a.R == 0 || a.k == 1 || !a.split_ok || a.d % 4) return false;
+  if (!big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff)) return false;
+  const long long piles = a.E < a.R ? a.E : a.R;
+  const long long n_tiles = (a.d + bnb - 1) / bnb;
+  const long long blocks = ((a.R + bm - 1) / bm + piles) * n_tiles;
+  return blocks > 2 * 256 && piles * n_tiles * 2 <= 256 && (a.d_ff + 63) / 64 >= 4;
+}
+
 TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_cand,
                        bool w4a8 = false) {
   const int N = up ? a.d_ff : a.d, K = up ? a.d : a.d_ff;
@@ -164,6 +177,17 @@ TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_
              : (double)(cand[i].bm + cand[i].bnb);
     double cost = (double)rounds * ((nk + S - 1) / S) * step_units + rounds * kUnitsPerRound;
     if (S > 1) cost += (2.0 * S - 1.0) * a.R * (double)N * 4.0 * kUnitsPerByte;
+    if (!up && !w4a8 && S == 1 && tail_split_fits(a, cand[i].bm, cand[i].bnb)) {
+      // The piles' last row tiles run as twice as many half-K blocks after
+      // the rounds of the other tiles; their two f32 planes are written and
+      // added once.
+      const double piles = a.E < a.R ? a.E : a.R;
+      const long long full = ((long long)((mt - piles) * nt) + 255) / 256;
+      const long long tail = ((long long)(piles * nt * 2) + 255) / 256;
+      cost = ((double)full * nk + (double)tail * ((nk + 1) / 2)) * step_units +
+             (double)(full + tail) * kUnitsPerRound +
+             3.0 * piles * cand[i].bm * (double)N * 4.0 * kUnitsPerByte;
+    }
     if (best_cost < 0 || cost < best_cost) {
       best = cand[i];
       best_cost = cost;
@@ -176,7 +200,8 @@ TileChoice choose_tile(const FfnArgs &a, bool up, const TileChoice *cand, int n_
 // the workspace sizing through down_split_factor and the launch agree).
 TileChoice down_tile(const FfnArgs &a) {
   static const TileChoice cand_bf16[] = {{256, 256, 1}, {320, 256, 1}, {256, 128, 1}, {128, 128, 1},
-                                         {256, 256, 2}, {256, 256, 3}, {256, 256, 4}};
+                                         {256, 256, 2}, {256, 256, 3}, {256, 256, 4}, {320, 256, 2},
+                                         {320, 256, 3}, {320, 256, 4}};
   static const TileChoice cand_mx[] = {{256, 256, 1}, {256, 128, 1}, {128, 128, 1},
                                        {256, 256, 2}, {256, 256, 3}, {256, 256, 4}};
   // W4A8: 128-row tiles with 256-deep steps where their LDS fits (they read
@@ -189,7 +214,7 @@ TileChoice down_tile(const FfnArgs &a) {
   if (a.act_quant)
     return mxw_fits(false, true, 128, 256, a.d_ff) ? choose_tile(a, false, cand_w4a8_deep, 3, true)
                                               : choose_tile(a, false, cand_w4a8, 4, true);
-  return a.w_dtype == 2 ? choose_tile(a, false, cand_mx, 6) : choose_tile(a, false, cand_bf16, 7);
+  return a.w_dtype == 2 ? choose_tile(a, false, cand_mx, 6) : choose_tile(a, false, cand_bf16, 10);
 }
 
 // Operands of the GEMM with MXFP4 codes in LDS: W4A8 takes MXFP8 matrices
@@ -356,11 +381,7 @@ TailPlan down_tail_plan(const FfnArgs &a) {
   if (a.w_dtype != 1 || a.act_quant || a.R == 0 || a.k == 1 || !a.split_ok || a.d % 4) return t;
   if (!big_ok(a, (size_t)a.R * a.d_ff * 2, a.d, a.d_ff)) return t;
   const TileChoice c = down_tile(a);
-  if (c.splits > 1) return t;
-  const long long piles = a.E < a.R ? a.E : a.R;
-  const long long n_tiles = (a.d + c.bnb - 1) / c.bnb;
-  const long long blocks = ((a.R + c.bm - 1) / c.bm + piles) * n_tiles;
-  if (blocks <= 2 * 256 || piles * n_tiles * 2 > 256 || (a.d_ff + 63) / 64 < 4) return t;
+  if (c.splits > 1 || !tail_split_fits(a, c.bm, c.bnb)) return t;
   t.splits = 2;
   t.bm = c.bm;
   t.bnb = c.bnb;

@@ -46,7 +46,8 @@ KERNEL_SOURCES = {
                            "csrc/common.h"],
     "mxw16_pair_kernel": ["csrc/gemm_mxw.hip", "csrc/gemm_mxw.h", "csrc/gemm_common.h",
                           "csrc/common.h", "csrc/ffn.hip"],
-    "mx_decode_kernel": ["csrc/decode.hip", "csrc/gemm_mxw.h", "csrc/common.h"],
+    "mx_decode_kernel": ["csrc/decode.hip", "csrc/gemm_mxw.h", "csrc/common.h",
+                         "csrc/route_dev.h"],
 }
 
 
