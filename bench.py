@@ -4,7 +4,9 @@
 
 A step is one moe_forward (router + top-k, dispatch, grouped expert FFN up
 and down, combine) over one batch of synthetic tokens already resident in
-HBM.  W untimed steps, then K timed steps between device synchronisations;
+HBM.  W untimed steps (by default at least 10 and a quarter second of them,
+so that a short layer is not timed while the clock ramps up under load),
+then K timed steps between device synchronisations;
 the expert weights rotate over several identical copies so that each step
 reads them from HBM rather than from the 256 MB last-level cache.
 
@@ -113,7 +115,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before timing (default: at least 10 and 0.25 s of them, "
+                         "so that the clock has settled under load)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -174,9 +178,21 @@ def main():
         B.moe_forward(D.shape, D.x, D.act, D.wg, D.bias, copies[i % len(copies)], D.y, D.act,
                       D.idx, D.topw, D.ws, D.ws_bytes, st)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    if args.warmup is not None:
+        warm = args.warmup
+        for i in range(warm):
+            step(i)
+        torch.cuda.synchronize()
+    else:
+        # Steps in groups of ten until a quarter second has run: a short layer
+        # would otherwise be timed while the clock still ramps up under load.
+        warm = 0
+        w0 = time.perf_counter()
+        while warm < 10 or time.perf_counter() - w0 < 0.25:
+            for _ in range(10):
+                step(warm)
+                warm += 1
+            torch.cuda.synchronize()
     per_launch = 1
     if args.graph:
         # One graph holds len(copies) consecutive steps, each on its own weight
@@ -194,7 +210,7 @@ def main():
                     step(i, cap)
         stream.wait_stream(cap)
         torch.cuda.synchronize()
-        for _ in range(max(1, args.warmup // per_launch)):
+        for _ in range(max(1, warm // per_launch)):
             graph.replay()
         torch.cuda.synchronize()
     launches = max(1, args.steps // per_launch)
@@ -256,7 +272,7 @@ def main():
 
     # Dominant kernel: the grouped up-projection, one launch per call.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.warmup):
+    for i in range(min(warm, 2 * args.steps)):
         B.moe_expert_up(D.shape, a_in, a_dt, perm, offsets, copies[i % len(copies)], h, stream)
     for i, (a, b) in enumerate(evs):
         a.record(stream)
@@ -307,7 +323,7 @@ def main():
     value = n / (ms_per_step * 1e-3)
     line = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps_timed, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "steps": steps_timed, "warmup": warm, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": (D.act if D.wdt != "mxfp4" else
                   "mxfp8 x mxfp4 (w4a8)" if aq else "bf16 (mxfp4 weights)"),
