@@ -53,6 +53,30 @@ def test_workspace_bytes():
     assert B.moe_workspace_bytes((n, d, E, k, f), 7) == 0
 
 
+def test_workspace_holds_the_down_pass_planes_the_tile_plan_needs():
+    """The bf16 down pass's block tile and K split are chosen on the host from
+    the shape, and the workspace sizes the f32 planes they need.  With about
+    512 rows per expert (Switch-shaped, one expert per token) 320 x 256 tiles
+    in four K splits make one round of 256 blocks: four planes of the pile
+    outputs.  With about 2048 rows per expert (Mixtral-shaped, top-2) the
+    pass runs unsplit over 3.5 rounds of 320 x 256 tiles, and the piles' last
+    row tiles take the two-way tail split: two planes of E x 320 rows."""
+    from mixture_experts_layer_wave_amd import binding as B
+
+    def extra(n, d, E, k, f):
+        R = n * k
+        splits = -(-d // 256)  # router K splits (256-deep, d a multiple of 32 here)
+        small = R * f * 2 + R * d * 4 + splits * n * E * 4  # hidden, pile outputs, logits
+        return B.moe_workspace_bytes((n, d, E, k, f), "bf16") - small, R
+
+    got, R = extra(4096, 1024, 8, 1, 4096)
+    planes = 4 * R * 1024 * 4
+    assert planes <= got < planes + (1 << 20)
+    got, R = extra(8192, 4096, 8, 2, 14336)
+    tail = 2 * 8 * 320 * 4096 * 4
+    assert tail <= got < tail + (1 << 20)
+
+
 @pytest.mark.parametrize("shape,status", [
     (None, -1),
     ((0, 8, 4, 1, 8), -2),
