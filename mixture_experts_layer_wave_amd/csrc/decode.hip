@@ -53,7 +53,12 @@ namespace {
 constexpr int kWaves = 4;      // waves per workgroup, splitting K
 constexpr int kCopyWaves = kWaves - 1;  // waves 1.. issue the copies; wave 0 stores
 constexpr int kMaxSteps = 8;   // 128-deep K steps per wave: K <= 32 * 4 * 4 * 8 = 4096
-constexpr int kBlocksPerCu = 2;  // persistent workgroups per CU
+constexpr int kBlocksPerCu = 2;  // persistent workgroups per CU (an even grid)
+// Share of the work list a CU's second workgroup takes against its first
+// (13/16, exact in binary), when each workgroup has at least kShareMinItems
+// items (below that the share only makes the ranges lumpier).
+constexpr double kSecondShare = 0.8125;
+constexpr int kShareMinItems = 4;
 constexpr int kMaxStages = 2;    // LDS ring depth per workgroup (2 measured faster than 3)
 // Few routed rows: a workgroup has about as many tiles as stages, and a
 // third stage (where LDS allows) puts them all in flight at once.
@@ -271,10 +276,31 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   const int W = s_gpre[E] * T;  // work items
   const int G = gridDim.x;
   // A8 up: ranges in whole quads of tiles (T % 4 == 0, so quads never
-  // straddle a group).  32-bit products: the host checks W * G < 2^32.
+  // straddle a group).  The dispatcher places blocks [0, G/2) first, one per
+  // CU, then [G/2, G) as each CU's second workgroup, whose waves are younger
+  // and issue after the first's: with equal ranges the second workgroups
+  // finished 13-15% later (per-block timelines at 8 and 64 tokens), leaving
+  // each CU half used at the end.  With several items per workgroup they get
+  // kSecondShare of a first workgroup's share.  The bounds are floor(W c(b) /
+  // c(G)) in double precision with the cumulative share c(b) a multiple of
+  // 1/16: exact products, one correctly rounded division, the same
+  // expression for a block's end and the next block's start, so the ranges
+  // tile [0, W).
+  // Fewer items: equal ranges in 32-bit integers (products below 4 G^2).
   constexpr int QT = (UP && A8) ? 4 : 1;
-  const int w_lo = QT * (int)((uint32_t)blockIdx.x * (uint32_t)(W / QT) / (uint32_t)G);
-  const int w_hi = QT * (int)((uint32_t)(blockIdx.x + 1) * (uint32_t)(W / QT) / (uint32_t)G);
+  int w_lo, w_hi;
+  if (W / QT >= kShareMinItems * G) {
+    const int H = G / 2;
+    auto cum = [&](int b) {
+      return b <= H ? (double)b : (double)H + (double)(b - H) * kSecondShare;
+    };
+    const double c_all = cum(G);
+    w_lo = QT * (int)floor((double)(W / QT) * cum(blockIdx.x) / c_all);
+    w_hi = QT * (int)floor((double)(W / QT) * cum(blockIdx.x + 1) / c_all);
+  } else {
+    w_lo = QT * (int)((uint32_t)blockIdx.x * (uint32_t)(W / QT) / (uint32_t)G);
+    w_hi = QT * (int)((uint32_t)(blockIdx.x + 1) * (uint32_t)(W / QT) / (uint32_t)G);
+  }
   const int n_my = w_hi - w_lo;
   if (n_my <= 0) return;
 
@@ -543,12 +569,6 @@ template <bool UP, bool A8>
 hipError_t launch_decode(DecodeParams p, int R, hipStream_t st) {
   p.plan = stage_plan(p.K, UP, p.E, R <= kFewRows ? kFewRowsStages : kMaxStages);
   if (p.plan.stages < 1) return hipErrorInvalidValue;
-  // The kernel cuts the work list with 32-bit products (workgroup index
-  // times items): at most R / 16 + min(E, R) groups of N / tile_rows tiles.
-  const uint64_t groups = (uint64_t)R / 16 + (uint64_t)(R < p.E ? R : p.E) + 1;
-  if (groups * (uint64_t)(p.N / tile_rows(UP)) * (uint64_t)(kBlocksPerCu * cu_count() + 1) >=
-      ((uint64_t)1 << 32))
-    return hipErrorInvalidValue;
   switch (decode_steps(p.K)) {
     case 1: return launch_decode_ks<UP, 1, A8>(p, st);
     case 2: return launch_decode_ks<UP, 2, A8>(p, st);
