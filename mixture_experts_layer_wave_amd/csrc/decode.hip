@@ -12,7 +12,7 @@
 // (down), or 8 rows of W1 next to the same 8 rows of W3 (up, so that the
 // SwiGLU pair meets in one accumulator).  Work item = (pile, group of 16
 // pile rows, tile).  The items of all non-empty experts form one list, cut
-// into equal contiguous ranges, one per workgroup; two persistent
+// into contiguous ranges, one per workgroup (sized below); two persistent
 // workgroups share a CU.  Each streams its tiles through a ring of S LDS
 // stages: every byte of a tile (codes and E8M0 scales, contiguous in
 // memory) is copied by direct global-to-LDS loads S-1 tiles ahead of the
