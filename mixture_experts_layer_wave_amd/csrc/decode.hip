@@ -286,7 +286,10 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
   // 1/16: exact products, one correctly rounded division, the same
   // expression for a block's end and the next block's start, so the ranges
   // tile [0, W).
-  // Fewer items: equal ranges in 32-bit integers (products below 4 G^2).
+  // Fewer items (one to a few per workgroup): q each and one more for the
+  // first W mod G blocks, which puts the extra items on first workgroups
+  // whenever there are at most G/2 of them (n = 1 layer 0.4-0.7 us faster
+  // than spreading them evenly).
   constexpr int QT = (UP && A8) ? 4 : 1;
   int w_lo, w_hi;
   if (W / QT >= kShareMinItems * G) {
@@ -298,8 +301,9 @@ __global__ __launch_bounds__(256) void mx_decode_kernel(DecodeParams p) {
     w_lo = QT * (int)floor((double)(W / QT) * cum(blockIdx.x) / c_all);
     w_hi = QT * (int)floor((double)(W / QT) * cum(blockIdx.x + 1) / c_all);
   } else {
-    w_lo = QT * (int)((uint32_t)blockIdx.x * (uint32_t)(W / QT) / (uint32_t)G);
-    w_hi = QT * (int)((uint32_t)(blockIdx.x + 1) * (uint32_t)(W / QT) / (uint32_t)G);
+    const int q = (W / QT) / G, rem = (W / QT) % G, b = blockIdx.x;
+    w_lo = QT * (b * q + min(b, rem));
+    w_hi = QT * ((b + 1) * q + min(b + 1, rem));
   }
   const int n_my = w_hi - w_lo;
   if (n_my <= 0) return;
